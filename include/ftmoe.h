@@ -1,0 +1,262 @@
+/*
+ * ftmoe.h — C ABI of the routed-expert MoE layer with a GPU slot cache
+ * (MI355X / gfx950, HIP).
+ *
+ * The layer follows the FreeToken pages: the full routed-expert pool lives in
+ * host memory and is the source of truth; a slot cache in HBM holds complete
+ * layer-expert records shared by all layers; one control kernel per layer
+ * dedupes the routed experts, classifies each as a hit or a miss, derives the
+ * fill count q, picks LRU victims and rewrites the routes into slot ids; the
+ * expert FFN runs on the GPU for hits and fills and on host cores for the
+ * remaining misses, and the two partial sums merge into the layer output.
+ * Prefill instead streams whole layers through two full-layer buffers.
+ *
+ * Conventions shared by every call
+ *  - All functions return ft_status.  On error nothing has been enqueued and
+ *    ft_last_error() (thread-local) describes the problem.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    GPU step is enqueued on it; only create, resize, stats, snapshot,
+ *    read_slot and destroy synchronise with the device.
+ *  - Device pointers must be allocated on the device that created the cache.
+ *  - A handle is used from one host thread at a time.
+ *  - bf16 values are passed as uint16_t bit patterns.
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef FTMOE_H
+#define FTMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FT_OK = 0,
+    FT_ERR_ARG = 1,          /* invalid argument or shape                       */
+    FT_ERR_NOMEM = 2,        /* device or pinned allocation failed              */
+    FT_ERR_HIP = 3,          /* a HIP runtime call failed                       */
+    FT_ERR_STATE = 4,        /* call not valid in the cache's current state     */
+    FT_ERR_UNSUPPORTED = 5   /* combination not implemented                     */
+} ft_status;
+
+/* Weight formats of a layer-expert record. */
+enum {
+    FT_FMT_BF16 = 0,         /* bf16 weights                                     */
+    FT_FMT_FP8_B128 = 1,     /* e4m3fn codes, one fp32 scale per 128x128 block   */
+    FT_FMT_MXFP4_B32 = 2     /* e2m1 codes, one e8m0 scale per 32 along K        */
+};
+
+/* Layer geometry.  d_model and d_ff must be multiples of 128. */
+typedef struct {
+    int32_t layers;          /* L: MoE layers held by the host bank              */
+    int32_t experts;         /* E: routed experts per layer (<= 4096)            */
+    int32_t top_k;           /* k: experts per token (1..E, <= 16)               */
+    int32_t d_model;         /* d: hidden size                                   */
+    int32_t d_ff;            /* f: expert FFN width                              */
+    int32_t fmt;             /* FT_FMT_*                                         */
+} ft_shape;
+
+/* Profiled bandwidths that set the fill/host split.  q = 0 if m = 0, else
+ * min(max(round_half_up(m * bp / bh), 1), m, slots - hits, cap) with
+ * cap = max_fetch when max_fetch >= 0 (no cap when -1).  Derivation:
+ * "Making Large MoE Models Practical on a Single Machine", section 5
+ * "Deriving q*" (T_fill = qS/B_P balanced against T_cpu = (m-q)S/(B_H-B_P));
+ * at-least-one-fill rule: txtmix article, q* policy paragraph. */
+typedef struct {
+    uint32_t bp_mbps;        /* B_P, MB/s, > 0                                   */
+    uint32_t bh_mbps;        /* B_H, MB/s, > 0                                   */
+    int32_t max_fetch;       /* -1 = no cap; >= 0 caps fills per call            */
+} ft_profile;
+
+typedef struct ft_cache ft_cache;
+
+/* Unique-id classes written by ft_cache_classify. */
+enum { FT_HIT = 0, FT_FILL = 1, FT_CPU = 2 };
+
+/* Forward modes and flags. */
+enum {
+    FT_MODE_CACHED = 0,      /* consume routes rewritten by ft_cache_classify    */
+    FT_MODE_STREAMED = 1,    /* compute from the full-layer buffer of `layer`    */
+    FT_PREFETCH_NEXT = 0x100 /* STREAMED: also enqueue layer+1's load            */
+};
+
+/* Output of one classify call: caller-owned DEVICE arrays of `capacity`
+ * entries (capacity >= T * top_k).  Entries past the valid counts are left
+ * unspecified ("The Expert Cache That Follows the Router", section "How
+ * residency follows demand without leaving the device": fixed-size device
+ * buffers with a valid count keep the dynamic miss count out of graph shapes).
+ *   counts[0] n_uniq   unique flat ids (flat id = layer * E + expert)
+ *   counts[1] hits
+ *   counts[2] m        misses
+ *   counts[3] q        fills (the first q misses in ascending flat-id order)
+ *   uniq[i]            ascending unique flat ids, i < n_uniq
+ *   cls[i]             FT_HIT / FT_FILL / FT_CPU of uniq[i]
+ *   slot[i]            slot holding uniq[i] after the call, -1 for FT_CPU
+ *   ev_slot[i], ev_old[i], ev_new[i]   i < q: the i-th fill's victim slot, the
+ *                      flat id it evicted (-1 if the slot was empty) and the
+ *                      flat id admitted
+ *   cpu_ids[i]         i < m - q: flat ids executed on the host            */
+typedef struct {
+    int32_t* counts;         /* int32[4] */
+    int32_t* uniq;
+    uint8_t* cls;
+    int32_t* slot;
+    int32_t* ev_slot;
+    int32_t* ev_old;
+    int32_t* ev_new;
+    int32_t* cpu_ids;
+    int32_t capacity;
+} ft_classify_out;
+
+/* Cumulative counters (read by ft_cache_stats, which synchronises). */
+typedef struct {
+    uint64_t calls;          /* classify calls                                   */
+    uint64_t routes;         /* routed (token, expert) pairs seen by classify    */
+    uint64_t unique;         /* unique layer-experts                             */
+    uint64_t hits, misses, fills, cpu_experts, evictions;
+    uint64_t bytes_filled;   /* record bytes copied host -> slot by fills        */
+    uint64_t layers_streamed;/* full-layer loads into the two buffers            */
+    uint64_t clock;          /* LRU clock (starts at 1)                          */
+    int32_t error_flags;     /* sticky device flags: 1 = expert id out of range  */
+    int32_t num_slots;
+} ft_stats;
+
+/* ---------------------------------------------------------------------------
+ * ft_cache_create — build a cold slot cache over a host bank.
+ *
+ * host_bank: caller-owned PINNED host memory (ft_host_alloc, or any
+ *   hipHostMalloc allocation) holding layers * experts records of
+ *   ft_record_bytes() bytes, record r = layer * E + expert at offset r * S
+ *   (flat-id-major banks: txtmix article, section on the FTW format; the host
+ *   pool is authoritative: "The Expert Cache That Follows the Router", section
+ *   "One logical expert, two physical levels of memory").  It must stay valid
+ *   and unchanged until ft_cache_destroy.
+ * num_slots: N complete records allocated in HBM (1..32768).
+ * max_tokens: largest T any later call will pass (sizes internal buffers).
+ * Errors: FT_ERR_ARG (shape, null, N), FT_ERR_NOMEM, FT_ERR_HIP.
+ * Synchronises the current device.
+ *
+ * Record layout (S bytes), every matrix [rows x K] with K contiguous:
+ *   BF16       WgT [f x d] | WuT [f x d] | WdT [d x f]                  (bf16)
+ *   FP8_B128   codes WgT | WuT | WdT (u8 e4m3fn), then fp32 scales
+ *              sg [f/128 x d/128] | su [f/128 x d/128] | sd [d/128 x f/128]
+ *   MXFP4_B32  codes WgT [f x d/2] | WuT [f x d/2] | WdT [d x f/2]
+ *              (two e2m1 per byte, low nibble = even k), then e8m0 scales
+ *              sg [f x d/32] | su [f x d/32] | sd [d x f/32]
+ * where FFN(x) = (silu(x WgT^T) * (x WuT^T)) WdT^T.
+ * ------------------------------------------------------------------------- */
+ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, const void* host_bank,
+                          int64_t num_slots, int32_t max_tokens, ft_cache** out);
+
+/* Release every resource of the cache (synchronises).  NULL is accepted. */
+ft_status ft_cache_destroy(ft_cache* cache);
+
+/* Bytes of one layer-expert record for a shape (0 for an invalid shape). */
+int64_t ft_record_bytes(const ft_shape* shape);
+
+/* ---------------------------------------------------------------------------
+ * ft_moe_route — top-k softmax routing ("Making Large MoE Models Practical on
+ * a Single Machine", section 1: each token selects a few of the layer's
+ * experts).
+ * x  [T x d]   bf16, device, row-major
+ * wr [d x E]   bf16, device, row-major (z = x wr)
+ * ids [T x k]  int32, device, out: experts by logit descending, ties to the
+ *              lower expert index
+ * w  [T x k]   fp32, device, out: softmax over the k chosen logits
+ * Logits are accumulated in fp64 from exact bf16 products.  Stateless; T >= 0
+ * (T = 0 enqueues nothing).  Errors: FT_ERR_ARG, FT_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+ft_status ft_moe_route(const ft_shape* shape, const uint16_t* x, const uint16_t* wr, int32_t T,
+                       int32_t* ids, float* w, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ft_cache_classify — the per-layer control step ("The Expert Cache That
+ * Follows the Router", section "How residency follows demand without leaving
+ * the device"; hyper.ai summary, section 方法: one single-pass kernel dedupes,
+ * classifies against the residency table, derives q and selects victims;
+ * txtmix article, section "CUDA-graph 兼容的 LRU 缓存": one scan yields the
+ * LRU candidates and the miss path takes the first q).
+ * ids [T x k]  int32, device, IN: expert ids 0..E-1 of `layer`;
+ *              OUT (in place): the route of each (token, j): the slot id for a
+ *              hit or fill, -(1 + expert) for an expert run on the host.
+ *              An id outside 0..E-1 sets error flag 1 (ft_stats) and its route
+ *              becomes INT32_MIN, which ft_moe_forward ignores.
+ * out          caller-owned device arrays (see ft_classify_out); may be NULL
+ *              when the caller does not need them.
+ * Enqueues the control kernel on `stream` and the fills (device-initiated
+ * copies of whole records from the pinned host bank into the victim slots) on
+ * the library's transfer stream; never synchronises with the host.
+ * Policy: unique ids ascend by flat id; hits are stamped clock+r, fills
+ * clock+hits+i, clock += hits+q; victims are the q smallest (stamp, slot)
+ * among slots not hit by this call (empty slots have stamp 0); the i-th fill
+ * takes the i-th victim; host-run misses leave residency and recency unchanged.
+ * Errors: FT_ERR_ARG (layer, T > max_tokens, null ids), FT_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+ft_status ft_cache_classify(ft_cache* cache, int32_t layer, int32_t* ids, int32_t T,
+                            const ft_classify_out* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ft_moe_forward — the routed SwiGLU expert FFN and the weighted top-k
+ * combine: y[t] = sum_j w[t,j] * FFN_{layer, e(t,j)}(x[t]), accumulated in
+ * fp32, written as bf16 (expert FFN with a gate/up and a down projection read
+ * from one slot record: "The Expert Cache That Follows the Router", section
+ * "One logical expert, two physical levels of memory"; exact merge of the GPU
+ * and host partial sums: METAL MEDIA summary, Figure 2 caption).
+ * mode FT_MODE_CACHED: routes are the in-place output of the preceding
+ *   ft_cache_classify for this layer.  Slot routes run on the GPU from the
+ *   slot pool (after that call's fills complete); -(1+e) routes run on the
+ *   library's host workers from the host bank (never from a slot, residency
+ *   unchanged: same page, paragraph on the host source as fallback); the
+ *   partial sums merge before the bf16 rounding.
+ * mode FT_MODE_STREAMED (needs num_slots >= 2E, else FT_ERR_STATE): routes are
+ *   raw expert ids 0..E-1; the layer is computed from full-layer buffer
+ *   layer % 2 (slots [b*E, (b+1)*E)), loading it first on the transfer stream
+ *   if it does not already hold `layer`; loading invalidates the previous
+ *   owners of those slots ("The Expert Cache That Follows the Router",
+ *   paragraphs on prefill buffers and on the release event and beginning
+ *   fence).  With FT_PREFETCH_NEXT the load of layer+1 into the other buffer
+ *   is enqueued after this layer's compute is issued, so that it overlaps it
+ *   ("Making Large MoE Models Practical on a Single Machine", section 2).
+ * x [T x d] bf16, routes [T x k] int32, w [T x k] fp32, y [T x d] bf16: device.
+ * Errors: FT_ERR_ARG, FT_ERR_STATE, FT_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+ft_status ft_moe_forward(ft_cache* cache, int32_t layer, int32_t mode, const uint16_t* x,
+                         const int32_t* routes, const float* w, int32_t T, uint16_t* y, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ft_cache_resize — rebuild the slot cache for a new slot count at a safe
+ * point (METAL MEDIA summary, item 4; hyper.ai summary, section 方法: the GPU
+ * expert cache is rebuilt against a revised VRAM budget without restarting).
+ * The caller guarantees no work is pending on this cache.  Keeps the
+ * min(new_num_slots, residents) entries with the largest stamps, packed into
+ * slots 0.. in ascending old-slot order, stamps and clock unchanged; every
+ * other new slot is empty.  Synchronises.  Errors: FT_ERR_ARG, FT_ERR_NOMEM
+ * (the old cache is then unchanged), FT_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+ft_status ft_cache_resize(ft_cache* cache, int64_t new_num_slots);
+
+/* Counters and sticky error flags (synchronises). */
+ft_status ft_cache_stats(const ft_cache* cache, ft_stats* out);
+
+/* Copy the maps to host memory (synchronises): slot_for_id [L*E],
+ * id_of_slot [N], stamp [N]; any pointer may be NULL. */
+ft_status ft_cache_snapshot(const ft_cache* cache, int32_t* slot_for_id, int32_t* id_of_slot,
+                            uint64_t* stamp, uint64_t* clock);
+
+/* Copy slot `slot`'s S record bytes to host memory `dst` (synchronises). */
+ft_status ft_cache_read_slot(const ft_cache* cache, int64_t slot, void* dst);
+
+/* Pinned, device-mapped host memory for host banks (hipHostMalloc).  Banks
+ * larger than torch's power-of-two pinned allocator can serve come from here. */
+ft_status ft_host_alloc(size_t bytes, void** ptr);
+ft_status ft_host_free(void* ptr);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* ft_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FTMOE_H */

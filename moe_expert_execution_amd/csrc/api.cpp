@@ -1,0 +1,493 @@
+// The C ABI of the routed-expert MoE layer (include/ftmoe.h): argument
+// validation, resource ownership, stream/event ordering, and the calls that
+// enqueue the kernels.  No C++ exception crosses the boundary.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "common.h"
+
+namespace ftmoe {
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+bool record_layout(const ft_shape& s, RecordLayout* o) {
+    const int64_t d = s.d_model, f = s.d_ff, fd = d * f;
+    if (d <= 0 || f <= 0 || d % 128 || f % 128) return false;
+    switch (s.fmt) {
+        case FT_FMT_BF16:
+            o->off_gate = 0;
+            o->off_up = 2 * fd;
+            o->off_down = 4 * fd;
+            o->off_sg = o->off_su = o->off_sd = 0;
+            o->S = 6 * fd;
+            return true;
+        case FT_FMT_FP8_B128: {
+            const int64_t nb = (d / 128) * (f / 128);
+            o->off_gate = 0;
+            o->off_up = fd;
+            o->off_down = 2 * fd;
+            o->off_sg = 3 * fd;
+            o->off_su = 3 * fd + 4 * nb;
+            o->off_sd = 3 * fd + 8 * nb;
+            o->S = 3 * fd + 12 * nb;
+            return true;
+        }
+        case FT_FMT_MXFP4_B32: {
+            const int64_t cb = fd / 2, sb = fd / 32;
+            o->off_gate = 0;
+            o->off_up = cb;
+            o->off_down = 2 * cb;
+            o->off_sg = 3 * cb;
+            o->off_su = 3 * cb + sb;
+            o->off_sd = 3 * cb + 2 * sb;
+            o->S = 3 * cb + 3 * sb;
+            return true;
+        }
+    }
+    return false;
+}
+
+namespace {
+
+template <typename T>
+hipError_t dalloc(T** p, size_t n) {
+    return hipMalloc(reinterpret_cast<void**>(p), n * sizeof(T) + 256);
+}
+
+ft_status check_shape(const ft_shape* s) {
+    FT_REQUIRE(s, "shape is null");
+    FT_REQUIRE(s->layers >= 1, "layers must be >= 1");
+    FT_REQUIRE(s->experts >= 1 && s->experts <= kMaxExperts, "experts must be in 1..%d", kMaxExperts);
+    FT_REQUIRE(s->top_k >= 1 && s->top_k <= kMaxTopK && s->top_k <= s->experts, "top_k must be in 1..min(E, %d)",
+               kMaxTopK);
+    FT_REQUIRE((int64_t)s->layers * s->experts < (1ll << 31), "layers * experts too large");
+    RecordLayout rl;
+    FT_REQUIRE(record_layout(*s, &rl), "d_model and d_ff must be positive multiples of 128 and fmt valid");
+    return FT_OK;
+}
+
+void free_cache(ft_cache* c) {
+    if (!c) return;
+    (void)hipDeviceSynchronize();
+    if (c->host) host_branch_destroy(c->host);
+    void* bufs[] = {c->pool, c->slot_for_id, c->id_of_slot, c->stamp, c->clock, c->counters, c->errflag,
+                    c->wl_counts, c->wl_slot, c->wl_src, c->plan.meta, c->plan.active_slot, c->plan.seg,
+                    c->plan.perm, c->plan.route_pos, c->plan.tile_active, c->plan.tile_row0,
+                    c->plan.chunk_counts, c->H, c->Y, c->Pdev, c->gv_part, c->gv_counters, c->gv_H};
+    for (void* b : bufs)
+        if (b) (void)hipFree(b);
+    hipEvent_t evs[] = {c->ev_ctrl, c->ev_fwd, c->ev_host, c->ev_xlast, c->ev_fence,
+                        c->ready[0], c->ready[1], c->release[0], c->release[1]};
+    for (hipEvent_t e : evs)
+        if (e) (void)hipEventDestroy(e);
+    if (c->xfer) (void)hipStreamDestroy(c->xfer);
+    if (c->hstream) (void)hipStreamDestroy(c->hstream);
+    delete c;
+}
+
+// Buffers whose size depends on the slot count.
+hipError_t alloc_plan(ft_cache* c) {
+    const int64_t cap = c->cap;
+    const int64_t act = std::min<int64_t>(cap, std::max<int64_t>(c->N, c->sh.experts));
+    c->plan.max_tiles = (cap + gemm_tile_m() - 1) / gemm_tile_m() + act + 1;
+    const int64_t keyspace = std::max<int64_t>(c->N, c->sh.experts);
+    const int64_t chunks = (c->max_tokens + kChunkTokens - 1) / kChunkTokens;
+    hipError_t e;
+    if ((e = dalloc(&c->plan.tile_active, c->plan.max_tiles))) return e;
+    if ((e = dalloc(&c->plan.tile_row0, c->plan.max_tiles))) return e;
+    if ((e = dalloc(&c->plan.chunk_counts, chunks * std::min<int64_t>(keyspace, 8192)))) return e;
+    return hipSuccess;
+}
+
+ft_status enqueue_load(ft_cache* c, int layer, int buf, hipStream_t st) {
+    // the buffer's previous layer must be done; the first load after decode
+    // work waits for everything already on the caller's stream (beginning fence)
+    if (!c->streaming) {
+        FT_HIP(hipEventRecord(c->ev_fence, st));
+        FT_HIP(hipStreamWaitEvent(c->xfer, c->ev_fence, 0));
+        c->streaming = true;
+    }
+    if (c->release_recorded[buf]) FT_HIP(hipStreamWaitEvent(c->xfer, c->release[buf], 0));
+    FT_HIP(launch_invalidate(c, buf, c->xfer));
+    const int64_t E = c->sh.experts, S = c->rl.S;
+    FT_HIP(hipMemcpyAsync(c->pool + (int64_t)buf * E * S, c->bank_host + (int64_t)layer * E * S, E * S,
+                          hipMemcpyHostToDevice, c->xfer));
+    FT_HIP(hipEventRecord(c->ready[buf], c->xfer));
+    FT_HIP(hipEventRecord(c->ev_xlast, c->xfer));
+    c->xfer_pending = true;
+    c->buf_layer[buf] = layer;
+    return FT_OK;
+}
+
+}  // namespace
+}  // namespace ftmoe
+
+using namespace ftmoe;
+
+extern "C" {
+
+const char* ft_last_error(void) { return g_err; }
+
+int64_t ft_record_bytes(const ft_shape* shape) {
+    RecordLayout rl;
+    if (!shape || !record_layout(*shape, &rl)) return 0;
+    return rl.S;
+}
+
+ft_status ft_host_alloc(size_t bytes, void** ptr) {
+    clear_error();
+    FT_REQUIRE(ptr && bytes > 0, "ptr must be non-null and bytes > 0");
+    hipError_t e = hipHostMalloc(ptr, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        set_error("hipHostMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+        *ptr = nullptr;
+        return FT_ERR_NOMEM;
+    }
+    return FT_OK;
+}
+
+ft_status ft_host_free(void* ptr) {
+    clear_error();
+    if (ptr) FT_HIP(hipHostFree(ptr));
+    return FT_OK;
+}
+
+ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, const void* host_bank,
+                          int64_t num_slots, int32_t max_tokens, ft_cache** out) {
+    clear_error();
+    FT_REQUIRE(out, "out is null");
+    *out = nullptr;
+    ft_status st = check_shape(shape);
+    if (st != FT_OK) return st;
+    FT_REQUIRE(profile && profile->bp_mbps > 0 && profile->bh_mbps > 0, "profile bandwidths must be > 0");
+    FT_REQUIRE(profile->max_fetch >= -1, "max_fetch must be >= -1");
+    FT_REQUIRE(host_bank, "host bank is null");
+    FT_REQUIRE(num_slots >= 1 && num_slots <= kMaxSlots, "num_slots must be in 1..%d", kMaxSlots);
+    FT_REQUIRE(max_tokens >= 1 && max_tokens <= 65535, "max_tokens must be in 1..65535");
+    FT_REQUIRE((int64_t)max_tokens * shape->top_k <= (1 << 24), "max_tokens * top_k too large");
+
+    ft_cache* c = new (std::nothrow) ft_cache();
+    if (!c) return FT_ERR_NOMEM;
+    memset(c, 0, sizeof(*c));
+    c->sh = *shape;
+    c->prof = *profile;
+    record_layout(*shape, &c->rl);
+    c->N = num_slots;
+    c->max_tokens = max_tokens;
+    c->cap = max_tokens * shape->top_k;
+    c->buf_layer[0] = c->buf_layer[1] = -1;
+    c->bank_host = static_cast<const uint8_t*>(host_bank);
+#define CK(call)                                                                             \
+    do {                                                                                     \
+        hipError_t e_ = (call);                                                              \
+        if (e_ != hipSuccess) {                                                              \
+            set_error("%s failed: %s", #call, hipGetErrorString(e_));                        \
+            free_cache(c);                                                                   \
+            return e_ == hipErrorOutOfMemory ? FT_ERR_NOMEM : FT_ERR_HIP;                    \
+        }                                                                                    \
+    } while (0)
+    CK(hipGetDevice(&c->device));
+    void* dptr = nullptr;
+    if (hipHostGetDevicePointer(&dptr, const_cast<void*>(host_bank), 0) != hipSuccess || !dptr) {
+        (void)hipGetLastError();
+        free_cache(c);
+        set_error("host bank must be pinned host memory (ft_host_alloc / hipHostMalloc)");
+        return FT_ERR_ARG;
+    }
+    c->bank_dev = static_cast<const uint8_t*>(dptr);
+    const int64_t L = shape->layers, E = shape->experts, S = c->rl.S, d = shape->d_model, f = shape->d_ff;
+    const int64_t cap = c->cap;
+    CK(hipMalloc(reinterpret_cast<void**>(&c->pool), (size_t)(c->N * S)));
+    CK(dalloc(&c->slot_for_id, L * E));
+    CK(dalloc(&c->id_of_slot, c->N));
+    CK(dalloc(&c->stamp, c->N));
+    CK(dalloc(&c->clock, 1));
+    CK(dalloc(&c->counters, C_N));
+    CK(dalloc(&c->errflag, 1));
+    CK(dalloc(&c->wl_counts, 4));
+    CK(dalloc(&c->wl_slot, cap));
+    CK(dalloc(&c->wl_src, cap));
+    CK(dalloc(&c->plan.meta, 4));
+    CK(dalloc(&c->plan.active_slot, cap));
+    CK(dalloc(&c->plan.seg, cap + 1));
+    CK(dalloc(&c->plan.perm, cap));
+    CK(dalloc(&c->plan.route_pos, cap));
+    CK(alloc_plan(c));
+    CK(dalloc(&c->H, cap * f));
+    CK(dalloc(&c->Y, cap * d));
+    CK(dalloc(&c->Pdev, (int64_t)max_tokens * d));
+    c->cap_gemv = std::min<int32_t>(max_tokens, kGemvMaxTokens) * shape->top_k;
+    CK(dalloc(&c->gv_part, (int64_t)8 * c->cap_gemv * f * 2));
+    CK(dalloc(&c->gv_counters, (int64_t)c->cap_gemv * (f / 16)));
+    CK(dalloc(&c->gv_H, (int64_t)c->cap_gemv * f));
+    CK(hipMemset(c->slot_for_id, 0xFF, sizeof(int32_t) * L * E));
+    CK(hipMemset(c->id_of_slot, 0xFF, sizeof(int32_t) * c->N));
+    CK(hipMemset(c->stamp, 0, sizeof(uint64_t) * c->N));
+    const uint64_t one = 1;
+    CK(hipMemcpy(c->clock, &one, sizeof(one), hipMemcpyHostToDevice));
+    CK(hipMemset(c->counters, 0, sizeof(unsigned long long) * C_N));
+    CK(hipMemset(c->errflag, 0, sizeof(int32_t)));
+    CK(hipMemset(c->gv_counters, 0, sizeof(int32_t) * c->cap_gemv * (f / 16)));
+    CK(hipMemset(c->plan.meta, 0, sizeof(int32_t) * 4));
+    CK(hipStreamCreateWithFlags(&c->xfer, hipStreamNonBlocking));
+    CK(hipStreamCreateWithFlags(&c->hstream, hipStreamNonBlocking));
+    hipEvent_t* evs[] = {&c->ev_ctrl, &c->ev_fwd, &c->ev_host, &c->ev_xlast, &c->ev_fence,
+                         &c->ready[0], &c->ready[1], &c->release[0], &c->release[1]};
+    for (hipEvent_t* e : evs) CK(hipEventCreateWithFlags(e, hipEventDisableTiming));
+    CK(hipDeviceSynchronize());
+#undef CK
+    c->host = host_branch_create(*shape, c->rl, c->bank_host, max_tokens);
+    if (!c->host) {
+        free_cache(c);
+        set_error("host branch: pinned staging allocation failed");
+        return FT_ERR_NOMEM;
+    }
+    *out = c;
+    return FT_OK;
+}
+
+ft_status ft_cache_destroy(ft_cache* cache) {
+    clear_error();
+    free_cache(cache);
+    return FT_OK;
+}
+
+ft_status ft_moe_route(const ft_shape* shape, const uint16_t* x, const uint16_t* wr, int32_t T, int32_t* ids,
+                       float* w, void* stream) {
+    clear_error();
+    FT_REQUIRE(shape, "shape is null");
+    FT_REQUIRE(shape->experts >= 1 && shape->experts <= 256, "routing supports 1..256 experts");
+    FT_REQUIRE(shape->top_k >= 1 && shape->top_k <= shape->experts && shape->top_k <= kMaxTopK, "bad top_k");
+    FT_REQUIRE(shape->d_model >= 1, "bad d_model");
+    FT_REQUIRE(T >= 0, "T must be >= 0");
+    if (T == 0) return FT_OK;
+    FT_REQUIRE(x && wr && ids && w, "null pointer");
+    FT_HIP(launch_route(x, wr, T, shape->d_model, shape->experts, shape->top_k, ids, w, (hipStream_t)stream));
+    return FT_OK;
+}
+
+ft_status ft_cache_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t T, const ft_classify_out* out,
+                            void* stream) {
+    clear_error();
+    FT_REQUIRE(c, "cache is null");
+    FT_REQUIRE(layer >= 0 && layer < c->sh.layers, "layer %d out of range", layer);
+    FT_REQUIRE(T >= 1 && T <= c->max_tokens, "T must be in 1..max_tokens (%d)", c->max_tokens);
+    FT_REQUIRE(ids, "ids is null");
+    if (out) {
+        FT_REQUIRE(out->counts, "out->counts is null");
+        FT_REQUIRE(out->capacity >= T * c->sh.top_k, "out capacity %d < T*k", out->capacity);
+    }
+    hipStream_t st = (hipStream_t)stream;
+    // earlier fills and full-layer loads must be done before the maps are read
+    if (c->xfer_pending) FT_HIP(hipStreamWaitEvent(st, c->ev_xlast, 0));
+    c->streaming = false;
+    c->buf_layer[0] = c->buf_layer[1] = -1;     // decode fills may reuse buffer slots
+    FT_HIP(launch_classify(c, layer, ids, T * c->sh.top_k, out, st));
+    FT_HIP(hipEventRecord(c->ev_ctrl, st));
+    FT_HIP(hipStreamWaitEvent(c->xfer, c->ev_ctrl, 0));
+    FT_HIP(launch_fill(c, c->xfer));
+    FT_HIP(hipEventRecord(c->ev_xlast, c->xfer));
+    c->xfer_pending = true;
+    return FT_OK;
+}
+
+ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_t* x, const int32_t* routes,
+                         const float* w, int32_t T, uint16_t* y, void* stream) {
+    clear_error();
+    FT_REQUIRE(c, "cache is null");
+    FT_REQUIRE(layer >= 0 && layer < c->sh.layers, "layer %d out of range", layer);
+    FT_REQUIRE(T >= 1 && T <= c->max_tokens, "T must be in 1..max_tokens (%d)", c->max_tokens);
+    FT_REQUIRE(x && routes && w && y, "null pointer");
+    const int m = mode & 0xFF;
+    FT_REQUIRE(m == FT_MODE_CACHED || m == FT_MODE_STREAMED, "unknown mode %d", m);
+    FT_REQUIRE((mode & ~0x1FF) == 0, "unknown flags");
+    hipStream_t st = (hipStream_t)stream;
+    const int k = c->sh.top_k;
+    const int64_t d = c->sh.d_model;
+    const bool gemv = T <= kGemvMaxTokens;
+    if (m == FT_MODE_CACHED) {
+        // host branch: copy the call's routes, weights and activations to pinned
+        // staging, run the host experts, copy their partial sum back
+        HostStaging hs = host_branch_staging(c->host);
+        FT_HIP(hipEventRecord(c->ev_fwd, st));
+        FT_HIP(hipStreamWaitEvent(c->hstream, c->ev_fwd, 0));
+        FT_HIP(hipMemcpyAsync(hs.routes, routes, sizeof(int32_t) * T * k, hipMemcpyDeviceToHost, c->hstream));
+        FT_HIP(hipMemcpyAsync(hs.w, w, sizeof(float) * T * k, hipMemcpyDeviceToHost, c->hstream));
+        FT_HIP(hipMemcpyAsync(hs.x, x, sizeof(uint16_t) * T * d, hipMemcpyDeviceToHost, c->hstream));
+        FT_HIP(host_branch_enqueue(c->host, layer, T, c->hstream));
+        FT_HIP(hipMemcpyAsync(c->Pdev, hs.P, sizeof(float) * T * d, hipMemcpyHostToDevice, c->hstream));
+        FT_HIP(hipEventRecord(c->ev_host, c->hstream));
+        // GPU experts (hits and fills) from the slot pool
+        FT_HIP(launch_plan(c, routes, T, -1, gemm_tile_m(), st));
+        if (c->xfer_pending) FT_HIP(hipStreamWaitEvent(st, c->ev_xlast, 0));
+        FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
+        FT_HIP(hipStreamWaitEvent(st, c->ev_host, 0));
+        FT_HIP(launch_combine(c, routes, w, T, true, y, st));
+        return FT_OK;
+    }
+    // STREAMED: full-layer buffer layer % 2
+    const int E = c->sh.experts;
+    if (c->N < 2 * (int64_t)E) {
+        set_error("STREAMED mode needs num_slots >= 2E (%lld < %d)", (long long)c->N, 2 * E);
+        return FT_ERR_STATE;
+    }
+    if (!gemv && (int64_t)T * k > kSmallPlanRoutes && E > 8192) {
+        set_error("too many experts for the chunked planner");
+        return FT_ERR_UNSUPPORTED;
+    }
+    const int b = layer % 2;
+    if (c->buf_layer[b] != layer) {
+        ft_status s = enqueue_load(c, layer, b, st);
+        if (s != FT_OK) return s;
+    }
+    FT_HIP(hipStreamWaitEvent(st, c->ready[b], 0));
+    FT_HIP(launch_plan(c, routes, T, b * E, gemm_tile_m(), st));
+    FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
+    FT_HIP(launch_combine(c, routes, w, T, false, y, st));
+    FT_HIP(hipEventRecord(c->release[b], st));
+    c->release_recorded[b] = true;
+    if ((mode & FT_PREFETCH_NEXT) && layer + 1 < c->sh.layers) {
+        const int nb = (layer + 1) % 2;
+        if (c->buf_layer[nb] != layer + 1) {
+            ft_status s = enqueue_load(c, layer + 1, nb, st);
+            if (s != FT_OK) return s;
+        }
+    }
+    return FT_OK;
+}
+
+ft_status ft_cache_resize(ft_cache* c, int64_t new_num_slots) {
+    clear_error();
+    FT_REQUIRE(c, "cache is null");
+    FT_REQUIRE(new_num_slots >= 1 && new_num_slots <= kMaxSlots, "num_slots must be in 1..%d", kMaxSlots);
+    FT_HIP(hipDeviceSynchronize());
+    const int64_t L = c->sh.layers, E = c->sh.experts, S = c->rl.S, N = c->N, Nn = new_num_slots;
+    std::vector<int32_t> ios(N);
+    std::vector<uint64_t> stamp(N);
+    FT_HIP(hipMemcpy(ios.data(), c->id_of_slot, sizeof(int32_t) * N, hipMemcpyDeviceToHost));
+    FT_HIP(hipMemcpy(stamp.data(), c->stamp, sizeof(uint64_t) * N, hipMemcpyDeviceToHost));
+    std::vector<int32_t> res;
+    for (int64_t s = 0; s < N; ++s)
+        if (ios[s] >= 0) res.push_back((int32_t)s);
+    std::stable_sort(res.begin(), res.end(), [&](int32_t a, int32_t b) { return stamp[a] > stamp[b]; });
+    if ((int64_t)res.size() > Nn) res.resize(Nn);
+    std::sort(res.begin(), res.end());
+    // new arrays first: on failure the old cache is untouched
+    uint8_t* npool = nullptr;
+    int32_t *nios = nullptr, *src = nullptr, *ntile_a = nullptr, *ntile_r = nullptr, *ncc = nullptr;
+    uint64_t* nstamp = nullptr;
+    auto fail = [&](hipError_t e) {
+        (void)hipFree(npool);
+        (void)hipFree(nios);
+        (void)hipFree(src);
+        (void)hipFree(nstamp);
+        set_error("resize allocation failed: %s", hipGetErrorString(e));
+        return e == hipErrorOutOfMemory ? FT_ERR_NOMEM : FT_ERR_HIP;
+    };
+    hipError_t e;
+    if ((e = hipMalloc(reinterpret_cast<void**>(&npool), (size_t)(Nn * S)))) return fail(e);
+    if ((e = dalloc(&nios, Nn))) return fail(e);
+    if ((e = dalloc(&nstamp, Nn))) return fail(e);
+    if ((e = dalloc(&src, std::max<size_t>(res.size(), 1)))) return fail(e);
+    std::vector<int32_t> h_ios(Nn, -1), h_sfi(L * E, -1);
+    std::vector<uint64_t> h_st(Nn, 0);
+    for (size_t i = 0; i < res.size(); ++i) {
+        h_ios[i] = ios[res[i]];
+        h_st[i] = stamp[res[i]];
+        h_sfi[ios[res[i]]] = (int32_t)i;
+    }
+    if (!res.empty()) {
+        if ((e = hipMemcpy(src, res.data(), sizeof(int32_t) * res.size(), hipMemcpyHostToDevice))) return fail(e);
+        if ((e = launch_resize_gather(c->pool, npool, S, src, (int)res.size(), 0))) return fail(e);
+        if ((e = hipDeviceSynchronize())) return fail(e);
+    }
+    FT_HIP(hipMemcpy(nios, h_ios.data(), sizeof(int32_t) * Nn, hipMemcpyHostToDevice));
+    FT_HIP(hipMemcpy(nstamp, h_st.data(), sizeof(uint64_t) * Nn, hipMemcpyHostToDevice));
+    FT_HIP(hipMemcpy(c->slot_for_id, h_sfi.data(), sizeof(int32_t) * L * E, hipMemcpyHostToDevice));
+    (void)hipFree(src);
+    (void)hipFree(c->pool);
+    (void)hipFree(c->id_of_slot);
+    (void)hipFree(c->stamp);
+    c->pool = npool;
+    c->id_of_slot = nios;
+    c->stamp = nstamp;
+    c->N = Nn;
+    (void)hipFree(c->plan.tile_active);
+    (void)hipFree(c->plan.tile_row0);
+    (void)hipFree(c->plan.chunk_counts);
+    c->plan.tile_active = c->plan.tile_row0 = c->plan.chunk_counts = nullptr;
+    (void)ntile_a;
+    (void)ntile_r;
+    (void)ncc;
+    FT_HIP(alloc_plan(c));
+    c->buf_layer[0] = c->buf_layer[1] = -1;
+    c->release_recorded[0] = c->release_recorded[1] = false;
+    c->xfer_pending = false;
+    c->streaming = false;
+    FT_HIP(hipDeviceSynchronize());
+    return FT_OK;
+}
+
+ft_status ft_cache_stats(const ft_cache* c, ft_stats* o) {
+    clear_error();
+    FT_REQUIRE(c && o, "null pointer");
+    FT_HIP(hipDeviceSynchronize());
+    unsigned long long cnt[C_N];
+    uint64_t clk;
+    int32_t err;
+    FT_HIP(hipMemcpy(cnt, c->counters, sizeof(cnt), hipMemcpyDeviceToHost));
+    FT_HIP(hipMemcpy(&clk, c->clock, sizeof(clk), hipMemcpyDeviceToHost));
+    FT_HIP(hipMemcpy(&err, c->errflag, sizeof(err), hipMemcpyDeviceToHost));
+    o->calls = cnt[C_CALLS];
+    o->routes = cnt[C_ROUTES];
+    o->unique = cnt[C_UNIQUE];
+    o->hits = cnt[C_HITS];
+    o->misses = cnt[C_MISSES];
+    o->fills = cnt[C_FILLS];
+    o->cpu_experts = cnt[C_CPU];
+    o->evictions = cnt[C_EVICT];
+    o->bytes_filled = cnt[C_BYTES];
+    o->layers_streamed = cnt[C_STREAMED];
+    o->clock = clk;
+    o->error_flags = err;
+    o->num_slots = (int32_t)c->N;
+    return FT_OK;
+}
+
+ft_status ft_cache_snapshot(const ft_cache* c, int32_t* slot_for_id, int32_t* id_of_slot, uint64_t* stamp,
+                            uint64_t* clock) {
+    clear_error();
+    FT_REQUIRE(c, "cache is null");
+    FT_HIP(hipDeviceSynchronize());
+    const int64_t LE = (int64_t)c->sh.layers * c->sh.experts;
+    if (slot_for_id) FT_HIP(hipMemcpy(slot_for_id, c->slot_for_id, sizeof(int32_t) * LE, hipMemcpyDeviceToHost));
+    if (id_of_slot) FT_HIP(hipMemcpy(id_of_slot, c->id_of_slot, sizeof(int32_t) * c->N, hipMemcpyDeviceToHost));
+    if (stamp) FT_HIP(hipMemcpy(stamp, c->stamp, sizeof(uint64_t) * c->N, hipMemcpyDeviceToHost));
+    if (clock) FT_HIP(hipMemcpy(clock, c->clock, sizeof(uint64_t), hipMemcpyDeviceToHost));
+    return FT_OK;
+}
+
+ft_status ft_cache_read_slot(const ft_cache* c, int64_t slot, void* dst) {
+    clear_error();
+    FT_REQUIRE(c && dst, "null pointer");
+    FT_REQUIRE(slot >= 0 && slot < c->N, "slot out of range");
+    FT_HIP(hipDeviceSynchronize());
+    FT_HIP(hipMemcpy(dst, c->pool + slot * c->rl.S, (size_t)c->rl.S, hipMemcpyDeviceToHost));
+    return FT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Weighted top-k combine: y[t] = sum over the token's GPU routes, j ascending,
+// of w[t,j] * Y[row(t,j)], plus the host branch's partial sum P[t] when the
+// token has routes executed on the host; accumulated in fp32 and rounded once
+// to bf16.  The GPU and host partial outputs merge into the layer output
+// (METAL MEDIA summary, Figure 2 caption; hyper.ai summary, section 方法).
+#include "wfmt.h"
+
+namespace ftmoe {
+namespace {
+
+constexpr int kCombThreads = 256;
+
+__global__ void __launch_bounds__(kCombThreads)
+    combine_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ route_pos,
+                   const float* __restrict__ w, const float* __restrict__ Y, const float* __restrict__ P, int T,
+                   int k, int d, int has_host, uint16_t* __restrict__ y) {
+    const int t = blockIdx.y;
+    const int c = (blockIdx.x * kCombThreads + threadIdx.x) * 4;
+    if (t >= T || c >= d) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool host = false;
+    for (int j = 0; j < k; ++j) {
+        const int r = t * k + j;
+        const int p = route_pos[r];
+        if (p >= 0) {
+            const float wj = w[r];
+            const float4 v = *reinterpret_cast<const float4*>(Y + (int64_t)p * d + c);
+            acc.x = fmaf(wj, v.x, acc.x);
+            acc.y = fmaf(wj, v.y, acc.y);
+            acc.z = fmaf(wj, v.z, acc.z);
+            acc.w = fmaf(wj, v.w, acc.w);
+        } else {
+            const int rv = routes[r];
+            host |= (rv < 0 && rv != INT32_MIN);
+        }
+    }
+    if (has_host && host) {
+        const float4 v = *reinterpret_cast<const float4*>(P + (int64_t)t * d + c);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+    o.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+    *reinterpret_cast<uint2*>(y + (int64_t)t * d + c) = o;
+}
+
+}  // namespace
+
+hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, bool has_host, uint16_t* y,
+                          hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    const int d = c->sh.d_model;
+    dim3 grid((d / 4 + kCombThreads - 1) / kCombThreads, T);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, st, routes, c->plan.route_pos, w, c->Y,
+                       c->Pdev, T, c->sh.top_k, d, has_host ? 1 : 0, y);
+    return hipGetLastError();
+}
+
+}  // namespace ftmoe

@@ -1,0 +1,152 @@
+// Internal declarations shared by the ftmoe library sources (gfx950, HIP).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <string>
+
+#include "ftmoe.h"
+
+namespace ftmoe {
+
+// ---- limits ---------------------------------------------------------------
+constexpr int kMaxExperts = 4096;      // E
+constexpr int kMaxSlots = 32768;       // N
+constexpr int kMaxTopK = 16;           // k
+constexpr int kCtrlThreads = 1024;     // one control workgroup
+constexpr int kKeysPerThread = kMaxSlots / kCtrlThreads;   // victim keys held per thread
+constexpr uint64_t kStampLimit = 1ull << 40;               // stamps fit 40 bits; slot 24 bits
+constexpr int kChunkTokens = 64;       // tokens per stable-sort chunk (one 64-bit mask)
+constexpr int kSmallPlanRoutes = 1024; // routes handled by the one-workgroup planner
+constexpr int kGemvMaxTokens = 4;      // tokens per call served by the GEMV path
+
+// device counters (ft_stats order)
+enum { C_CALLS, C_ROUTES, C_UNIQUE, C_HITS, C_MISSES, C_FILLS, C_CPU, C_EVICT, C_BYTES, C_STREAMED, C_N };
+
+// ---- error plumbing -----------------------------------------------------------
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define FT_HIP(call)                                                                    \
+    do {                                                                                \
+        hipError_t e_ = (call);                                                         \
+        if (e_ != hipSuccess) {                                                         \
+            ::ftmoe::set_error("%s failed: %s (%s:%d)", #call, hipGetErrorString(e_),   \
+                               __FILE__, __LINE__);                                     \
+            return FT_ERR_HIP;                                                          \
+        }                                                                               \
+    } while (0)
+
+#define FT_REQUIRE(cond, ...)                          \
+    do {                                               \
+        if (!(cond)) {                                 \
+            ::ftmoe::set_error(__VA_ARGS__);           \
+            return FT_ERR_ARG;                         \
+        }                                              \
+    } while (0)
+
+// ---- record geometry ------------------------------------------------------------
+struct RecordLayout {
+    int64_t S;             // bytes per record
+    int64_t off_gate, off_up, off_down;         // code / value offsets
+    int64_t off_sg, off_su, off_sd;             // scale offsets (fp8, mxfp4)
+};
+bool record_layout(const ft_shape& s, RecordLayout* out);
+
+// ---- the host branch ------------------------------------------------------------
+struct HostBranch;
+HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const uint8_t* bank_host,
+                               int32_t max_tokens);
+void host_branch_destroy(HostBranch* hb);
+// Pinned staging owned by the host branch (device-visible for async copies).
+struct HostStaging {
+    uint16_t* x;       // [max_tokens x d]
+    int32_t* routes;   // [max_tokens x k]
+    float* w;          // [max_tokens x k]
+    float* P;          // [max_tokens x d]
+};
+HostStaging host_branch_staging(HostBranch* hb);
+// Enqueue the host computation of layer `layer` for T tokens on `stream`
+// (staging must already hold routes, w and x for those tokens).
+hipError_t host_branch_enqueue(HostBranch* hb, int32_t layer, int32_t T, hipStream_t stream);
+int host_branch_threads(HostBranch* hb);
+
+// ---- the cache handle ---------------------------------------------------------
+struct PlanBuffers {
+    int32_t* meta;          // [4]: n_active, n_tiles, n_gpu_routes, unused
+    int32_t* active_slot;   // [cap]
+    int32_t* seg;           // [cap + 1]: sorted-row offset of each active slot
+    int32_t* perm;          // [cap]: route index of each sorted row
+    int32_t* route_pos;     // [cap]: sorted row of each route, -1 if not on the GPU
+    int32_t* tile_active;   // [max tiles]
+    int32_t* tile_row0;     // [max tiles]
+    int32_t* chunk_counts;  // [chunks x keyspace] (large planner)
+    int64_t max_tiles;
+};
+
+}  // namespace ftmoe
+
+struct ft_cache {
+    ft_shape sh;
+    ft_profile prof;
+    ftmoe::RecordLayout rl;
+    int64_t N;
+    int32_t max_tokens;
+    int32_t cap;               // max_tokens * k
+    int device;
+    const uint8_t* bank_host;
+    const uint8_t* bank_dev;   // device-visible address of the pinned bank
+    uint8_t* pool;             // N * S bytes of HBM
+    // control state (device)
+    int32_t* slot_for_id;      // [L*E]
+    int32_t* id_of_slot;       // [N]
+    uint64_t* stamp;           // [N]
+    uint64_t* clock;           // [1]
+    unsigned long long* counters;  // [C_N]
+    int32_t* errflag;          // [1]
+    // internal copy of the last classify's fill worklist and counts
+    int32_t* wl_counts;        // [4]
+    int32_t* wl_slot;          // [cap]
+    int32_t* wl_src;           // [cap]
+    // forward scratch
+    ftmoe::PlanBuffers plan;
+    uint16_t* H;               // [cap x f] bf16 (GEMM path)
+    float* Y;                  // [cap x d] fp32
+    float* Pdev;               // [max_tokens x d] fp32
+    int32_t cap_gemv;          // rows served by the GEMV path
+    float* gv_part;            // GEMV K-split partials
+    int32_t* gv_counters;      // GEMV last-block counters (self-resetting)
+    float* gv_H;               // [cap_gemv x f] fp32 (GEMV path)
+    // streams and events
+    hipStream_t xfer;          // transfer stream (fills, full-layer loads)
+    hipStream_t hstream;       // host-branch copies and host function
+    hipEvent_t ev_ctrl, ev_fwd, ev_host, ev_xlast, ev_fence;
+    bool xfer_pending;         // ev_xlast recorded
+    bool streaming;            // inside a run of STREAMED calls (beginning fence taken)
+    // full-layer buffers
+    int buf_layer[2];
+    hipEvent_t ready[2], release[2];
+    bool release_recorded[2];
+    ftmoe::HostBranch* host;
+};
+
+namespace ftmoe {
+// ---- kernel launchers (each returns hipGetLastError() of its launches) ----
+hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int d, int E, int k, int32_t* ids,
+                        float* w, hipStream_t st);
+hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, const ft_classify_out* out,
+                           hipStream_t st);
+hipError_t launch_fill(ft_cache* c, hipStream_t st);
+hipError_t launch_invalidate(ft_cache* c, int buf, hipStream_t st);
+hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t S, const int32_t* src_slots,
+                                int n, hipStream_t st);
+// plan: routes -> active slots, sorted rows, tiles.  slot_base >= 0 means routes
+// are raw expert ids mapped to slot slot_base + e (full-layer buffer).
+hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, hipStream_t st);
+hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
+hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
+hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, bool has_host,
+                          uint16_t* y, hipStream_t st);
+int gemm_tile_m();
+}  // namespace ftmoe

@@ -1,0 +1,326 @@
+// Token-to-slot sort/scan that builds the expert kernels' work lists.
+//
+// Input: routes [T x k] (slot ids for GPU routes; negative = host or invalid;
+// or, for a full-layer buffer, raw expert ids mapped to slot base + e).
+// Output (PlanBuffers): the GPU rows sorted by (slot, route index) — a stable
+// counting sort — with
+//   perm[p]        route index of sorted row p
+//   route_pos[r]   sorted row of route r, -1 when r is not a GPU route
+//   active_slot[a] the a-th slot with rows, ascending
+//   seg[a]         first sorted row of active slot a (seg[n_active] = rows)
+//   tile_active / tile_row0: BM-row tiles of each active slot
+//   meta           {n_active, n_tiles, n_rows}
+// A token that lists the same expert twice keeps only its first route; the
+// duplicate is dropped and error flag 4 is raised.
+//
+// Up to 1024 routes: one workgroup, bitonic sort of (slot, route) keys.
+// More: three kernels over 64-token chunks — per-chunk slot masks and counts,
+// one scan, then rank = chunk offset + popcount(mask below the token).
+#include "common.h"
+
+namespace ftmoe {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kLargeKeySpace = 8192;   // slots addressable by the chunked planner
+
+struct PlanArgs {
+    const int32_t* routes;
+    int32_t R, k, T;
+    int32_t slot_base;      // >= 0: routes are expert ids, slot = base + e
+    int32_t E;              // expert count (validates raw ids)
+    int32_t N;              // slots
+    int32_t bm;             // tile rows
+    int32_t key_space;      // large planner: keys 0..key_space-1
+    int32_t* errflag;
+    int32_t* meta;
+    int32_t* active_slot;
+    int32_t* seg;
+    int32_t* perm;
+    int32_t* route_pos;
+    int32_t* tile_active;
+    int32_t* tile_row0;
+    int32_t* chunk_counts;
+};
+
+// Slot of route r, or -1 when it is not a GPU route (host, invalid, duplicate).
+__device__ __forceinline__ int route_slot(const PlanArgs& a, int r) {
+    int v = a.routes[r];
+    int s;
+    if (a.slot_base >= 0) {
+        s = (v >= 0 && v < a.E) ? a.slot_base + v : -1;
+    } else {
+        s = (v >= 0 && v < a.N) ? v : -1;
+    }
+    if (s < 0) return -1;
+    const int t = r / a.k, j = r - t * a.k;
+    for (int jj = 0; jj < j; ++jj) {          // drop a repeated expert of the same token
+        if (a.routes[t * a.k + jj] == v) {
+            atomicOr(a.errflag, 4);
+            return -1;
+        }
+    }
+    return s;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int incl = wave_incl_scan(v, lane);
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int i = 0; i < kPlanThreads / 64; ++i) {
+        int s = wsum[i];
+        base += (i < wid) ? s : 0;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
+
+// Tiles of every active slot, in order.  Thread i handles active i.
+__device__ void emit_tiles(const PlanArgs& a, int n_active, int* wsum) {
+    int total_tiles = 0;
+    for (int base = 0; base < n_active; base += kPlanThreads) {
+        const int i = base + threadIdx.x;
+        int nt = 0, rows = 0, r0 = 0;
+        if (i < n_active) {
+            r0 = a.seg[i];
+            rows = a.seg[i + 1] - r0;
+            nt = (rows + a.bm - 1) / a.bm;
+        }
+        int tot;
+        int off = block_excl_scan(nt, wsum, &tot) + total_tiles;
+        for (int j = 0; j < nt; ++j) {
+            a.tile_active[off + j] = i;
+            a.tile_row0[off + j] = r0 + j * a.bm;
+        }
+        total_tiles += tot;
+    }
+    if (threadIdx.x == 0) a.meta[1] = total_tiles;
+}
+
+// ---- one-workgroup planner (R <= 1024) ------------------------------------------
+__global__ void __launch_bounds__(kPlanThreads) plan_small_kernel(PlanArgs a) {
+    __shared__ uint32_t keys[kSmallPlanRoutes];
+    __shared__ int wsum[kPlanThreads / 64];
+    const int tid = threadIdx.x;
+    int P = 1;
+    while (P < a.R) P <<= 1;
+
+    // key = slot << 10 | route (slot < 32768, route < 1024); non-GPU routes last
+    if (tid < P) {
+        uint32_t key = 0xFFFFFFFFu;
+        if (tid < a.R) {
+            int s = route_slot(a, tid);
+            if (s >= 0) key = ((uint32_t)s << 10) | (uint32_t)tid;
+            a.route_pos[tid] = -1;
+        }
+        keys[tid] = key;
+    }
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (tid < P) {
+                int partner = tid ^ stride;
+                if (partner > tid) {
+                    uint32_t x = keys[tid], y = keys[partner];
+                    bool up = (tid & size) == 0;
+                    if ((x > y) == up) {
+                        keys[tid] = y;
+                        keys[partner] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // rows, heads, active list
+    int valid = (tid < a.R && keys[tid] != 0xFFFFFFFFu) ? 1 : 0;
+    int rows;
+    block_excl_scan(valid, wsum, &rows);
+    int head = 0;
+    if (valid) {
+        uint32_t kk = keys[tid];
+        int r = (int)(kk & 1023u);
+        a.perm[tid] = r;
+        a.route_pos[r] = tid;
+        head = (tid == 0 || (keys[tid - 1] >> 10) != (kk >> 10)) ? 1 : 0;
+    }
+    int n_active;
+    int ai = block_excl_scan(head, wsum, &n_active);
+    if (head) {
+        a.active_slot[ai] = (int)(keys[tid] >> 10);
+        a.seg[ai] = tid;
+    }
+    if (tid == 0) {
+        a.seg[n_active] = rows;
+        a.meta[0] = n_active;
+        a.meta[2] = rows;
+    }
+    __syncthreads();
+    emit_tiles(a, n_active, wsum);
+}
+
+// ---- chunked planner (any R; key space <= 8192) --------------------------------
+// Kernel A: per 64-token chunk, the mask of tokens routed to each key, and its popcount.
+__global__ void __launch_bounds__(kPlanThreads) plan_count_kernel(PlanArgs a) {
+    __shared__ unsigned long long mask[kLargeKeySpace];
+    const int c = blockIdx.x, K = a.key_space;
+    for (int i = threadIdx.x; i < K; i += kPlanThreads) mask[i] = 0ull;
+    __syncthreads();
+    const int r = c * kChunkTokens * a.k + threadIdx.x;
+    if (threadIdx.x < kChunkTokens * a.k && r < a.R) {
+        int s = route_slot(a, r);
+        if (s >= 0) {
+            int key = a.slot_base >= 0 ? s - a.slot_base : s;
+            atomicOr(&mask[key], 1ull << (threadIdx.x / a.k));
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < K; i += kPlanThreads)
+        a.chunk_counts[(int64_t)c * K + i] = __popcll(mask[i]);
+}
+
+// Kernel B: per-key totals, segment starts, per-chunk offsets, active list, tiles.
+// G threads share a key (each sums a contiguous range of chunks); keys are
+// processed in ascending passes of 1024 / G.
+__global__ void __launch_bounds__(kPlanThreads) plan_scan_kernel(PlanArgs a, int nchunks) {
+    __shared__ int part[kPlanThreads];
+    __shared__ int kstart[kPlanThreads];
+    __shared__ int kact[kPlanThreads];
+    __shared__ int wsum[kPlanThreads / 64];
+    const int tid = threadIdx.x, K = a.key_space;
+    int G = 1;
+    while (G * 2 * K <= kPlanThreads) G *= 2;
+    const int kpp = kPlanThreads / G;
+    const int cpg = (nchunks + G - 1) / G;
+    const int g = tid % G;
+    const int c0 = g * cpg, c1 = (c0 + cpg) < nchunks ? (c0 + cpg) : nchunks;
+    int run_rows = 0, run_active = 0;
+    for (int kb = 0; kb < K; kb += kpp) {
+        const int key = kb + tid / G;
+        int s = 0;
+        if (key < K)
+            for (int c = c0; c < c1; ++c) s += a.chunk_counts[(int64_t)c * K + key];
+        part[tid] = s;
+        __syncthreads();
+        const int gb = tid - g;
+        int pre = 0, tot = 0;
+        for (int i = 0; i < G; ++i) {
+            int v = part[gb + i];
+            pre += (i < g) ? v : 0;
+            tot += v;
+        }
+        const bool lead = (g == 0) && key < K;
+        int pass_rows, pass_active;
+        int ex = block_excl_scan(lead ? tot : 0, wsum, &pass_rows);
+        int ax = block_excl_scan((lead && tot > 0) ? 1 : 0, wsum, &pass_active);
+        if (g == 0) {
+            kstart[tid / G] = run_rows + ex;
+            kact[tid / G] = run_active + ax;
+        }
+        __syncthreads();
+        if (key < K) {
+            const int start = kstart[tid / G];
+            int off = start + pre;
+            for (int c = c0; c < c1; ++c) {
+                int64_t o = (int64_t)c * K + key;
+                int cnt = a.chunk_counts[o];
+                a.chunk_counts[o] = off;     // counts become offsets
+                off += cnt;
+            }
+            if (lead && tot > 0) {
+                const int ai = kact[tid / G];
+                a.active_slot[ai] = a.slot_base >= 0 ? a.slot_base + key : key;
+                a.seg[ai] = start;
+            }
+        }
+        run_rows += pass_rows;
+        run_active += pass_active;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        a.seg[run_active] = run_rows;
+        a.meta[0] = run_active;
+        a.meta[2] = run_rows;
+    }
+    __syncthreads();
+    emit_tiles(a, run_active, wsum);
+}
+
+// Kernel C: stable scatter.
+__global__ void __launch_bounds__(kPlanThreads) plan_scatter_kernel(PlanArgs a) {
+    __shared__ unsigned long long mask[kLargeKeySpace];
+    const int c = blockIdx.x, K = a.key_space;
+    for (int i = threadIdx.x; i < K; i += kPlanThreads) mask[i] = 0ull;
+    __syncthreads();
+    const int r = c * kChunkTokens * a.k + threadIdx.x;
+    const bool mine = threadIdx.x < kChunkTokens * a.k && r < a.R;
+    int key = -1, tl = 0;
+    if (mine) {
+        int s = route_slot(a, r);
+        if (s >= 0) {
+            key = a.slot_base >= 0 ? s - a.slot_base : s;
+            tl = threadIdx.x / a.k;
+            atomicOr(&mask[key], 1ull << tl);
+        }
+    }
+    __syncthreads();
+    if (mine) {
+        if (key >= 0) {
+            unsigned long long below = tl ? (mask[key] & ((1ull << tl) - 1ull)) : 0ull;
+            int p = a.chunk_counts[(int64_t)c * K + key] + __popcll(below);
+            a.perm[p] = r;
+            a.route_pos[r] = p;
+        } else {
+            a.route_pos[r] = -1;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, hipStream_t st) {
+    PlanArgs a;
+    a.routes = routes;
+    a.k = c->sh.top_k;
+    a.T = T;
+    a.R = T * a.k;
+    a.slot_base = slot_base;
+    a.E = c->sh.experts;
+    a.N = (int32_t)c->N;
+    a.bm = bm;
+    a.key_space = slot_base >= 0 ? c->sh.experts : (int32_t)c->N;
+    a.errflag = c->errflag;
+    a.meta = c->plan.meta;
+    a.active_slot = c->plan.active_slot;
+    a.seg = c->plan.seg;
+    a.perm = c->plan.perm;
+    a.route_pos = c->plan.route_pos;
+    a.tile_active = c->plan.tile_active;
+    a.tile_row0 = c->plan.tile_row0;
+    a.chunk_counts = c->plan.chunk_counts;
+    if (a.R <= kSmallPlanRoutes) {
+        hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+    } else {
+        if (a.key_space > kLargeKeySpace) return hipErrorInvalidValue;
+        int nchunks = (T + kChunkTokens - 1) / kChunkTokens;
+        hipLaunchKernelGGL(plan_count_kernel, dim3(nchunks), dim3(kPlanThreads), 0, st, a);
+        hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a, nchunks);
+        hipLaunchKernelGGL(plan_scatter_kernel, dim3(nchunks), dim3(kPlanThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ftmoe

@@ -1,0 +1,135 @@
+// Top-k softmax routing: z = x Wr with every bf16 product exact and the sum
+// accumulated in fp64; the k largest logits per token (ties to the lower
+// expert); weights = softmax over the chosen k.  The router picks k of the
+// layer's E experts per token ("Making Large MoE Models Practical on a Single
+// Machine", section 1).
+#include "common.h"
+
+namespace ftmoe {
+namespace {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteTokens = 16;     // tokens per workgroup
+constexpr int kRouteMaxE = 256;      // experts supported by this kernel
+constexpr int kDChunk = 256;         // hidden-size chunk staged in LDS
+
+__device__ __forceinline__ double bf16_to_f64(uint16_t u) {
+    return (double)__uint_as_float((uint32_t)u << 16);
+}
+
+// Logits of kRouteTokens tokens: thread (g, e) sums the k-slice i = g, g + G,
+// ... of column e; the G partial sums are added in a fixed order.
+__global__ void __launch_bounds__(kRouteThreads)
+    route_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E, int k,
+                 int32_t* __restrict__ ids, float* __restrict__ w) {
+    __shared__ uint16_t xs[kRouteTokens][kDChunk];
+    __shared__ double zs[kRouteTokens][kRouteMaxE];
+
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.x * kRouteTokens;
+    const int G = kRouteThreads / E > 0 ? kRouteThreads / E : 1;   // k-splits per column
+    const int e = tid % E;
+    const int g = tid / E;
+    const bool active = g < G && tid < G * E;
+
+    for (int i = tid; i < kRouteTokens * E; i += kRouteThreads) zs[i / E][i % E] = 0.0;
+
+    double acc[kRouteTokens];
+#pragma unroll
+    for (int t = 0; t < kRouteTokens; ++t) acc[t] = 0.0;
+
+    for (int c0 = 0; c0 < d; c0 += kDChunk) {
+        const int cl = (d - c0) < kDChunk ? (d - c0) : kDChunk;
+        __syncthreads();
+        for (int i = tid; i < kRouteTokens * kDChunk; i += kRouteThreads) {
+            int t = i / kDChunk, c = i % kDChunk;
+            uint16_t v = 0;
+            if (t0 + t < T && c < cl) v = x[(int64_t)(t0 + t) * d + c0 + c];
+            xs[t][c] = v;
+        }
+        __syncthreads();
+        if (active) {
+            for (int c = g; c < cl; c += G) {
+                double wv = bf16_to_f64(wr[(int64_t)(c0 + c) * E + e]);
+#pragma unroll
+                for (int t = 0; t < kRouteTokens; ++t) acc[t] = fma(bf16_to_f64(xs[t][c]), wv, acc[t]);
+            }
+        }
+    }
+    __syncthreads();
+    // fixed-order reduction of the G partial sums
+    for (int gg = 0; gg < G; ++gg) {
+        if (active && g == gg) {
+#pragma unroll
+            for (int t = 0; t < kRouteTokens; ++t) zs[t][e] += acc[t];
+        }
+        __syncthreads();
+    }
+
+    // top-k and softmax: one wave per token
+    const int lane = tid & 63, wid = tid >> 6;
+    for (int t = wid; t < kRouteTokens; t += kRouteThreads / 64) {
+        if (t0 + t >= T) break;
+        double zl[kRouteMaxE / 64];
+        bool taken[kRouteMaxE / 64];
+#pragma unroll
+        for (int j = 0; j < kRouteMaxE / 64; ++j) {
+            int ee = lane + 64 * j;
+            zl[j] = ee < E ? zs[t][ee] : -INFINITY;
+            taken[j] = ee >= E;
+        }
+        double zsel[kMaxTopK];
+        int esel[kMaxTopK];
+        for (int r = 0; r < k; ++r) {
+            // best of this lane: largest z, ties to lower expert index
+            double bz = -INFINITY;
+            int be = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < kRouteMaxE / 64; ++j) {
+                int ee = lane + 64 * j;
+                if (!taken[j] && (zl[j] > bz || (zl[j] == bz && ee < be))) {
+                    bz = zl[j];
+                    be = ee;
+                }
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                double oz = __shfl_xor(bz, off, 64);
+                int oe = __shfl_xor(be, off, 64);
+                if (oz > bz || (oz == bz && oe < be)) {
+                    bz = oz;
+                    be = oe;
+                }
+            }
+            zsel[r] = bz;
+            esel[r] = be;
+#pragma unroll
+            for (int j = 0; j < kRouteMaxE / 64; ++j)
+                if (lane + 64 * j == be) taken[j] = true;
+        }
+        if (lane == 0) {
+            double s = 0.0;
+            double ex[kMaxTopK];
+            for (int r = 0; r < k; ++r) {
+                ex[r] = exp(zsel[r] - zsel[0]);
+                s += ex[r];
+            }
+            for (int r = 0; r < k; ++r) {
+                ids[(int64_t)(t0 + t) * k + r] = esel[r];
+                w[(int64_t)(t0 + t) * k + r] = (float)(ex[r] / s);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int d, int E, int k, int32_t* ids, float* w,
+                        hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    int blocks = (T + kRouteTokens - 1) / kRouteTokens;
+    hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(kRouteThreads), 0, st, x, wr, T, d, E, k, ids, w);
+    return hipGetLastError();
+}
+
+}  // namespace ftmoe

@@ -69,12 +69,18 @@ def _bf16_mat(buf, off, rows, cols):
     return bf16_to_f64(u), off + 2 * rows * cols
 
 
+# The decoders above applied once to every code point; indexing these tables is
+# the same function, evaluated faster on large records.
+_E4M3_TABLE = e4m3fn_to_f64(np.arange(256, dtype=np.uint8))
+_E2M1_TABLE = e2m1_to_f64(np.arange(16, dtype=np.uint8))
+
+
 def _fp8_mat(codes_buf, off, rows, cols, scales):
     c = np.frombuffer(codes_buf, dtype=np.uint8, count=rows * cols, offset=off).reshape(rows, cols)
-    w = e4m3fn_to_f64(c)
+    w = _E4M3_TABLE[c]
     # each element scales by the fp32 scale of its 128x128 block
-    s = np.repeat(np.repeat(scales, 128, axis=0), 128, axis=1)
-    return w * s
+    w = w.reshape(rows // 128, 128, cols // 128, 128) * scales[:, None, :, None]
+    return w.reshape(rows, cols)
 
 
 def _mx_mat(buf, off, rows, cols, soff):
@@ -83,7 +89,8 @@ def _mx_mat(buf, off, rows, cols, soff):
     codes[:, 0::2] = packed & 0xF
     codes[:, 1::2] = packed >> 4
     sc = np.frombuffer(buf, dtype=np.uint8, count=rows * cols // 32, offset=soff).reshape(rows, cols // 32)
-    return e2m1_to_f64(codes) * np.repeat(e8m0_to_f64(sc), 32, axis=1)
+    w = _E2M1_TABLE[codes].reshape(rows, cols // 32, 32) * e8m0_to_f64(sc)[:, :, None]
+    return w.reshape(rows, cols)
 
 
 def decode_record(rec, fmt: str, d: int, f: int):

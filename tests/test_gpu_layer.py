@@ -1,0 +1,150 @@
+"""GPU parity of the float layer (routing -> control -> GPU experts + host
+experts -> combine) against the oracle, on the shapes of the decode, prefill,
+block-FP8 and MXFP4 configurations: every output at small T, sampled token
+rows at full T.  Bar: max |y - y_ref| <= 2e-2 max |y_ref| (bf16 weights) and
+<= 5e-2 max |y_ref| (FP8, MXFP4), outputs accumulated in fp32."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_execution_amd as M
+import synth
+from moe_expert_execution_amd.tensors import SlotCache
+from oracle import cache as OC, route as OR
+
+from gpu_util import (assert_close_rel, bf16_bits_to_f64, cuda, dev, dev_u16, expert_fn, gpu, make_bank,
+                      oracle_rows)
+
+TOL = {"bf16": 2e-2, "fp8": 5e-2, "mxfp4": 5e-2}
+
+
+def run_cached(sc, layer, x, ids, w):
+    T = x.shape[0]
+    st = torch.cuda.current_stream().cuda_stream
+    xd, idd, wd = dev_u16(x), dev(ids.astype(np.int32)), dev(w.astype(np.float32))
+    y = torch.zeros((T, x.shape[1]), dtype=torch.int16, device="cuda")
+    M.ft_cache_classify(sc.handle, layer, idd.data_ptr(), T, None, st)
+    M.ft_moe_forward(sc.handle, layer, M.FT_MODE_CACHED, xd.data_ptr(), idd.data_ptr(), wd.data_ptr(), T,
+                     y.data_ptr(), st)
+    torch.cuda.synchronize()
+    return bf16_bits_to_f64(y), idd.cpu().numpy()
+
+
+@gpu
+def test_decode_gemv_bf16():
+    """Decode shape (d=2048, E=128, top-8, f=768, bf16) over 2 layers with 64
+    slots: T = 1..4 tokens (GEMV path), hits, fills and host experts mixed."""
+    cuda()
+    cfg = synth.CONFIGS["decode"].with_(layers=2, slots=64)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, 4, cfg.bp_mbps,
+                   cfg.bh_mbps)
+    sim = OC.SlotCacheSim(cfg.layers, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+    try:
+        exs = [expert_fn(recs, cfg, l, maxsize=40) for l in range(cfg.layers)]
+        xs = [synth.ar1_tokens(cfg, l, 16) for l in range(cfg.layers)]
+        classes = set()
+        for step in range(6):
+            for l in range(cfg.layers):
+                T = 1 + (step % 4)
+                x = xs[l][step:step + T] if T == 1 else synth.tokens(cfg, T, 50 + step, l)
+                ids, w, _ = OR.route(x, synth.router(cfg, l), cfg.k)
+                r = sim.classify(l, ids)
+                classes |= set(r.cls)
+                y, routes = run_cached(sc, l, x, ids, w)
+                assert np.array_equal(routes, r.routes)
+                assert_close_rel(y, oracle_rows(x, ids, w, exs[l], range(T)), TOL["bf16"], f"step {step} layer {l}")
+        assert classes == {OC.HIT, OC.FILL, OC.CPU}
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
+def test_prefill_streamed_bf16():
+    """Prefill shape (d=2048, E=128, top-8, f=768): two layers through the
+    full-layer double buffer with prefetch, T = 8192 (sampled rows), then
+    ragged T = 300 and T = 100 (all rows)."""
+    cuda()
+    cfg = synth.CONFIGS["prefill"].with_(layers=2, slots=256)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, 8192, cfg.bp_mbps,
+                   cfg.bh_mbps)
+    st = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(5)
+    try:
+        for T in (8192, 300, 100):
+            x = synth.tokens(cfg, T, 7, T)
+            xd = dev_u16(x)
+            for l in range(cfg.layers):
+                ids, w, _ = OR.route(x, synth.router(cfg, l), cfg.k)
+                idd, wd = dev(ids.astype(np.int32)), dev(w)
+                y = torch.zeros((T, cfg.d), dtype=torch.int16, device="cuda")
+                M.ft_moe_forward(sc.handle, l, M.FT_MODE_STREAMED | M.FT_PREFETCH_NEXT, xd.data_ptr(),
+                                 idd.data_ptr(), wd.data_ptr(), T, y.data_ptr(), st)
+                torch.cuda.synchronize()
+                yg = bf16_bits_to_f64(y)
+                rows = np.sort(rng.choice(T, size=min(T, 24), replace=False)) if T > 300 else np.arange(T)
+                if T == 100:
+                    rows = np.arange(T)
+                ref = oracle_rows(x, ids, w, expert_fn(recs, cfg, l, maxsize=130), rows)
+                assert_close_rel(yg[rows], ref, TOL["bf16"], f"T {T} layer {l}")
+        s = M.ft_cache_stats(sc.handle)
+        assert s.error_flags == 0 and s.layers_streamed >= 2
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
+@pytest.mark.parametrize("T,steps,nsample", [(1, 6, 1), (64, 3, 4), (2048, 1, 4)])
+def test_fp8_cached(T, steps, nsample):
+    """Block-FP8 shape (d=4096, E=256, top-8, f=2048, e4m3 + 128x128 scales),
+    64 slots, Zipf routes: GEMV (T=1) and MFMA (T=64, 2048) paths."""
+    cuda()
+    cfg = synth.CONFIGS["fp8"]
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, "fp8", bank.ptr, cfg.slots, T, cfg.bp_mbps, cfg.bh_mbps)
+    rng = np.random.default_rng(T)
+    try:
+        ex = expert_fn(recs, cfg, 0, maxsize=40)
+        for step in range(steps):
+            x = synth.tokens(cfg, T, 300 + step, T)
+            ids, w = synth.zipf_routes(cfg, T, step)
+            y, _ = run_cached(sc, 0, x, ids, w)
+            rows = np.sort(rng.choice(T, size=nsample, replace=False))
+            assert_close_rel(y[rows], oracle_rows(x, ids, w, ex, rows), TOL["fp8"], f"T {T} step {step}")
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
+@pytest.mark.parametrize("T,steps,nsample", [(1, 4, 1), (16, 1, 2)])
+def test_mxfp4_cached(T, steps, nsample):
+    """MXFP4 shape (d=7168, E=256, top-8, f=2048, e2m1 + e8m0 per 32), one
+    layer, 64 slots: GEMV (T=1) and MFMA (T=16) paths."""
+    cuda()
+    cfg = synth.CONFIGS["mxfp4"].with_(layers=1, slots=64)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, "mxfp4", bank.ptr, cfg.slots, T, cfg.bp_mbps, cfg.bh_mbps)
+    rng = np.random.default_rng(T + 1)
+    try:
+        ex = expert_fn(recs, cfg, 0, maxsize=20)
+        wr = synth.router(cfg, 0)
+        for step in range(steps):
+            x = synth.tokens(cfg, T, 400 + step, T)
+            ids, w, _ = OR.route(x, wr, cfg.k)
+            y, _ = run_cached(sc, 0, x, ids, w)
+            rows = np.sort(rng.choice(T, size=nsample, replace=False))
+            assert_close_rel(y[rows], oracle_rows(x, ids, w, ex, rows), TOL["mxfp4"], f"T {T} step {step}")
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
