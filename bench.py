@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer with a GPU slot cache on one MI355X.
+
+Headline workload (printed as the one JSON line on stdout): decode, 48 MoE
+layers, d=2048, E=128 experts, top-8, f=768, bf16, one token per step; the
+host bank holds all 6,144 layer-expert records (58 GB pinned), the slot cache
+1,024 of them and starts cold; B_P/B_H = 20/60 GB/s; hidden states follow a
+per-layer AR(1) stream.  A step is one token through all 48 layers: routing,
+the control kernel, fills, GPU experts, host experts and the combine.
+`value` is tokens/s over the K timed steps that follow W warm-up steps
+(W + K = 256 by default).
+
+Also reported: the live roofline of the dominant kernel (the decode gate/up
+GEMV, HIP events on the stream it runs on), the oracle timed on the host
+cores on a bounded sample, and a prefill section (8,192-token chunk: MFMA
+utilisation of the grouped GEMMs with all experts resident, and 24 layers
+streamed through the double buffer over PCIe).
+
+    python bench.py [--gpus 1] [--steps 240] [--warmup 16]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0}
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "wfmt.h"):
+        with open(os.path.join(ROOT, "moe_expert_execution_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "gemv_traffic.json")
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha") != kernel_source_sha() or d.get("kernel") != kernel_key:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def decode_bench(args):
+    import numpy as np
+    import torch
+
+    import moe_expert_execution_amd as M
+    import synth
+    from moe_expert_execution_amd.tensors import PinnedBank, SlotCache
+
+    cfg = synth.CONFIGS["decode"]
+    L, E, k, d, f, S = cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, cfg.S
+    steps = args.warmup + args.steps
+    t = time.time()
+    bank = PinnedBank(L * E * S)
+    synth.bank(cfg, out=bank.records(S), nthreads=min(16, len(os.sched_getaffinity(0))))
+    log(f"decode bank {L * E * S / 1e9:.1f} GB pinned+generated in {time.time() - t:.1f}s")
+    wr = torch.stack([torch.from_numpy(synth.router(cfg, l).view(np.int16)) for l in range(L)]).cuda()
+    xs = torch.stack([torch.from_numpy(synth.ar1_tokens(cfg, l, steps).view(np.int16)) for l in range(L)]).cuda()
+    sc = SlotCache(L, E, k, d, f, "bf16", bank.ptr, cfg.slots, 1, cfg.bp_mbps, cfg.bh_mbps)
+    shp = sc.shape
+    ids = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((L, d), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    h = sc.handle
+
+    def step(s):
+        for l in range(L):
+            xp = xs[l, s].data_ptr()
+            M.ft_moe_route(shp, xp, wr[l].data_ptr(), 1, ids[l].data_ptr(), w[l].data_ptr(), stream)
+            M.ft_cache_classify(h, l, ids[l].data_ptr(), 1, None, stream)
+            M.ft_moe_forward(h, l, M.FT_MODE_CACHED, xp, ids[l].data_ptr(), w[l].data_ptr(), 1, y[l].data_ptr(),
+                             stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    s0 = M.ft_cache_stats(h).as_dict()
+    M.ft_cache_set_timing(h, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, steps):
+        step(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tm = M.ft_cache_timing(h)
+    s1 = M.ft_cache_stats(h).as_dict()
+    elapsed = t1 - t0
+    delta = {key: s1[key] - s0[key] for key in ("calls", "unique", "hits", "misses", "fills", "cpu_experts",
+                                                "evictions", "bytes_filled")}
+    assert s1["error_flags"] == 0, s1
+    # algorithmic bytes: each GPU-executed expert's gate and up banks are read
+    # once by the gate/up GEMV, its down bank once by the down GEMV
+    gu_bytes = 2 * f * d * 2
+    dn_bytes = d * f * 2
+    n_gu, n_dn = tm.launches[M.FT_K_GEMV_GU], tm.launches[M.FT_K_GEMV_DOWN]
+    ms_gu, ms_dn = tm.ms[M.FT_K_GEMV_GU], tm.ms[M.FT_K_GEMV_DOWN]
+    experts = tm.gemv_experts
+    gu_gbs = experts * gu_bytes / (ms_gu / 1e3) / 1e9
+    dn_gbs = experts * dn_bytes / (ms_dn / 1e3) / 1e9
+    both_gbs = experts * (gu_bytes + dn_bytes) / ((ms_gu + ms_dn) / 1e3) / 1e9
+    kernel_key = "gemv_gateup_kernel<bf16,1>"
+    traffic = measured_traffic(kernel_key)
+    res = {
+        "value": args.steps / elapsed,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "roofline": {
+            "bound": "hbm", "kernel": kernel_key, "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic,
+            "bytes_per_launch": experts * gu_bytes / max(n_gu, 1),
+            "avg_launch_us": ms_gu / max(n_gu, 1) * 1e3, "launches": n_gu,
+        },
+        "decode_kernels": {
+            "gemv_down": {"achieved_gbs": dn_gbs, "avg_launch_us": ms_dn / max(n_dn, 1) * 1e3},
+            "gemv_pair": {"achieved_gbs": both_gbs, "frac": both_gbs / HBM_PEAK_GBS},
+            "gpu_experts_per_layer_step": experts / max(n_gu, 1),
+        },
+        "cache": {**delta, "layer_calls": delta["calls"],
+                  "miss_rate": delta["misses"] / max(delta["unique"], 1),
+                  "fill_gbs_effective": delta["bytes_filled"] / elapsed / 1e9},
+    }
+    log(f"decode: {res['value']:.1f} tok/s, {res['ms_per_step']:.2f} ms/step, gate/up GEMV {gu_gbs:.0f} GB/s "
+        f"({gu_gbs / HBM_PEAK_GBS:.1%}), pair {both_gbs:.0f} GB/s, miss rate {res['cache']['miss_rate']:.2f}")
+    sc.close()
+    return res, bank, cfg
+
+
+def cpu_baseline(bank, cfg, sample_steps):
+    """The oracle (route + slot-cache simulator + fp64 layer) on the host cores,
+    on decode steps 0..sample_steps-1 of the same workload, all 48 layers."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import cache as OC, formats as OF, moe as OM, route as OR
+    L, E, k = cfg.layers, cfg.E, cfg.k
+    recs = bank.records(cfg.S)
+    xs = [synth.ar1_tokens(cfg, l, sample_steps) for l in range(L)]
+    wrs = [synth.router(cfg, l) for l in range(L)]
+    sim = OC.SlotCacheSim(L, E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+    t0 = time.perf_counter()
+    for s in range(sample_steps):
+        for l in range(L):
+            x = xs[l][s:s + 1]
+            ids, w, _ = OR.route(x, wrs[l], k)
+            sim.classify(l, ids)
+            OM.moe_layer(x, ids, w, lambda e: OF.decode_record(recs[l * E + e], cfg.fmt, cfg.d, cfg.f))
+    el = time.perf_counter() - t0
+    blas = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = len(os.sched_getaffinity(0))
+    return {"value": sample_steps / el, "unit": "tokens/s", "cores": cores, "blas_threads": blas[0] if blas else 1,
+            "kind": "oracle", "seconds": el,
+            "sample": f"decode steps 0..{sample_steps - 1} x {L} layers (route + LRU simulator + fp64 layer)"}
+
+
+def prefill_bench(args):
+    import numpy as np
+    import torch
+
+    import moe_expert_execution_amd as M
+    import synth
+    from moe_expert_execution_amd.tensors import PinnedBank, SlotCache
+
+    cfg = synth.CONFIGS["prefill"]
+    L, E, k, d, f, S, T = cfg.stream_layers, cfg.E, cfg.k, cfg.d, cfg.f, cfg.S, cfg.tokens[0]
+    t = time.time()
+    bank = PinnedBank(L * E * S)
+    synth.bank(cfg.with_(layers=L), out=bank.records(S), nthreads=min(16, len(os.sched_getaffinity(0))))
+    log(f"prefill bank {L * E * S / 1e9:.1f} GB in {time.time() - t:.1f}s")
+    sc = SlotCache(L, E, k, d, f, "bf16", bank.ptr, 2 * E, T, cfg.bp_mbps, cfg.bh_mbps)
+    h, shp = sc.handle, sc.shape
+    stream = torch.cuda.current_stream().cuda_stream
+    x = torch.from_numpy(synth.tokens(cfg, T, 7).view(np.int16)).cuda()
+    wr = torch.stack([torch.from_numpy(synth.router(cfg, l).view(np.int16)) for l in range(L)]).cuda()
+    ids = torch.empty((L, T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    for l in range(L):
+        M.ft_moe_route(shp, x.data_ptr(), wr[l].data_ptr(), T, ids[l].data_ptr(), w[l].data_ptr(), stream)
+    torch.cuda.synchronize()
+
+    def fwd(l, flags=M.FT_PREFETCH_NEXT):
+        M.ft_moe_forward(h, l, M.FT_MODE_STREAMED | flags, x.data_ptr(), ids[l].data_ptr(), w[l].data_ptr(), T,
+                         y.data_ptr(), stream)
+
+    # (1) grouped GEMMs with layer 0 resident in buffer 0 (no transfer in the loop)
+    fwd(0, 0)
+    torch.cuda.synchronize()
+    M.ft_cache_set_timing(h, True)
+    reps = 10
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fwd(0, 0)
+    torch.cuda.synchronize()
+    t_layer = (time.perf_counter() - t0) / reps
+    tm = M.ft_cache_timing(h)
+    rows = tm.gemm_rows / reps
+    fl_gu, fl_dn = 2.0 * rows * d * 2 * f, 2.0 * rows * f * d
+    ms_gu = tm.ms[M.FT_K_GEMM_GU] / reps
+    ms_dn = tm.ms[M.FT_K_GEMM_DOWN] / reps
+    tf_gu = fl_gu / (ms_gu / 1e3) / 1e12
+    tf_dn = fl_dn / (ms_dn / 1e3) / 1e12
+    tf_pair = (fl_gu + fl_dn) / ((ms_gu + ms_dn) / 1e3) / 1e12
+    M.ft_cache_set_timing(h, False)
+    # (2) all layers streamed through the double buffer, prefetching layer l+1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for l in range(L):
+        fwd(l)
+    torch.cuda.synchronize()
+    t_stream = time.perf_counter() - t0
+    st = M.ft_cache_stats(h)
+    assert st.error_flags == 0
+    bytes_stream = L * E * S
+    res = {
+        "workload": f"prefill chunk T={T}, d={d}, E={E}, top-{k}, f={f}, bf16",
+        "gemm": {"dtype": "bf16", "peak_tflops": MFMA_PEAK_TFLOPS["bf16"],
+                 "gateup_tflops": tf_gu, "down_tflops": tf_dn, "pair_tflops": tf_pair,
+                 "frac": tf_pair / MFMA_PEAK_TFLOPS["bf16"], "gateup_ms": ms_gu, "down_ms": ms_dn,
+                 "layer_ms_resident": t_layer * 1e3, "rows": rows},
+        "stream": {"layers": L, "bytes": bytes_stream, "seconds": t_stream,
+                   "pcie_gbs": bytes_stream / t_stream / 1e9, "tokens_per_s": T / t_stream,
+                   "compute_only_s": L * t_layer, "gpu_busy_frac": L * t_layer / t_stream},
+    }
+    log(f"prefill: GEMM pair {tf_pair:.0f} TFLOP/s ({res['gemm']['frac']:.1%} of bf16 peak), layer "
+        f"{t_layer * 1e3:.2f} ms; stream {res['stream']['pcie_gbs']:.1f} GB/s over {L} layers in {t_stream:.2f}s")
+    sc.close()
+    bank.close()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--cpu-sample-steps", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the layer and its slot cache run on a single device and this build has "
+              f"no multi-GPU path, so --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_expert_execution_amd as M
+    M.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    dec, bank, cfg = decode_bench(args)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(bank, cfg, args.cpu_sample_steps)
+        log(f"cpu oracle: {cpu['value']:.4f} tok/s over {cpu['seconds']:.1f}s on {cpu['cores']} cores")
+    bank.close()
+    pre = None if args.no_prefill else prefill_bench(args)
+
+    line = {
+        "metric": "MoE-layer tokens/s: decode HBM GB/s %peak; prefill MFMA %peak",
+        "value": dec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode: 48 MoE layers, d=2048, E=128, top-8, ffn=768, bf16, 1 token/step, "
+                               "1024 of 6144 layer-experts cached (cold start), B_P/B_H 20/60 GB/s, AR(1) hidden "
+                               "states", "global_batch": 1, "seq_len": args.warmup + args.steps,
+                   "parallelism": "single GPU"},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "decode_kernels": dec["decode_kernels"],
+        "cache": dec["cache"],
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

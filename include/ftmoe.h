@@ -240,6 +240,23 @@ ft_status ft_cache_resize(ft_cache* cache, int64_t new_num_slots);
 /* Counters and sticky error flags (synchronises). */
 ft_status ft_cache_stats(const ft_cache* cache, ft_stats* out);
 
+/* Expert-kernel timing (measurement support).  When enabled, every
+ * ft_moe_forward brackets its expert kernels with HIP events on the caller's
+ * stream; ft_cache_timing synchronises and returns, per kernel class
+ * (0 GEMV gate/up, 1 GEMV down, 2 GEMM gate/up, 3 GEMM down), the number of
+ * launches and their summed event durations, plus device-side counts of the
+ * work those launches did: expert records read (one per active slot per call)
+ * and GPU rows (routes) computed. */
+enum { FT_K_GEMV_GU = 0, FT_K_GEMV_DOWN = 1, FT_K_GEMM_GU = 2, FT_K_GEMM_DOWN = 3, FT_K_COUNT = 4 };
+typedef struct {
+    uint64_t launches[FT_K_COUNT];
+    double ms[FT_K_COUNT];
+    uint64_t gemv_experts, gemv_rows;   /* summed over GEMV-path calls */
+    uint64_t gemm_experts, gemm_rows;   /* summed over GEMM-path calls */
+} ft_timing;
+ft_status ft_cache_set_timing(ft_cache* cache, int32_t enable);   /* also resets the totals */
+ft_status ft_cache_timing(const ft_cache* cache, ft_timing* out);
+
 /* Copy the maps to host memory (synchronises): slot_for_id [L*E],
  * id_of_slot [N], stamp [N]; any pointer may be NULL. */
 ft_status ft_cache_snapshot(const ft_cache* cache, int32_t* slot_for_id, int32_t* id_of_slot,

@@ -47,6 +47,14 @@ class FtStats(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+FT_K_GEMV_GU, FT_K_GEMV_DOWN, FT_K_GEMM_GU, FT_K_GEMM_DOWN = range(4)
+
+
+class FtTiming(ctypes.Structure):
+    _fields_ = [("launches", u64 * 4), ("ms", ctypes.c_double * 4), ("gemv_experts", u64), ("gemv_rows", u64),
+                ("gemm_experts", u64), ("gemm_rows", u64)]
+
+
 class FtError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"ftmoe status {status}: {msg}")
@@ -66,6 +74,8 @@ _SIGS = {
     "ft_cache_resize": (i32, [vp, i64]),
     "ft_cache_stats": (i32, [vp, ctypes.POINTER(FtStats)]),
     "ft_cache_snapshot": (i32, [vp, vp, vp, vp, vp]),
+    "ft_cache_set_timing": (i32, [vp, i32]),
+    "ft_cache_timing": (i32, [vp, ctypes.POINTER(FtTiming)]),
     "ft_cache_read_slot": (i32, [vp, i64, vp]),
     "ft_host_alloc": (i32, [ctypes.c_size_t, ctypes.POINTER(vp)]),
     "ft_host_free": (i32, [vp]),
@@ -156,6 +166,16 @@ def ft_cache_stats(h: int) -> FtStats:
     s = FtStats()
     _check(lib().ft_cache_stats(h, ctypes.byref(s)))
     return s
+
+
+def ft_cache_set_timing(h: int, enable: bool) -> None:
+    _check(lib().ft_cache_set_timing(h, 1 if enable else 0))
+
+
+def ft_cache_timing(h: int) -> FtTiming:
+    t = FtTiming()
+    _check(lib().ft_cache_timing(h, ctypes.byref(t)))
+    return t
 
 
 def ft_cache_snapshot(h: int, n_ids: int, n_slots: int):

@@ -61,6 +61,69 @@ bool record_layout(const ft_shape& s, RecordLayout* o) {
     return false;
 }
 
+// ---- expert-kernel timing: a ring of event pairs, folded into totals when a
+// pair is reused or read
+struct Timing {
+    static constexpr int kRing = 4096;
+    hipEvent_t ev[kRing][2];
+    int cls[kRing];
+    bool live[kRing];
+    int next = 0;
+    uint64_t launches[FT_K_COUNT] = {};
+    double ms[FT_K_COUNT] = {};
+    bool ok = true;
+};
+
+static void fold(Timing* t, int i) {
+    if (!t->live[i]) return;
+    float msec = 0.f;
+    if (hipEventSynchronize(t->ev[i][1]) == hipSuccess && hipEventElapsedTime(&msec, t->ev[i][0], t->ev[i][1]) == hipSuccess) {
+        t->ms[t->cls[i]] += msec;
+        t->launches[t->cls[i]] += 1;
+    }
+    t->live[i] = false;
+}
+
+Timing* timing_create() {
+    auto* t = new Timing();
+    for (int i = 0; i < Timing::kRing; ++i) {
+        t->live[i] = false;
+        if (hipEventCreate(&t->ev[i][0]) != hipSuccess || hipEventCreate(&t->ev[i][1]) != hipSuccess) t->ok = false;
+    }
+    return t;
+}
+
+void timing_destroy(Timing* t) {
+    if (!t) return;
+    for (int i = 0; i < Timing::kRing; ++i) {
+        (void)hipEventDestroy(t->ev[i][0]);
+        (void)hipEventDestroy(t->ev[i][1]);
+    }
+    delete t;
+}
+
+int timing_begin(Timing* t, int cls, hipStream_t st) {
+    const int i = t->next;
+    t->next = (t->next + 1) % Timing::kRing;
+    fold(t, i);     // the pair recorded kRing launches ago has long completed
+    t->cls[i] = cls;
+    (void)hipEventRecord(t->ev[i][0], st);
+    return i;
+}
+
+void timing_end(Timing* t, int i, hipStream_t st) {
+    (void)hipEventRecord(t->ev[i][1], st);
+    t->live[i] = true;
+}
+
+void timing_read(Timing* t, uint64_t* launches, double* ms) {
+    for (int i = 0; i < Timing::kRing; ++i) fold(t, i);
+    for (int k = 0; k < FT_K_COUNT; ++k) {
+        launches[k] = t->launches[k];
+        ms[k] = t->ms[k];
+    }
+}
+
 namespace {
 
 template <typename T>
@@ -84,6 +147,7 @@ void free_cache(ft_cache* c) {
     if (!c) return;
     (void)hipDeviceSynchronize();
     if (c->host) host_branch_destroy(c->host);
+    if (c->timing) timing_destroy(c->timing);
     void* bufs[] = {c->pool, c->slot_for_id, c->id_of_slot, c->stamp, c->clock, c->counters, c->errflag,
                     c->wl_counts, c->wl_slot, c->wl_src, c->plan.meta, c->plan.active_slot, c->plan.seg,
                     c->plan.perm, c->plan.route_pos, c->plan.tile_active, c->plan.tile_row0,
@@ -331,9 +395,9 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         FT_HIP(host_branch_enqueue(c->host, layer, T, c->hstream));
         FT_HIP(hipMemcpyAsync(c->Pdev, hs.P, sizeof(float) * T * d, hipMemcpyHostToDevice, c->hstream));
         FT_HIP(hipEventRecord(c->ev_host, c->hstream));
-        // GPU experts (hits and fills) from the slot pool
-        FT_HIP(launch_plan(c, routes, T, -1, gemm_tile_m(), st));
+        // GPU experts (hits and fills) from the slot pool, once the fills landed
         if (c->xfer_pending) FT_HIP(hipStreamWaitEvent(st, c->ev_xlast, 0));
+        FT_HIP(launch_plan(c, routes, T, -1, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, st));
         FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
         FT_HIP(hipStreamWaitEvent(st, c->ev_host, 0));
         FT_HIP(launch_combine(c, routes, w, T, true, y, st));
@@ -355,7 +419,7 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         if (s != FT_OK) return s;
     }
     FT_HIP(hipStreamWaitEvent(st, c->ready[b], 0));
-    FT_HIP(launch_plan(c, routes, T, b * E, gemm_tile_m(), st));
+    FT_HIP(launch_plan(c, routes, T, b * E, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, st));
     FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
     FT_HIP(launch_combine(c, routes, w, T, false, y, st));
     FT_HIP(hipEventRecord(c->release[b], st));
@@ -465,6 +529,43 @@ ft_status ft_cache_stats(const ft_cache* c, ft_stats* o) {
     o->clock = clk;
     o->error_flags = err;
     o->num_slots = (int32_t)c->N;
+    return FT_OK;
+}
+
+ft_status ft_cache_set_timing(ft_cache* c, int32_t enable) {
+    clear_error();
+    FT_REQUIRE(c, "cache is null");
+    FT_HIP(hipDeviceSynchronize());
+    if (c->timing) {
+        timing_destroy(c->timing);
+        c->timing = nullptr;
+    }
+    const unsigned long long z[4] = {0, 0, 0, 0};
+    FT_HIP(hipMemcpy(c->counters + C_GEMV_EXPERTS, z, sizeof(z), hipMemcpyHostToDevice));
+    if (enable) {
+        c->timing = timing_create();
+        if (!c->timing->ok) {
+            timing_destroy(c->timing);
+            c->timing = nullptr;
+            set_error("timing events could not be created");
+            return FT_ERR_HIP;
+        }
+    }
+    return FT_OK;
+}
+
+ft_status ft_cache_timing(const ft_cache* c, ft_timing* o) {
+    clear_error();
+    FT_REQUIRE(c && o, "null pointer");
+    FT_HIP(hipDeviceSynchronize());
+    memset(o, 0, sizeof(*o));
+    if (c->timing) timing_read(c->timing, o->launches, o->ms);
+    unsigned long long w[4];
+    FT_HIP(hipMemcpy(w, c->counters + C_GEMV_EXPERTS, sizeof(w), hipMemcpyDeviceToHost));
+    o->gemv_experts = w[0];
+    o->gemv_rows = w[1];
+    o->gemm_experts = w[2];
+    o->gemm_rows = w[3];
     return FT_OK;
 }
 

@@ -22,7 +22,8 @@ constexpr int kSmallPlanRoutes = 1024; // routes handled by the one-workgroup pl
 constexpr int kGemvMaxTokens = 4;      // tokens per call served by the GEMV path
 
 // device counters (ft_stats order)
-enum { C_CALLS, C_ROUTES, C_UNIQUE, C_HITS, C_MISSES, C_FILLS, C_CPU, C_EVICT, C_BYTES, C_STREAMED, C_N };
+enum { C_CALLS, C_ROUTES, C_UNIQUE, C_HITS, C_MISSES, C_FILLS, C_CPU, C_EVICT, C_BYTES, C_STREAMED,
+       C_GEMV_EXPERTS, C_GEMV_ROWS, C_GEMM_EXPERTS, C_GEMM_ROWS, C_N };
 
 // ---- error plumbing -----------------------------------------------------------
 void set_error(const char* fmt, ...);
@@ -71,6 +72,15 @@ HostStaging host_branch_staging(HostBranch* hb);
 // (staging must already hold routes, w and x for those tokens).
 hipError_t host_branch_enqueue(HostBranch* hb, int32_t layer, int32_t T, hipStream_t stream);
 int host_branch_threads(HostBranch* hb);
+
+// ---- optional expert-kernel timing ------------------------------------------------
+struct Timing;
+Timing* timing_create();
+void timing_destroy(Timing* t);
+// Record the start event of a launch of class `cls`; returns the slot to close.
+int timing_begin(Timing* t, int cls, hipStream_t st);
+void timing_end(Timing* t, int slot, hipStream_t st);
+void timing_read(Timing* t, uint64_t* launches, double* ms);   // synchronises on pending events
 
 // ---- the cache handle ---------------------------------------------------------
 struct PlanBuffers {
@@ -129,6 +139,7 @@ struct ft_cache {
     hipEvent_t ready[2], release[2];
     bool release_recorded[2];
     ftmoe::HostBranch* host;
+    ftmoe::Timing* timing;     // null unless timing is enabled
 };
 
 namespace ftmoe {
@@ -143,7 +154,10 @@ hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int6
                                 int n, hipStream_t st);
 // plan: routes -> active slots, sorted rows, tiles.  slot_base >= 0 means routes
 // are raw expert ids mapped to slot slot_base + e (full-layer buffer).
-hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, hipStream_t st);
+// `work_counter` (C_GEMV_EXPERTS or C_GEMM_EXPERTS) receives the active-slot
+// count and the next counter the row count.
+hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, int work_counter,
+                       hipStream_t st);
 hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, bool has_host,

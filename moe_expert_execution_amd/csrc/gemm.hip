@@ -225,10 +225,14 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(GemmArgs a) {
 }
 
 template <int FMT>
-hipError_t launch_fmt(const GemmArgs& a, int64_t max_tiles, hipStream_t st) {
+hipError_t launch_fmt(const GemmArgs& a, int64_t max_tiles, Timing* tm, hipStream_t st) {
     const int64_t g1 = max_tiles * (a.f / 64), g2 = max_tiles * (a.d / kBN);
+    int ts = tm ? timing_begin(tm, FT_K_GEMM_GU, st) : -1;
     hipLaunchKernelGGL((gemm_kernel<FMT, true>), dim3((unsigned)g1), dim3(kGemmThreads), 0, st, a);
+    if (tm) timing_end(tm, ts, st);
+    ts = tm ? timing_begin(tm, FT_K_GEMM_DOWN, st) : -1;
     hipLaunchKernelGGL((gemm_kernel<FMT, false>), dim3((unsigned)g2), dim3(kGemmThreads), 0, st, a);
+    if (tm) timing_end(tm, ts, st);
     return hipGetLastError();
 }
 
@@ -263,9 +267,9 @@ hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     const int64_t max_tiles = (R + kBM - 1) / kBM + act;
     if (max_tiles > c->plan.max_tiles) return hipErrorInvalidValue;
     switch (c->sh.fmt) {
-        case FT_FMT_BF16: return launch_fmt<FT_FMT_BF16>(a, max_tiles, st);
-        case FT_FMT_FP8_B128: return launch_fmt<FT_FMT_FP8_B128>(a, max_tiles, st);
-        case FT_FMT_MXFP4_B32: return launch_fmt<FT_FMT_MXFP4_B32>(a, max_tiles, st);
+        case FT_FMT_BF16: return launch_fmt<FT_FMT_BF16>(a, max_tiles, c->timing, st);
+        case FT_FMT_FP8_B128: return launch_fmt<FT_FMT_FP8_B128>(a, max_tiles, c->timing, st);
+        case FT_FMT_MXFP4_B32: return launch_fmt<FT_FMT_MXFP4_B32>(a, max_tiles, c->timing, st);
     }
     return hipErrorInvalidValue;
 }

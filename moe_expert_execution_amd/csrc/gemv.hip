@@ -321,9 +321,13 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_down_kernel(GemvArgs a) {
 }
 
 template <int FMT, int TG>
-hipError_t launch_fmt(const GemvArgs& a, hipStream_t st) {
+hipError_t launch_fmt(const GemvArgs& a, Timing* tm, hipStream_t st) {
+    int ts = tm ? timing_begin(tm, FT_K_GEMV_GU, st) : -1;
     hipLaunchKernelGGL((gemv_gateup_kernel<FMT, TG>), dim3(kGemvBlocks), dim3(kGemvThreads), 0, st, a);
+    if (tm) timing_end(tm, ts, st);
+    ts = tm ? timing_begin(tm, FT_K_GEMV_DOWN, st) : -1;
     hipLaunchKernelGGL((gemv_down_kernel<FMT, TG>), dim3(kGemvBlocks), dim3(kGemvThreads), 0, st, a);
+    if (tm) timing_end(tm, ts, st);
     return hipGetLastError();
 }
 
@@ -356,12 +360,12 @@ hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     const bool one = T == 1;
     switch (c->sh.fmt) {
         case FT_FMT_BF16:
-            return one ? launch_fmt<FT_FMT_BF16, 1>(a, st) : launch_fmt<FT_FMT_BF16, kGemvMaxTokens>(a, st);
+            return one ? launch_fmt<FT_FMT_BF16, 1>(a, c->timing, st) : launch_fmt<FT_FMT_BF16, kGemvMaxTokens>(a, c->timing, st);
         case FT_FMT_FP8_B128:
-            return one ? launch_fmt<FT_FMT_FP8_B128, 1>(a, st) : launch_fmt<FT_FMT_FP8_B128, kGemvMaxTokens>(a, st);
+            return one ? launch_fmt<FT_FMT_FP8_B128, 1>(a, c->timing, st) : launch_fmt<FT_FMT_FP8_B128, kGemvMaxTokens>(a, c->timing, st);
         case FT_FMT_MXFP4_B32:
-            return one ? launch_fmt<FT_FMT_MXFP4_B32, 1>(a, st)
-                       : launch_fmt<FT_FMT_MXFP4_B32, kGemvMaxTokens>(a, st);
+            return one ? launch_fmt<FT_FMT_MXFP4_B32, 1>(a, c->timing, st)
+                       : launch_fmt<FT_FMT_MXFP4_B32, kGemvMaxTokens>(a, c->timing, st);
     }
     return hipErrorInvalidValue;
 }

@@ -41,6 +41,7 @@ struct PlanArgs {
     int32_t* tile_active;
     int32_t* tile_row0;
     int32_t* chunk_counts;
+    unsigned long long* work;   // [2]: active slots, rows (accumulated)
 };
 
 // Slot of route r, or -1 when it is not a GPU route (host, invalid, duplicate).
@@ -167,6 +168,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_small_kernel(PlanArgs a) {
         a.seg[n_active] = rows;
         a.meta[0] = n_active;
         a.meta[2] = rows;
+        atomicAdd(&a.work[0], (unsigned long long)n_active);
+        atomicAdd(&a.work[1], (unsigned long long)rows);
     }
     __syncthreads();
     emit_tiles(a, n_active, wsum);
@@ -254,6 +257,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_scan_kernel(PlanArgs a, int
         a.seg[run_active] = run_rows;
         a.meta[0] = run_active;
         a.meta[2] = run_rows;
+        atomicAdd(&a.work[0], (unsigned long long)run_active);
+        atomicAdd(&a.work[1], (unsigned long long)run_rows);
     }
     __syncthreads();
     emit_tiles(a, run_active, wsum);
@@ -291,7 +296,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_scatter_kernel(PlanArgs a) 
 
 }  // namespace
 
-hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, hipStream_t st) {
+hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, int work_counter,
+                       hipStream_t st) {
     PlanArgs a;
     a.routes = routes;
     a.k = c->sh.top_k;
@@ -311,6 +317,7 @@ hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base,
     a.tile_active = c->plan.tile_active;
     a.tile_row0 = c->plan.tile_row0;
     a.chunk_counts = c->plan.chunk_counts;
+    a.work = c->counters + work_counter;
     if (a.R <= kSmallPlanRoutes) {
         hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
     } else {
