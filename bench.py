@@ -104,7 +104,8 @@ def decode_bench(args):
     s1 = M.ft_cache_stats(h).as_dict()
     elapsed = t1 - t0
     delta = {key: s1[key] - s0[key] for key in ("calls", "unique", "hits", "misses", "fills", "cpu_experts",
-                                                "evictions", "bytes_filled")}
+                                                "evictions", "bytes_filled", "host_experts", "host_bytes",
+                                                "host_seconds")}
     assert s1["error_flags"] == 0, s1
     # algorithmic bytes: each GPU-executed expert's gate and up banks are read
     # once by the gate/up GEMV, its down bank once by the down GEMV
@@ -133,11 +134,21 @@ def decode_bench(args):
             "gpu_experts_per_layer_step": experts / max(n_gu, 1),
         },
         "cache": {**delta, "layer_calls": delta["calls"],
-                  "miss_rate": delta["misses"] / max(delta["unique"], 1),
-                  "fill_gbs_effective": delta["bytes_filled"] / elapsed / 1e9},
+                  "miss_rate": delta["misses"] / max(delta["unique"], 1)},
+        "branches": {
+            # achieved B_P: record bytes over the fill kernels' event time
+            "fill_gbs": delta["bytes_filled"] / max(tm.ms[M.FT_K_FILL] / 1e3, 1e-12) / 1e9,
+            "fill_ms_total": tm.ms[M.FT_K_FILL],
+            # achieved B_H: record bytes the host workers read over their busy time
+            "host_gbs": delta["host_bytes"] / max(delta["host_seconds"], 1e-12) / 1e9,
+            "host_seconds_total": delta["host_seconds"],
+            "host_threads_env": os.environ.get("FTMOE_HOST_THREADS", "default"),
+        },
     }
     log(f"decode: {res['value']:.1f} tok/s, {res['ms_per_step']:.2f} ms/step, gate/up GEMV {gu_gbs:.0f} GB/s "
-        f"({gu_gbs / HBM_PEAK_GBS:.1%}), pair {both_gbs:.0f} GB/s, miss rate {res['cache']['miss_rate']:.2f}")
+        f"({gu_gbs / HBM_PEAK_GBS:.1%}), pair {both_gbs:.0f} GB/s, miss rate {res['cache']['miss_rate']:.2f}, "
+        f"fill {res['branches']['fill_gbs']:.1f} GB/s, host {res['branches']['host_gbs']:.1f} GB/s "
+        f"({delta['host_seconds']:.2f}s busy of {elapsed:.2f}s)")
     sc.close()
     return res, bank, cfg
 
@@ -287,6 +298,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_kernels": dec["decode_kernels"],
         "cache": dec["cache"],
+        "branches": dec["branches"],
         "prefill": pre,
     }
     print(json.dumps(line), flush=True)

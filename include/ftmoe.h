@@ -119,8 +119,13 @@ typedef struct {
     uint64_t bytes_filled;   /* record bytes copied host -> slot by fills        */
     uint64_t layers_streamed;/* full-layer loads into the two buffers            */
     uint64_t clock;          /* LRU clock (starts at 1)                          */
-    int32_t error_flags;     /* sticky device flags: 1 = expert id out of range  */
+    int32_t error_flags;     /* sticky device flags: 1 = expert id out of range,
+                                2 = LRU clock past 2^40, 4 = repeated expert in a
+                                token's routes (the repeat is dropped)          */
     int32_t num_slots;
+    uint64_t host_experts;   /* expert FFNs run by the host workers               */
+    uint64_t host_bytes;     /* expert-record bytes the host workers read         */
+    double host_seconds;     /* wall time of host-branch calls that had work      */
 } ft_stats;
 
 /* ---------------------------------------------------------------------------
@@ -242,12 +247,13 @@ ft_status ft_cache_stats(const ft_cache* cache, ft_stats* out);
 
 /* Expert-kernel timing (measurement support).  When enabled, every
  * ft_moe_forward brackets its expert kernels with HIP events on the caller's
- * stream; ft_cache_timing synchronises and returns, per kernel class
- * (0 GEMV gate/up, 1 GEMV down, 2 GEMM gate/up, 3 GEMM down), the number of
- * launches and their summed event durations, plus device-side counts of the
- * work those launches did: expert records read (one per active slot per call)
- * and GPU rows (routes) computed. */
-enum { FT_K_GEMV_GU = 0, FT_K_GEMV_DOWN = 1, FT_K_GEMM_GU = 2, FT_K_GEMM_DOWN = 3, FT_K_COUNT = 4 };
+ * stream and every ft_cache_classify its fill kernel on the transfer stream;
+ * ft_cache_timing synchronises and returns, per kernel class (0 GEMV gate/up,
+ * 1 GEMV down, 2 GEMM gate/up, 3 GEMM down, 4 fill), the number of launches
+ * and their summed event durations, plus device-side counts of the work those
+ * launches did: expert records read (one per active slot per call) and GPU
+ * rows (routes) computed. */
+enum { FT_K_GEMV_GU = 0, FT_K_GEMV_DOWN = 1, FT_K_GEMM_GU = 2, FT_K_GEMM_DOWN = 3, FT_K_FILL = 4, FT_K_COUNT = 5 };
 typedef struct {
     uint64_t launches[FT_K_COUNT];
     double ms[FT_K_COUNT];

@@ -41,17 +41,18 @@ class FtClassifyOut(ctypes.Structure):
 class FtStats(ctypes.Structure):
     _fields_ = [("calls", u64), ("routes", u64), ("unique", u64), ("hits", u64), ("misses", u64), ("fills", u64),
                 ("cpu_experts", u64), ("evictions", u64), ("bytes_filled", u64), ("layers_streamed", u64),
-                ("clock", u64), ("error_flags", i32), ("num_slots", i32)]
+                ("clock", u64), ("error_flags", i32), ("num_slots", i32), ("host_experts", u64),
+                ("host_bytes", u64), ("host_seconds", ctypes.c_double)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
-FT_K_GEMV_GU, FT_K_GEMV_DOWN, FT_K_GEMM_GU, FT_K_GEMM_DOWN = range(4)
+FT_K_GEMV_GU, FT_K_GEMV_DOWN, FT_K_GEMM_GU, FT_K_GEMM_DOWN, FT_K_FILL = range(5)
 
 
 class FtTiming(ctypes.Structure):
-    _fields_ = [("launches", u64 * 4), ("ms", ctypes.c_double * 4), ("gemv_experts", u64), ("gemv_rows", u64),
+    _fields_ = [("launches", u64 * 5), ("ms", ctypes.c_double * 5), ("gemv_experts", u64), ("gemv_rows", u64),
                 ("gemm_experts", u64), ("gemm_rows", u64)]
 
 

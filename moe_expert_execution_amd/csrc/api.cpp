@@ -126,6 +126,8 @@ void timing_read(Timing* t, uint64_t* launches, double* ms) {
 
 namespace {
 
+ft_status flush_fill(ft_cache* c, hipStream_t st);
+
 template <typename T>
 hipError_t dalloc(T** p, size_t n) {
     return hipMalloc(reinterpret_cast<void**>(p), n * sizeof(T) + 256);
@@ -145,13 +147,14 @@ ft_status check_shape(const ft_shape* s) {
 
 void free_cache(ft_cache* c) {
     if (!c) return;
+    if (c->fill_pending) (void)flush_fill(c, c->fill_stream);
     (void)hipDeviceSynchronize();
     if (c->host) host_branch_destroy(c->host);
     if (c->timing) timing_destroy(c->timing);
     void* bufs[] = {c->pool, c->slot_for_id, c->id_of_slot, c->stamp, c->clock, c->counters, c->errflag,
                     c->wl_counts, c->wl_slot, c->wl_src, c->plan.meta, c->plan.active_slot, c->plan.seg,
                     c->plan.perm, c->plan.route_pos, c->plan.tile_active, c->plan.tile_row0,
-                    c->plan.chunk_counts, c->H, c->Y, c->Pdev, c->gv_part, c->gv_counters, c->gv_H};
+                    c->plan.chunk_counts, c->H, c->Y, c->gv_H};
     for (void* b : bufs)
         if (b) (void)hipFree(b);
     hipEvent_t evs[] = {c->ev_ctrl, c->ev_fwd, c->ev_host, c->ev_xlast, c->ev_fence,
@@ -175,6 +178,27 @@ hipError_t alloc_plan(ft_cache* c) {
     if ((e = dalloc(&c->plan.tile_row0, c->plan.max_tiles))) return e;
     if ((e = dalloc(&c->plan.chunk_counts, chunks * std::min<int64_t>(keyspace, 8192)))) return e;
     return hipSuccess;
+}
+
+// Enqueue the fills chosen by the last classify (if not yet enqueued) on `st`.
+// Classify leaves them pending so that forward can first stage the host
+// branch's inputs: the copy over PCIe and the host experts then run together.
+// Every later call on the cache flushes a pending fill before it can read a slot.
+ft_status flush_fill(ft_cache* c, hipStream_t st) {
+    if (!c->fill_pending) return FT_OK;
+    const int ts = c->timing ? timing_begin(c->timing, FT_K_FILL, st) : -1;
+    FT_HIP(launch_fill(c, st));
+    if (c->timing) timing_end(c->timing, ts, st);
+    c->fill_pending = false;
+    return FT_OK;
+}
+
+// Flush on the stream of the classify that chose the fills (sync points).
+ft_status flush_fill_sync(ft_cache* c) {
+    ft_status s = flush_fill(c, c->fill_stream);
+    if (s != FT_OK) return s;
+    FT_HIP(hipDeviceSynchronize());
+    return FT_OK;
 }
 
 ft_status enqueue_load(ft_cache* c, int layer, int buf, hipStream_t st) {
@@ -293,10 +317,7 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     CK(alloc_plan(c));
     CK(dalloc(&c->H, cap * f));
     CK(dalloc(&c->Y, cap * d));
-    CK(dalloc(&c->Pdev, (int64_t)max_tokens * d));
     c->cap_gemv = std::min<int32_t>(max_tokens, kGemvMaxTokens) * shape->top_k;
-    CK(dalloc(&c->gv_part, (int64_t)8 * c->cap_gemv * f * 2));
-    CK(dalloc(&c->gv_counters, (int64_t)c->cap_gemv * (f / 16)));
     CK(dalloc(&c->gv_H, (int64_t)c->cap_gemv * f));
     CK(hipMemset(c->slot_for_id, 0xFF, sizeof(int32_t) * L * E));
     CK(hipMemset(c->id_of_slot, 0xFF, sizeof(int32_t) * c->N));
@@ -305,7 +326,6 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     CK(hipMemcpy(c->clock, &one, sizeof(one), hipMemcpyHostToDevice));
     CK(hipMemset(c->counters, 0, sizeof(unsigned long long) * C_N));
     CK(hipMemset(c->errflag, 0, sizeof(int32_t)));
-    CK(hipMemset(c->gv_counters, 0, sizeof(int32_t) * c->cap_gemv * (f / 16)));
     CK(hipMemset(c->plan.meta, 0, sizeof(int32_t) * 4));
     CK(hipStreamCreateWithFlags(&c->xfer, hipStreamNonBlocking));
     CK(hipStreamCreateWithFlags(&c->hstream, hipStreamNonBlocking));
@@ -356,16 +376,16 @@ ft_status ft_cache_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t T,
         FT_REQUIRE(out->capacity >= T * c->sh.top_k, "out capacity %d < T*k", out->capacity);
     }
     hipStream_t st = (hipStream_t)stream;
-    // earlier fills and full-layer loads must be done before the maps are read
+    // fills of a previous classify that no forward consumed, and full-layer
+    // loads, land before this call reads the maps
+    ft_status fs = flush_fill(c, st);
+    if (fs != FT_OK) return fs;
     if (c->xfer_pending) FT_HIP(hipStreamWaitEvent(st, c->ev_xlast, 0));
     c->streaming = false;
     c->buf_layer[0] = c->buf_layer[1] = -1;     // decode fills may reuse buffer slots
     FT_HIP(launch_classify(c, layer, ids, T * c->sh.top_k, out, st));
-    FT_HIP(hipEventRecord(c->ev_ctrl, st));
-    FT_HIP(hipStreamWaitEvent(c->xfer, c->ev_ctrl, 0));
-    FT_HIP(launch_fill(c, c->xfer));
-    FT_HIP(hipEventRecord(c->ev_xlast, c->xfer));
-    c->xfer_pending = true;
+    c->fill_pending = true;
+    c->fill_stream = st;
     return FT_OK;
 }
 
@@ -384,26 +404,36 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
     const int64_t d = c->sh.d_model;
     const bool gemv = T <= kGemvMaxTokens;
     if (m == FT_MODE_CACHED) {
-        // host branch: copy the call's routes, weights and activations to pinned
-        // staging, run the host experts, copy their partial sum back
+        // host branch: the planner copies the call's routes, weights and
+        // activations into pinned staging and, with the mailbox, posts the
+        // call's sequence number; the host workers run the host experts and
+        // leave their partial sums in pinned memory
         HostStaging hs = host_branch_staging(c->host);
-        FT_HIP(hipEventRecord(c->ev_fwd, st));
-        FT_HIP(hipStreamWaitEvent(c->hstream, c->ev_fwd, 0));
-        FT_HIP(hipMemcpyAsync(hs.routes, routes, sizeof(int32_t) * T * k, hipMemcpyDeviceToHost, c->hstream));
-        FT_HIP(hipMemcpyAsync(hs.w, w, sizeof(float) * T * k, hipMemcpyDeviceToHost, c->hstream));
-        FT_HIP(hipMemcpyAsync(hs.x, x, sizeof(uint16_t) * T * d, hipMemcpyDeviceToHost, c->hstream));
-        FT_HIP(host_branch_enqueue(c->host, layer, T, c->hstream));
-        FT_HIP(hipMemcpyAsync(c->Pdev, hs.P, sizeof(float) * T * d, hipMemcpyHostToDevice, c->hstream));
-        FT_HIP(hipEventRecord(c->ev_host, c->hstream));
-        // GPU experts (hits and fills) from the slot pool, once the fills landed
+        HostSignal sig = host_branch_prepare(c->host, layer, T);
+        FT_HIP(launch_plan(c, routes, T, -1, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, w, x, &hs, &sig,
+                           st));
+        if (!sig.mailbox) {
+            FT_HIP(hipEventRecord(c->ev_fwd, st));
+            FT_HIP(hipStreamWaitEvent(c->hstream, c->ev_fwd, 0));
+            FT_HIP(host_branch_enqueue(c->host, layer, T, c->hstream));
+            FT_HIP(hipEventRecord(c->ev_host, c->hstream));
+        }
+        // this layer's fills, then the GPU experts (hits and fills) from the slot pool
+        ft_status fs = flush_fill(c, st);
+        if (fs != FT_OK) return fs;
         if (c->xfer_pending) FT_HIP(hipStreamWaitEvent(st, c->ev_xlast, 0));
-        FT_HIP(launch_plan(c, routes, T, -1, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, st));
         FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
-        FT_HIP(hipStreamWaitEvent(st, c->ev_host, 0));
-        FT_HIP(launch_combine(c, routes, w, T, true, y, st));
+        if (sig.mailbox) {
+            FT_HIP(hipStreamWaitValue64(st, sig.done_word, sig.seq, hipStreamWaitValueGte, ~0ull));
+        } else {
+            FT_HIP(hipStreamWaitEvent(st, c->ev_host, 0));
+        }
+        FT_HIP(launch_combine(c, routes, w, T, hs.P, y, st));
         return FT_OK;
     }
     // STREAMED: full-layer buffer layer % 2
+    ft_status fs = flush_fill(c, st);
+    if (fs != FT_OK) return fs;
     const int E = c->sh.experts;
     if (c->N < 2 * (int64_t)E) {
         set_error("STREAMED mode needs num_slots >= 2E (%lld < %d)", (long long)c->N, 2 * E);
@@ -419,9 +449,10 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         if (s != FT_OK) return s;
     }
     FT_HIP(hipStreamWaitEvent(st, c->ready[b], 0));
-    FT_HIP(launch_plan(c, routes, T, b * E, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, st));
+    FT_HIP(launch_plan(c, routes, T, b * E, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, w, x, nullptr,
+                       nullptr, st));
     FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
-    FT_HIP(launch_combine(c, routes, w, T, false, y, st));
+    FT_HIP(launch_combine(c, routes, w, T, nullptr, y, st));
     FT_HIP(hipEventRecord(c->release[b], st));
     c->release_recorded[b] = true;
     if ((mode & FT_PREFETCH_NEXT) && layer + 1 < c->sh.layers) {
@@ -438,7 +469,8 @@ ft_status ft_cache_resize(ft_cache* c, int64_t new_num_slots) {
     clear_error();
     FT_REQUIRE(c, "cache is null");
     FT_REQUIRE(new_num_slots >= 1 && new_num_slots <= kMaxSlots, "num_slots must be in 1..%d", kMaxSlots);
-    FT_HIP(hipDeviceSynchronize());
+    ft_status fs = flush_fill_sync(c);
+    if (fs != FT_OK) return fs;
     const int64_t L = c->sh.layers, E = c->sh.experts, S = c->rl.S, N = c->N, Nn = new_num_slots;
     std::vector<int32_t> ios(N);
     std::vector<uint64_t> stamp(N);
@@ -509,7 +541,8 @@ ft_status ft_cache_resize(ft_cache* c, int64_t new_num_slots) {
 ft_status ft_cache_stats(const ft_cache* c, ft_stats* o) {
     clear_error();
     FT_REQUIRE(c && o, "null pointer");
-    FT_HIP(hipDeviceSynchronize());
+    ft_status fs = flush_fill_sync(const_cast<ft_cache*>(c));
+    if (fs != FT_OK) return fs;
     unsigned long long cnt[C_N];
     uint64_t clk;
     int32_t err;
@@ -529,13 +562,15 @@ ft_status ft_cache_stats(const ft_cache* c, ft_stats* o) {
     o->clock = clk;
     o->error_flags = err;
     o->num_slots = (int32_t)c->N;
+    host_branch_counters(c->host, &o->host_bytes, &o->host_seconds, &o->host_experts);
     return FT_OK;
 }
 
 ft_status ft_cache_set_timing(ft_cache* c, int32_t enable) {
     clear_error();
     FT_REQUIRE(c, "cache is null");
-    FT_HIP(hipDeviceSynchronize());
+    ft_status fs = flush_fill_sync(c);
+    if (fs != FT_OK) return fs;
     if (c->timing) {
         timing_destroy(c->timing);
         c->timing = nullptr;
@@ -557,7 +592,8 @@ ft_status ft_cache_set_timing(ft_cache* c, int32_t enable) {
 ft_status ft_cache_timing(const ft_cache* c, ft_timing* o) {
     clear_error();
     FT_REQUIRE(c && o, "null pointer");
-    FT_HIP(hipDeviceSynchronize());
+    ft_status fs = flush_fill_sync(const_cast<ft_cache*>(c));
+    if (fs != FT_OK) return fs;
     memset(o, 0, sizeof(*o));
     if (c->timing) timing_read(c->timing, o->launches, o->ms);
     unsigned long long w[4];
@@ -573,7 +609,8 @@ ft_status ft_cache_snapshot(const ft_cache* c, int32_t* slot_for_id, int32_t* id
                             uint64_t* clock) {
     clear_error();
     FT_REQUIRE(c, "cache is null");
-    FT_HIP(hipDeviceSynchronize());
+    ft_status fs = flush_fill_sync(const_cast<ft_cache*>(c));
+    if (fs != FT_OK) return fs;
     const int64_t LE = (int64_t)c->sh.layers * c->sh.experts;
     if (slot_for_id) FT_HIP(hipMemcpy(slot_for_id, c->slot_for_id, sizeof(int32_t) * LE, hipMemcpyDeviceToHost));
     if (id_of_slot) FT_HIP(hipMemcpy(id_of_slot, c->id_of_slot, sizeof(int32_t) * c->N, hipMemcpyDeviceToHost));
@@ -586,7 +623,8 @@ ft_status ft_cache_read_slot(const ft_cache* c, int64_t slot, void* dst) {
     clear_error();
     FT_REQUIRE(c && dst, "null pointer");
     FT_REQUIRE(slot >= 0 && slot < c->N, "slot out of range");
-    FT_HIP(hipDeviceSynchronize());
+    ft_status fs = flush_fill_sync(const_cast<ft_cache*>(c));
+    if (fs != FT_OK) return fs;
     FT_HIP(hipMemcpy(dst, c->pool + slot * c->rl.S, (size_t)c->rl.S, hipMemcpyDeviceToHost));
     return FT_OK;
 }

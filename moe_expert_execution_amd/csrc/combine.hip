@@ -12,8 +12,8 @@ constexpr int kCombThreads = 256;
 
 __global__ void __launch_bounds__(kCombThreads)
     combine_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ route_pos,
-                   const float* __restrict__ w, const float* __restrict__ Y, const float* __restrict__ P, int T,
-                   int k, int d, int has_host, uint16_t* __restrict__ y) {
+                   const float* __restrict__ w, const float* __restrict__ Y, const float* P, int T, int k, int d,
+                   uint16_t* __restrict__ y) {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * kCombThreads + threadIdx.x) * 4;
     if (t >= T || c >= d) return;
@@ -34,12 +34,13 @@ __global__ void __launch_bounds__(kCombThreads)
             host |= (rv < 0 && rv != INT32_MIN);
         }
     }
-    if (has_host && host) {
-        const float4 v = *reinterpret_cast<const float4*>(P + (int64_t)t * d + c);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+    if (P && host) {
+        // pinned host memory written by the host workers: system-scope loads
+        const float* p = P + (int64_t)t * d + c;
+        acc.x += __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        acc.y += __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        acc.z += __hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        acc.w += __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     uint2 o;
     o.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
@@ -49,13 +50,13 @@ __global__ void __launch_bounds__(kCombThreads)
 
 }  // namespace
 
-hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, bool has_host, uint16_t* y,
+hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, const float* P, uint16_t* y,
                           hipStream_t st) {
     if (T <= 0) return hipSuccess;
     const int d = c->sh.d_model;
     dim3 grid((d / 4 + kCombThreads - 1) / kCombThreads, T);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, st, routes, c->plan.route_pos, w, c->Y,
-                       c->Pdev, T, c->sh.top_k, d, has_host ? 1 : 0, y);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, st, routes, c->plan.route_pos, w, c->Y, P, T,
+                       c->sh.top_k, d, y);
     return hipGetLastError();
 }
 

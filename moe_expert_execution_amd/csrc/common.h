@@ -68,10 +68,23 @@ struct HostStaging {
     float* P;          // [max_tokens x d]
 };
 HostStaging host_branch_staging(HostBranch* hb);
+// How a forward call hands work to the host branch.  Mailbox: the planner
+// stores `seq` to *seq_word (pinned) after staging; a polling host thread runs
+// the call and stores `seq` to *done_word, which the stream waits for.
+// Otherwise a stream host function runs the call.
+struct HostSignal {
+    bool mailbox;
+    uint64_t seq;
+    uint64_t* seq_word;
+    uint64_t* done_word;
+};
+HostSignal host_branch_prepare(HostBranch* hb, int32_t layer, int32_t T);
 // Enqueue the host computation of layer `layer` for T tokens on `stream`
 // (staging must already hold routes, w and x for those tokens).
 hipError_t host_branch_enqueue(HostBranch* hb, int32_t layer, int32_t T, hipStream_t stream);
 int host_branch_threads(HostBranch* hb);
+// bytes of expert records the workers read, and seconds spent in host calls with work
+void host_branch_counters(HostBranch* hb, uint64_t* bytes, double* seconds, uint64_t* experts);
 
 // ---- optional expert-kernel timing ------------------------------------------------
 struct Timing;
@@ -123,16 +136,15 @@ struct ft_cache {
     ftmoe::PlanBuffers plan;
     uint16_t* H;               // [cap x f] bf16 (GEMM path)
     float* Y;                  // [cap x d] fp32
-    float* Pdev;               // [max_tokens x d] fp32
     int32_t cap_gemv;          // rows served by the GEMV path
-    float* gv_part;            // GEMV K-split partials
-    int32_t* gv_counters;      // GEMV last-block counters (self-resetting)
     float* gv_H;               // [cap_gemv x f] fp32 (GEMV path)
     // streams and events
     hipStream_t xfer;          // transfer stream (fills, full-layer loads)
     hipStream_t hstream;       // host-branch copies and host function
     hipEvent_t ev_ctrl, ev_fwd, ev_host, ev_xlast, ev_fence;
     bool xfer_pending;         // ev_xlast recorded
+    bool fill_pending;         // the last classify's fills are not enqueued yet
+    hipStream_t fill_stream;   // the stream of that classify
     bool streaming;            // inside a run of STREAMED calls (beginning fence taken)
     // full-layer buffers
     int buf_layer[2];
@@ -156,11 +168,16 @@ hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int6
 // are raw expert ids mapped to slot slot_base + e (full-layer buffer).
 // `work_counter` (C_GEMV_EXPERTS or C_GEMM_EXPERTS) receives the active-slot
 // count and the next counter the row count.
+// With `stage`, routes, w and x of the call are also copied into the host
+// branch's pinned staging.
 hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, int work_counter,
+                       const float* w, const uint16_t* x, const HostStaging* stage, const HostSignal* sig,
                        hipStream_t st);
 hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
-hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, bool has_host,
+// P: the host branch's partial sums [T x d] in pinned host memory (null when
+// the call has no host branch).
+hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, const float* P,
                           uint16_t* y, hipStream_t st);
 int gemm_tile_m();
 }  // namespace ftmoe

@@ -1,14 +1,15 @@
 // Decode expert FFN: bandwidth-bound split-K GEMVs over the active slots.
 //
 // Each active slot serves a few token rows (decode: usually one).  Gate/up:
-// every workgroup item is (slot, 16 neurons, K-split); each wave streams the
-// gate and up rows of 4 neurons with coalesced 16-byte loads (one 64-lane
-// wave covers 1 KiB of a row), the split count adapts to the number of active
-// slots read from the device so the grid stays full, and the last workgroup
-// of each (slot, neuron block) — found with one atomic counter, no waiting —
-// adds the K-split partials in a fixed order and applies SwiGLU,
-// h = silu(g) * u, into fp32 H.  Down: (slot, 16 output columns) items read the
-// down rows and H and write fp32 Y per sorted row.  The expert FFN (gate/up
+// every workgroup item is (slot, 8 neurons): the 16 gate and up rows are read
+// with coalesced 16-byte loads, K split over the four waves (each lane one
+// 16-byte chunk of every row per step, so 16 loads are in flight per lane);
+// wave sums and then the four K-quarters are added in a fixed order inside the
+// workgroup — no cross-workgroup reduction, no device-scope fence — and SwiGLU,
+// h = silu(g) * u, is written to fp32 H.  Work items are counted from the
+// device-side number of active slots, so one fixed grid serves any hit/fill
+// mix.  Down: (slot, 16 output columns) items read the down rows and H and
+// write fp32 Y per sorted row.  The expert FFN (gate/up
 // then down, from one slot record) is the one "The Expert Cache That Follows
 // the Router" describes in section "One logical expert, two physical levels of
 // memory"; SwiGLU is this build's activation.
@@ -17,9 +18,8 @@
 namespace ftmoe {
 
 constexpr int kGemvThreads = 256;
-constexpr int kGemvMaxKS = 8;
 constexpr int kGemvBlocks = 1024;
-constexpr int kGemvNeurons = 16;    // per gate/up item (4 waves x 4)
+constexpr int kGemvNeurons = 8;     // per gate/up item: 8 gate + 8 up rows, K split over the 4 waves
 constexpr int kGemvCols = 16;       // per down item (4 waves x 4)
 
 struct GemvArgs {
@@ -32,8 +32,6 @@ struct GemvArgs {
     const uint8_t* pool;
     int64_t S;
     int64_t off_gate, off_up, off_down, off_sg, off_su, off_sd;
-    float* part;        // [kGemvMaxKS][cap_g][f][2]
-    int32_t* counters;  // [cap_g][f / 16], zero between calls
     float* Hf;          // [cap_g][f]
     float* Y;           // [cap][d]
     int cap_g;
@@ -139,122 +137,115 @@ template <int FMT, int TG>
 __global__ void __launch_bounds__(kGemvThreads) gemv_gateup_kernel(GemvArgs a) {
     constexpr int EPC = WF<FMT>::EPC;
     constexpr int XW = EPC / 2;     // packed bf16 words of x per chunk
-    __shared__ int sh_last;
+    constexpr int NN = kGemvNeurons;
+    __shared__ float red[4][NN][2][TG];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int n_active = a.meta[0];
     const int d = a.d, f = a.f;
-    const int NB = f / kGemvNeurons;
-    const int cpr = d / EPC;
-    const int nwc = (cpr + 63) / 64;
-    const int base_items = n_active * NB;
-    if (base_items == 0) return;
-    int KS = ((int)gridDim.x + base_items - 1) / base_items;
-    KS = KS < 1 ? 1 : KS;
-    KS = KS > nwc ? nwc : KS;
-    KS = KS > kGemvMaxKS ? kGemvMaxKS : KS;
-    const int items = base_items * KS;
+    const int NB = f / NN;
+    const int items = n_active * NB;
+    const int cpr = d / EPC;                 // 16-byte chunks per row
+    const int cpw = (cpr + 3) / 4;           // the K quarter of each wave
+    const int c_begin = wid * cpw;
+    const int c_end = (c_begin + cpw) < cpr ? (c_begin + cpw) : cpr;
     const int64_t rowb = WF<FMT>::row_bytes(d);
 
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        const int ai = item / (NB * KS);
-        const int rem = item - ai * NB * KS;
-        const int nb = rem / KS;
-        const int ks = rem - nb * KS;
+        const int ai = item / NB;
+        const int nb = item - ai * NB;
         const int slot = a.active_slot[ai];
         const int r0 = a.seg[ai];
         int nrows = a.seg[ai + 1] - r0;
         nrows = nrows > TG ? TG : nrows;
         const uint8_t* rec = a.pool + (int64_t)slot * a.S;
-        const int n0 = nb * kGemvNeurons + wid * 4;
-        const int wc0 = ks * nwc / KS, wc1 = (ks + 1) * nwc / KS;
+        const int n0 = nb * NN;
 
         const uint16_t* xr[TG];
 #pragma unroll
         for (int t = 0; t < TG; ++t) {
-            int rr = r0 + (t < nrows ? t : nrows - 1);
+            const int rr = r0 + (t < nrows ? t : nrows - 1);
             xr[t] = a.x + (int64_t)(a.perm[rr] / a.k) * d;
         }
-        float acc[4][2][TG];
+        float acc[NN][2][TG];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NN; ++i)
 #pragma unroll
             for (int g = 0; g < 2; ++g)
 #pragma unroll
                 for (int t = 0; t < TG; ++t) acc[i][g][t] = 0.0f;
 
-        for (int wc = wc0; wc < wc1; ++wc) {
-            const int c = wc * 64 + lane;
-            if (c < cpr) {
-                const int k0 = c * EPC;
-                uint4 wv[4][2];
+        for (int c = c_begin + lane; c < c_end; c += 64) {
+            const int k0 = c * EPC;
+            uint4 wv[NN][2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    wv[i][0] = *reinterpret_cast<const uint4*>(rec + a.off_gate + (int64_t)(n0 + i) * rowb + c * 16);
-                    wv[i][1] = *reinterpret_cast<const uint4*>(rec + a.off_up + (int64_t)(n0 + i) * rowb + c * 16);
-                }
-                float sc[4][2];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if constexpr (FMT == FT_FMT_MXFP4_B32) {
-                        sc[i][0] = chunk_scale<FMT>(rec, a.off_sg, n0 + i, k0, d);
-                        sc[i][1] = chunk_scale<FMT>(rec, a.off_su, n0 + i, k0, d);
-                    } else {
-                        sc[i][0] = chunk_scale<FMT>(rec, a.off_sg, n0, k0, d);
-                        sc[i][1] = chunk_scale<FMT>(rec, a.off_su, n0, k0, d);
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < TG; ++t) {
-                    uint32_t xw[XW];
-#pragma unroll
-                    for (int q = 0; q < XW / 4; ++q) {
-                        uint4 v = *reinterpret_cast<const uint4*>(xr[t] + k0 + 8 * q);
-                        xw[4 * q] = v.x;
-                        xw[4 * q + 1] = v.y;
-                        xw[4 * q + 2] = v.z;
-                        xw[4 * q + 3] = v.w;
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int g = 0; g < 2; ++g) acc[i][g][t] += chunk_dot_bf16x<FMT>(wv[i][g], sc[i][g], xw);
-                }
+            for (int i = 0; i < NN; ++i) {
+                wv[i][0] = *reinterpret_cast<const uint4*>(rec + a.off_gate + (int64_t)(n0 + i) * rowb + c * 16);
+                wv[i][1] = *reinterpret_cast<const uint4*>(rec + a.off_up + (int64_t)(n0 + i) * rowb + c * 16);
             }
-        }
-        // wave sums -> K-split partials
+            float sc[NN][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < NN; ++i) {
+                // FP8: the NN neurons share one 128-row scale block; MXFP4: one scale per row
+                const int nr = (FMT == FT_FMT_MXFP4_B32) ? n0 + i : n0;
+                sc[i][0] = chunk_scale<FMT>(rec, a.off_sg, nr, k0, d);
+                sc[i][1] = chunk_scale<FMT>(rec, a.off_su, nr, k0, d);
+            }
+            uint32_t xw[TG][XW];
+#pragma unroll
+            for (int t = 0; t < TG; ++t)
+#pragma unroll
+                for (int q = 0; q < XW / 4; ++q) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(xr[t] + k0 + 8 * q);
+                    xw[t][4 * q] = v.x;
+                    xw[t][4 * q + 1] = v.y;
+                    xw[t][4 * q + 2] = v.z;
+                    xw[t][4 * q + 3] = v.w;
+                }
+#pragma unroll
+            for (int i = 0; i < NN; ++i)
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    if constexpr (FMT == FT_FMT_BF16) {
+#pragma unroll
+                        for (int t = 0; t < TG; ++t) acc[i][g][t] += chunk_dot_bf16x<FMT>(wv[i][g], 1.0f, xw[t]);
+                    } else {
+                        // decode the chunk once, use it for every token
+                        float v[EPC];
+                        if constexpr (FMT == FT_FMT_FP8_B128) {
+                            WF<FMT>::to_f32(wv[i][g], v);
+                        } else {
+                            WF<FMT>::to_f32(wv[i][g], sc[i][g], v);
+                        }
+#pragma unroll
+                        for (int t = 0; t < TG; ++t) {
+                            float sacc = 0.0f;
+#pragma unroll
+                            for (int j = 0; j < XW; ++j) {
+                                sacc = fmaf(v[2 * j], bf16lo(xw[t][j]), sacc);
+                                sacc = fmaf(v[2 * j + 1], bf16hi(xw[t][j]), sacc);
+                            }
+                            acc[i][g][t] += (FMT == FT_FMT_FP8_B128) ? sacc * sc[i][g] : sacc;
+                        }
+                    }
+                }
+        }
+        // K-split partials: wave sums, then the four waves in a fixed order
+#pragma unroll
+        for (int i = 0; i < NN; ++i)
 #pragma unroll
             for (int g = 0; g < 2; ++g)
 #pragma unroll
                 for (int t = 0; t < TG; ++t) {
-                    float v = wave_sum(acc[i][g][t]);
-                    if (lane == 0 && t < nrows)
-                        a.part[(((int64_t)ks * a.cap_g + r0 + t) * f + n0 + i) * 2 + g] = v;
+                    const float v = wave_sum(acc[i][g][t]);
+                    if (lane == 0) red[wid][i][g][t] = v;
                 }
         __syncthreads();
-        if (threadIdx.x == 0) {
-            __threadfence();
-            int old = atomicAdd(&a.counters[ai * NB + nb], 1);
-            int last = (old == KS - 1);
-            if (last) a.counters[ai * NB + nb] = 0;
-            sh_last = last;
-        }
-        __syncthreads();
-        if (sh_last) {
-            __threadfence();
-            const int tid = threadIdx.x;
-            if (tid < kGemvNeurons * nrows) {
-                const int n = nb * kGemvNeurons + (tid % kGemvNeurons);
-                const int rr = r0 + tid / kGemvNeurons;
-                float gs = 0.0f, us = 0.0f;
-                for (int s = 0; s < KS; ++s) {
-                    const float* p = a.part + (((int64_t)s * a.cap_g + rr) * f + n) * 2;
-                    gs += __builtin_nontemporal_load(p);
-                    us += __builtin_nontemporal_load(p + 1);
-                }
-                a.Hf[(int64_t)rr * f + n] = silu(gs) * us;
-            }
+        const int tid = threadIdx.x;
+        if (tid < NN * nrows) {
+            const int i = tid % NN, t = tid / NN;
+            const float gs = (red[0][i][0][t] + red[1][i][0][t]) + (red[2][i][0][t] + red[3][i][0][t]);
+            const float us = (red[0][i][1][t] + red[1][i][1][t]) + (red[2][i][1][t] + red[3][i][1][t]);
+            a.Hf[(int64_t)(r0 + t) * f + n0 + i] = silu(gs) * us;
         }
         __syncthreads();
     }
@@ -352,8 +343,6 @@ hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     a.off_sg = c->rl.off_sg;
     a.off_su = c->rl.off_su;
     a.off_sd = c->rl.off_sd;
-    a.part = c->gv_part;
-    a.counters = c->gv_counters;
     a.Hf = c->gv_H;
     a.Y = c->Y;
     a.cap_g = c->cap_gemv;

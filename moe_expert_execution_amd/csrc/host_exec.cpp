@@ -20,6 +20,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <mutex>
@@ -74,6 +75,18 @@ struct HostBranch {
         std::atomic<int> busy{0};
     } ring[kRing];
     uint64_t ring_next = 0;
+    // mailbox (pinned): [0] seq posted by the GPU, [8] done posted by the poller
+    bool use_mailbox = false;
+    uint64_t* mbox = nullptr;
+    uint64_t next_seq = 0;                   // last seq handed out (enqueuing thread)
+    std::atomic<uint64_t> processed{0};      // last seq the poller finished
+    struct Params {
+        int layer, T;
+    } params[kRing];
+    std::thread poller;
+    // counters (read after a device synchronisation)
+    std::atomic<uint64_t> c_bytes{0}, c_experts{0};
+    std::atomic<uint64_t> c_ns{0};
 };
 
 namespace {
@@ -231,13 +244,12 @@ void worker_main(HostBranch* hb, int idx, int cpu) {
     (void)idx;
 }
 
-// Runs on the HIP runtime's callback thread, in stream order.
-void host_fn(void* p) {
-    auto* call = static_cast<HostBranch::Call*>(p);
-    HostBranch* hb = call->hb;
-    const int T = call->T, k = hb->sh.top_k, d = hb->sh.d_model, E = hb->sh.experts;
+// One host-branch call: read the staged routes, run the host experts with the
+// worker pool, leave the partial sums in staging P.
+void run_call(HostBranch* hb, int layer, int T) {
+    const int k = hb->sh.top_k, d = hb->sh.d_model, E = hb->sh.experts;
     Job& jb = hb->job;
-    jb.layer = call->layer;
+    jb.layer = layer;
     jb.T = T;
     jb.experts.clear();
     jb.tok_off.clear();
@@ -271,6 +283,7 @@ void host_fn(void* p) {
     }
     jb.tok_off.push_back((int)jb.tok.size());
     if (!jb.experts.empty()) {
+        const auto t_start = std::chrono::steady_clock::now();
         for (int t = 0; t < T; ++t)
             if (has[t]) memset(hb->stg.P + (int64_t)t * d, 0, sizeof(float) * d);
         // fp32 activations of every token with host routes
@@ -289,8 +302,53 @@ void host_fn(void* p) {
         std::vector<float> rowbuf(2 * (size_t)std::max(hb->sh.d_model, hb->sh.d_ff) + 64);
         run_job(hb, hb->nthreads + 1, rowbuf);
         while (hb->finished.load(std::memory_order_acquire) < hb->nthreads) _mm_pause();
+        const auto ns = std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() -
+                                                                             t_start).count();
+        hb->c_ns.fetch_add((uint64_t)ns);
+        hb->c_experts.fetch_add(jb.experts.size());
+        hb->c_bytes.fetch_add(jb.experts.size() * (uint64_t)hb->rl.S);
     }
+}
+
+// Runs on the HIP runtime's callback thread, in stream order.
+void host_fn(void* p) {
+    auto* call = static_cast<HostBranch::Call*>(p);
+    run_call(call->hb, call->layer, call->T);
     call->busy.store(0, std::memory_order_release);
+}
+
+// Mailbox poller: waits for the GPU to post a sequence number, runs that call,
+// posts it as done.  Every posted number is answered, in order.
+void poller_main(HostBranch* hb, int cpu) {
+    if (cpu >= 0) {
+        cpu_set_t set;
+        CPU_ZERO(&set);
+        CPU_SET(cpu, &set);
+        pthread_setaffinity_np(pthread_self(), sizeof(set), &set);
+    }
+    volatile uint64_t* seq_word = hb->mbox;
+    uint64_t* done_word = hb->mbox + 8;
+    uint64_t last = 0;
+    int idle = 0;
+    while (!hb->stop.load(std::memory_order_relaxed)) {
+        const uint64_t s = __atomic_load_n(seq_word, __ATOMIC_ACQUIRE);
+        if (s == last) {
+            if (++idle < 200000) {
+                _mm_pause();
+            } else {
+                std::this_thread::sleep_for(std::chrono::microseconds(20));
+            }
+            continue;
+        }
+        idle = 0;
+        for (uint64_t n = last + 1; n <= s; ++n) {
+            const HostBranch::Params p = hb->params[n % kRing];
+            run_call(hb, p.layer, p.T);
+            __atomic_store_n(done_word, n, __ATOMIC_RELEASE);
+            hb->processed.store(n, std::memory_order_release);
+        }
+        last = s;
+    }
 }
 
 }  // namespace
@@ -313,6 +371,14 @@ HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const
     hb->stg.w = (float*)p;
     ok &= hipHostMalloc(&p, sizeof(float) * max_tokens * d, hipHostMallocDefault) == hipSuccess;
     hb->stg.P = (float*)p;
+    ok &= hipHostMalloc(&p, 128, hipHostMallocDefault) == hipSuccess;
+    hb->mbox = (uint64_t*)p;
+    if (hb->mbox) memset(hb->mbox, 0, 128);
+    // the kernels write and read the staging through these same addresses
+    for (void* hp : {(void*)hb->stg.x, (void*)hb->stg.routes, (void*)hb->stg.w, (void*)hb->stg.P, (void*)hb->mbox}) {
+        void* dp = nullptr;
+        ok &= hp && hipHostGetDevicePointer(&dp, hp, 0) == hipSuccess && dp == hp;
+    }
     if (!ok) {
         host_branch_destroy(hb);
         return nullptr;
@@ -335,7 +401,33 @@ HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const
         int cpu = cpus.empty() ? -1 : cpus[(i + 2) % cpus.size()];
         hb->workers.emplace_back(worker_main, hb, i, cpu);
     }
+    // signalling: a polled mailbox when the device can wait on a memory value
+    // (FTMOE_HOST_SIGNAL=callback forces stream host functions)
+    int dev = 0, can_wait = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&can_wait, hipDeviceAttributeCanUseStreamWaitValue, dev) != hipSuccess)
+        can_wait = 0;
+    const char* sig = getenv("FTMOE_HOST_SIGNAL");
+    hb->use_mailbox = can_wait && !(sig && strcmp(sig, "callback") == 0);
+    if (hb->use_mailbox) hb->poller = std::thread(poller_main, hb, cpus.empty() ? -1 : cpus[1 % cpus.size()]);
     return hb;
+}
+
+HostSignal host_branch_prepare(HostBranch* hb, int32_t layer, int32_t T) {
+    HostSignal s{};
+    s.mailbox = hb->use_mailbox;
+    if (!s.mailbox) return s;
+    const uint64_t n = ++hb->next_seq;
+    // the poller reads params[n % kRing] only after the GPU posted n; keep it
+    // from lapping an entry that is still unread
+    while (n - hb->processed.load(std::memory_order_acquire) >= (uint64_t)kRing) std::this_thread::yield();
+    hb->params[n % kRing].layer = layer;
+    hb->params[n % kRing].T = T;
+    std::atomic_thread_fence(std::memory_order_release);
+    s.seq = n;
+    s.seq_word = hb->mbox;
+    s.done_word = hb->mbox + 8;
+    return s;
 }
 
 void host_branch_destroy(HostBranch* hb) {
@@ -345,15 +437,24 @@ void host_branch_destroy(HostBranch* hb) {
         hb->stop.store(true);
     }
     hb->cv.notify_all();
+    if (hb->poller.joinable()) hb->poller.join();
     for (auto& t : hb->workers) t.join();
     if (hb->stg.x) (void)hipHostFree(hb->stg.x);
     if (hb->stg.routes) (void)hipHostFree(hb->stg.routes);
     if (hb->stg.w) (void)hipHostFree(hb->stg.w);
     if (hb->stg.P) (void)hipHostFree(hb->stg.P);
+    if (hb->mbox) (void)hipHostFree(hb->mbox);
     delete hb;
 }
 
 HostStaging host_branch_staging(HostBranch* hb) { return hb->stg; }
+
+void host_branch_counters(HostBranch* hb, uint64_t* bytes, double* seconds, uint64_t* experts) {
+    *bytes = hb->c_bytes.load();
+    *seconds = hb->c_ns.load() * 1e-9;
+    *experts = hb->c_experts.load();
+}
+
 
 int host_branch_threads(HostBranch* hb) { return hb->nthreads + 1; }
 

@@ -42,7 +42,39 @@ struct PlanArgs {
     int32_t* tile_row0;
     int32_t* chunk_counts;
     unsigned long long* work;   // [2]: active slots, rows (accumulated)
+    // host-branch staging (pinned, device-visible; null = none): the call's
+    // routes, weights and activations for the host workers
+    const float* w;
+    const uint16_t* x;
+    int32_t d;
+    int32_t* h_routes;
+    float* h_w;
+    uint16_t* h_x;
+    uint64_t* seq_word;      // mailbox: store seq here once staging is visible (null = none)
+    uint64_t seq;
 };
+
+// Post the call to the host branch's mailbox after the staging writes of the
+// whole workgroup (system-scope release).
+__device__ __forceinline__ void post_mailbox(const PlanArgs& a) {
+    if (a.seq_word && threadIdx.x == 0) {
+        __threadfence_system();
+        __hip_atomic_store(a.seq_word, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
+// Copy routes, weights and activations of the call into pinned host staging
+// (zero-copy writes over PCIe) with the whole workgroup / grid.
+__device__ __forceinline__ void stage_to_host(const PlanArgs& a, int tid, int nthr) {
+    for (int r = tid; r < a.R; r += nthr) {
+        a.h_routes[r] = a.routes[r];
+        a.h_w[r] = a.w[r];
+    }
+    const int nx = a.T * a.d / 8;   // 16-byte chunks (d % 128 == 0)
+    const uint4* xs = reinterpret_cast<const uint4*>(a.x);
+    uint4* xd = reinterpret_cast<uint4*>(a.h_x);
+    for (int i = tid; i < nx; i += nthr) xd[i] = xs[i];
+}
 
 // Slot of route r, or -1 when it is not a GPU route (host, invalid, duplicate).
 __device__ __forceinline__ int route_slot(const PlanArgs& a, int r) {
@@ -116,6 +148,11 @@ __global__ void __launch_bounds__(kPlanThreads) plan_small_kernel(PlanArgs a) {
     __shared__ uint32_t keys[kSmallPlanRoutes];
     __shared__ int wsum[kPlanThreads / 64];
     const int tid = threadIdx.x;
+    if (a.h_routes) {
+        stage_to_host(a, tid, kPlanThreads);
+        __syncthreads();
+        post_mailbox(a);
+    }
     int P = 1;
     while (P < a.R) P <<= 1;
 
@@ -199,6 +236,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_count_kernel(PlanArgs a) {
 // G threads share a key (each sums a contiguous range of chunks); keys are
 // processed in ascending passes of 1024 / G.
 __global__ void __launch_bounds__(kPlanThreads) plan_scan_kernel(PlanArgs a, int nchunks) {
+    post_mailbox(a);   // the staging kernel ran earlier on this stream
     __shared__ int part[kPlanThreads];
     __shared__ int kstart[kPlanThreads];
     __shared__ int kact[kPlanThreads];
@@ -264,6 +302,11 @@ __global__ void __launch_bounds__(kPlanThreads) plan_scan_kernel(PlanArgs a, int
     emit_tiles(a, run_active, wsum);
 }
 
+// Host staging for the chunked planner's calls.
+__global__ void __launch_bounds__(256) stage_kernel(PlanArgs a) {
+    stage_to_host(a, blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
+}
+
 // Kernel C: stable scatter.
 __global__ void __launch_bounds__(kPlanThreads) plan_scatter_kernel(PlanArgs a) {
     __shared__ unsigned long long mask[kLargeKeySpace];
@@ -297,8 +340,17 @@ __global__ void __launch_bounds__(kPlanThreads) plan_scatter_kernel(PlanArgs a) 
 }  // namespace
 
 hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, int work_counter,
+                       const float* w, const uint16_t* x, const HostStaging* stage, const HostSignal* sig,
                        hipStream_t st) {
     PlanArgs a;
+    a.seq_word = (sig && sig->mailbox) ? sig->seq_word : nullptr;
+    a.seq = sig ? sig->seq : 0;
+    a.w = w;
+    a.x = x;
+    a.d = c->sh.d_model;
+    a.h_routes = stage ? stage->routes : nullptr;
+    a.h_w = stage ? stage->w : nullptr;
+    a.h_x = stage ? stage->x : nullptr;
     a.routes = routes;
     a.k = c->sh.top_k;
     a.T = T;
@@ -323,6 +375,7 @@ hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base,
     } else {
         if (a.key_space > kLargeKeySpace) return hipErrorInvalidValue;
         int nchunks = (T + kChunkTokens - 1) / kChunkTokens;
+        if (stage) hipLaunchKernelGGL(stage_kernel, dim3(256), dim3(256), 0, st, a);
         hipLaunchKernelGGL(plan_count_kernel, dim3(nchunks), dim3(kPlanThreads), 0, st, a);
         hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a, nchunks);
         hipLaunchKernelGGL(plan_scatter_kernel, dim3(nchunks), dim3(kPlanThreads), 0, st, a);

@@ -3,6 +3,10 @@
 // expert); weights = softmax over the chosen k.  The router picks k of the
 // layer's E experts per token ("Making Large MoE Models Practical on a Single
 // Machine", section 1).
+//
+// Calls with T <= 16 use a file-scope device array for partial logits, shared
+// by every such call on the device: concurrent small-T calls on different
+// streams must be ordered by the caller.
 #include "common.h"
 
 namespace ftmoe {
@@ -122,11 +126,163 @@ __global__ void __launch_bounds__(kRouteThreads)
     }
 }
 
+// ---- small T (decode): the d-range is split over kRouteDS workgroups so the
+// router matrix streams through many CUs; partial logits go to a file-scope
+// device array and a second kernel adds them in a fixed order, then selects.
+constexpr int kRouteSmallT = 16;
+constexpr int kRouteDS = 32;
+__device__ double g_route_part[kRouteDS * kRouteSmallT * kRouteMaxE];
+
+template <int TT>
+__global__ void __launch_bounds__(kRouteThreads)
+    route_partial_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E) {
+    __shared__ double red[kRouteThreads][TT];
+    const int tid = threadIdx.x;
+    const int ds = blockIdx.x;
+    const int span = (d + kRouteDS - 1) / kRouteDS;
+    const int r0 = ds * span, r1 = (r0 + span) < d ? (r0 + span) : d;
+    const int G = kRouteThreads / E > 0 ? kRouteThreads / E : 1;
+    const int e = tid % E, g = tid / E;
+    const bool active = g < G && tid < G * E;
+    double acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = 0.0;
+    if (active) {
+#pragma unroll 4
+        for (int r = r0 + g; r < r1; r += G) {
+            const double wv = bf16_to_f64(wr[(int64_t)r * E + e]);
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+                if (t < T) acc[t] = fma(bf16_to_f64(x[(int64_t)t * d + r]), wv, acc[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) red[tid][t] = acc[t];
+    __syncthreads();
+    if (tid < E) {
+        for (int t = 0; t < T && t < TT; ++t) {
+            double s = 0.0;
+            for (int gg = 0; gg < G; ++gg) s += red[gg * E + tid][t];
+            g_route_part[((int64_t)ds * kRouteSmallT + t) * kRouteMaxE + tid] = s;
+        }
+    }
+}
+
+// One token, E % 8 == 0: each thread streams 16-byte pieces (8 experts) of
+// router rows; a workgroup covers d / kRouteDS rows.
+__global__ void __launch_bounds__(kRouteThreads)
+    route_partial_vec_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int d, int E) {
+    __shared__ double red[kRouteThreads][8];   // [row sub-group * ncg + column group][8 experts]
+    const int tid = threadIdx.x;
+    const int ds = blockIdx.x;
+    const int ncg = E / 8;                      // 16-byte column groups per row
+    const int rpi = kRouteThreads / ncg;        // rows per iteration
+    const int cg = tid % ncg, rs = tid / ncg;
+    const int span = (d + kRouteDS - 1) / kRouteDS;
+    const int r0 = ds * span, r1 = (r0 + span) < d ? (r0 + span) : d;
+    double acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+    if (rs < rpi) {
+#pragma unroll 2
+        for (int r = r0 + rs; r < r1; r += rpi) {
+            const uint4 wv = *reinterpret_cast<const uint4*>(wr + (int64_t)r * E + cg * 8);
+            const double xv = bf16_to_f64(x[r]);
+            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[2 * j] = fma(xv, (double)__uint_as_float(ww[j] << 16), acc[2 * j]);
+                acc[2 * j + 1] = fma(xv, (double)__uint_as_float(ww[j] & 0xFFFF0000u), acc[2 * j + 1]);
+            }
+        }
+        const int slot = rs * ncg + cg;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[slot][j] = acc[j];
+    }
+    __syncthreads();
+    if (tid < E) {
+        const int g = tid / 8, j = tid % 8;
+        double s = 0.0;
+        for (int q = 0; q < rpi; ++q) s += red[q * ncg + g][j];
+        g_route_part[((int64_t)ds * kRouteSmallT) * kRouteMaxE + tid] = s;
+    }
+}
+
+// one wave per token: z = sum of the kRouteDS partials (fixed order), top-k, softmax
+__global__ void __launch_bounds__(64) route_select_kernel(int T, int E, int k, int32_t* __restrict__ ids,
+                                                          float* __restrict__ w) {
+    const int t = blockIdx.x, lane = threadIdx.x;
+    if (t >= T) return;
+    double zl[kRouteMaxE / 64];
+    bool taken[kRouteMaxE / 64];
+#pragma unroll
+    for (int j = 0; j < kRouteMaxE / 64; ++j) {
+        const int ee = lane + 64 * j;
+        double z = -INFINITY;
+        if (ee < E) {
+            z = 0.0;
+            for (int ds = 0; ds < kRouteDS; ++ds) z += g_route_part[((int64_t)ds * kRouteSmallT + t) * kRouteMaxE + ee];
+        }
+        zl[j] = z;
+        taken[j] = ee >= E;
+    }
+    double zsel[kMaxTopK];
+    int esel[kMaxTopK];
+    for (int r = 0; r < k; ++r) {
+        double bz = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxE / 64; ++j) {
+            const int ee = lane + 64 * j;
+            if (!taken[j] && (zl[j] > bz || (zl[j] == bz && ee < be))) {
+                bz = zl[j];
+                be = ee;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const double oz = __shfl_xor(bz, off, 64);
+            const int oe = __shfl_xor(be, off, 64);
+            if (oz > bz || (oz == bz && oe < be)) {
+                bz = oz;
+                be = oe;
+            }
+        }
+        zsel[r] = bz;
+        esel[r] = be;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxE / 64; ++j)
+            if (lane + 64 * j == be) taken[j] = true;
+    }
+    if (lane == 0) {
+        double s = 0.0, ex[kMaxTopK];
+        for (int r = 0; r < k; ++r) {
+            ex[r] = exp(zsel[r] - zsel[0]);
+            s += ex[r];
+        }
+        for (int r = 0; r < k; ++r) {
+            ids[(int64_t)t * k + r] = esel[r];
+            w[(int64_t)t * k + r] = (float)(ex[r] / s);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int d, int E, int k, int32_t* ids, float* w,
                         hipStream_t st) {
     if (T <= 0) return hipSuccess;
+    if (T <= kRouteSmallT) {
+        if (T == 1 && E % 8 == 0)
+            hipLaunchKernelGGL(route_partial_vec_kernel, dim3(kRouteDS), dim3(kRouteThreads), 0, st, x, wr, d, E);
+        else if (T == 1)
+            hipLaunchKernelGGL(route_partial_kernel<1>, dim3(kRouteDS), dim3(kRouteThreads), 0, st, x, wr, T, d, E);
+        else
+            hipLaunchKernelGGL(route_partial_kernel<kRouteSmallT>, dim3(kRouteDS), dim3(kRouteThreads), 0, st, x, wr,
+                               T, d, E);
+        hipLaunchKernelGGL(route_select_kernel, dim3(T), dim3(64), 0, st, T, E, k, ids, w);
+        return hipGetLastError();
+    }
     int blocks = (T + kRouteTokens - 1) / kRouteTokens;
     hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(kRouteThreads), 0, st, x, wr, T, d, E, k, ids, w);
     return hipGetLastError();
