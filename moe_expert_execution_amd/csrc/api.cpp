@@ -102,18 +102,17 @@ void timing_destroy(Timing* t) {
     delete t;
 }
 
-int timing_begin(Timing* t, int cls, hipStream_t st) {
+TimedLaunch timing_launch(Timing* t, int cls) {
+    TimedLaunch tl;
+    if (!t) return tl;
     const int i = t->next;
     t->next = (t->next + 1) % Timing::kRing;
-    fold(t, i);     // the pair recorded kRing launches ago has long completed
+    fold(t, i);     // the pair used kRing launches ago has long completed
     t->cls[i] = cls;
-    (void)hipEventRecord(t->ev[i][0], st);
-    return i;
-}
-
-void timing_end(Timing* t, int i, hipStream_t st) {
-    (void)hipEventRecord(t->ev[i][1], st);
     t->live[i] = true;
+    tl.start = t->ev[i][0];
+    tl.stop = t->ev[i][1];
+    return tl;
 }
 
 void timing_read(Timing* t, uint64_t* launches, double* ms) {
@@ -186,9 +185,7 @@ hipError_t alloc_plan(ft_cache* c) {
 // Every later call on the cache flushes a pending fill before it can read a slot.
 ft_status flush_fill(ft_cache* c, hipStream_t st) {
     if (!c->fill_pending) return FT_OK;
-    const int ts = c->timing ? timing_begin(c->timing, FT_K_FILL, st) : -1;
-    FT_HIP(launch_fill(c, st));
-    if (c->timing) timing_end(c->timing, ts, st);
+    FT_HIP(launch_fill(c, st, timing_launch(c->timing, FT_K_FILL)));
     c->fill_pending = false;
     return FT_OK;
 }

@@ -1,5 +1,6 @@
 // Internal declarations shared by the ftmoe library sources (gfx950, HIP).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,9 +91,12 @@ void host_branch_counters(HostBranch* hb, uint64_t* bytes, double* seconds, uint
 struct Timing;
 Timing* timing_create();
 void timing_destroy(Timing* t);
-// Record the start event of a launch of class `cls`; returns the slot to close.
-int timing_begin(Timing* t, int cls, hipStream_t st);
-void timing_end(Timing* t, int slot, hipStream_t st);
+// Events that hipExtLaunchKernelGGL stamps at the start and end of one launch
+// of class `cls` (both null when `t` is null, i.e. timing is off).
+struct TimedLaunch {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+TimedLaunch timing_launch(Timing* t, int cls);
 void timing_read(Timing* t, uint64_t* launches, double* ms);   // synchronises on pending events
 
 // ---- the cache handle ---------------------------------------------------------
@@ -160,7 +164,7 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int d, int
                         float* w, hipStream_t st);
 hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, const ft_classify_out* out,
                            hipStream_t st);
-hipError_t launch_fill(ft_cache* c, hipStream_t st);
+hipError_t launch_fill(ft_cache* c, hipStream_t st, TimedLaunch tl = TimedLaunch());
 hipError_t launch_invalidate(ft_cache* c, int buf, hipStream_t st);
 hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t S, const int32_t* src_slots,
                                 int n, hipStream_t st);

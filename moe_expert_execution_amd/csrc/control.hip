@@ -392,9 +392,10 @@ hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, 
     return hipGetLastError();
 }
 
-hipError_t launch_fill(ft_cache* c, hipStream_t st) {
-    hipLaunchKernelGGL(fill_kernel, dim3(kFillBlocks), dim3(kFillThreads), 0, st, c->wl_counts, c->wl_slot,
-                       c->wl_src, c->bank_dev, c->pool, c->rl.S);
+hipError_t launch_fill(ft_cache* c, hipStream_t st, TimedLaunch tl) {
+    hipExtLaunchKernelGGL(fill_kernel, dim3(kFillBlocks), dim3(kFillThreads), 0, st, tl.start, tl.stop, 0,
+                          (const int32_t*)c->wl_counts, (const int32_t*)c->wl_slot, (const int32_t*)c->wl_src,
+                          c->bank_dev, c->pool, c->rl.S);
     return hipGetLastError();
 }
 

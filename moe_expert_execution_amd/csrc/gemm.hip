@@ -227,12 +227,12 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(GemmArgs a) {
 template <int FMT>
 hipError_t launch_fmt(const GemmArgs& a, int64_t max_tiles, Timing* tm, hipStream_t st) {
     const int64_t g1 = max_tiles * (a.f / 64), g2 = max_tiles * (a.d / kBN);
-    int ts = tm ? timing_begin(tm, FT_K_GEMM_GU, st) : -1;
-    hipLaunchKernelGGL((gemm_kernel<FMT, true>), dim3((unsigned)g1), dim3(kGemmThreads), 0, st, a);
-    if (tm) timing_end(tm, ts, st);
-    ts = tm ? timing_begin(tm, FT_K_GEMM_DOWN, st) : -1;
-    hipLaunchKernelGGL((gemm_kernel<FMT, false>), dim3((unsigned)g2), dim3(kGemmThreads), 0, st, a);
-    if (tm) timing_end(tm, ts, st);
+    TimedLaunch t1 = timing_launch(tm, FT_K_GEMM_GU);
+    hipExtLaunchKernelGGL((gemm_kernel<FMT, true>), dim3((unsigned)g1), dim3(kGemmThreads), 0, st, t1.start, t1.stop,
+                          0, a);
+    TimedLaunch t2 = timing_launch(tm, FT_K_GEMM_DOWN);
+    hipExtLaunchKernelGGL((gemm_kernel<FMT, false>), dim3((unsigned)g2), dim3(kGemmThreads), 0, st, t2.start,
+                          t2.stop, 0, a);
     return hipGetLastError();
 }
 

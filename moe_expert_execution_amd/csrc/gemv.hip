@@ -313,12 +313,12 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_down_kernel(GemvArgs a) {
 
 template <int FMT, int TG>
 hipError_t launch_fmt(const GemvArgs& a, Timing* tm, hipStream_t st) {
-    int ts = tm ? timing_begin(tm, FT_K_GEMV_GU, st) : -1;
-    hipLaunchKernelGGL((gemv_gateup_kernel<FMT, TG>), dim3(kGemvBlocks), dim3(kGemvThreads), 0, st, a);
-    if (tm) timing_end(tm, ts, st);
-    ts = tm ? timing_begin(tm, FT_K_GEMV_DOWN, st) : -1;
-    hipLaunchKernelGGL((gemv_down_kernel<FMT, TG>), dim3(kGemvBlocks), dim3(kGemvThreads), 0, st, a);
-    if (tm) timing_end(tm, ts, st);
+    TimedLaunch t1 = timing_launch(tm, FT_K_GEMV_GU);
+    hipExtLaunchKernelGGL((gemv_gateup_kernel<FMT, TG>), dim3(kGemvBlocks), dim3(kGemvThreads), 0, st, t1.start,
+                          t1.stop, 0, a);
+    TimedLaunch t2 = timing_launch(tm, FT_K_GEMV_DOWN);
+    hipExtLaunchKernelGGL((gemv_down_kernel<FMT, TG>), dim3(kGemvBlocks), dim3(kGemvThreads), 0, st, t2.start,
+                          t2.stop, 0, a);
     return hipGetLastError();
 }
 
