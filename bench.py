@@ -265,6 +265,7 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (kernel work)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -289,6 +290,9 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n}))
         return
 
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_bench(args)}), flush=True)
+        return
     dec, bank, cfg = decode_bench(args)
     cpu = None
     if not args.no_cpu_baseline:

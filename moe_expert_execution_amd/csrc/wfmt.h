@@ -15,6 +15,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // a 16-byte chunk held in registers
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -57,8 +58,9 @@ template <>
 struct WF<FT_FMT_FP8_B128> {
     static constexpr int EPC = 16;
     __device__ static int64_t row_bytes(int K) { return (int64_t)K; }
-    __device__ static void to_f32(const uint4 c, float* v) {
-        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    __device__ static void to_f32(const uint4 c, float* v) { to_f32(u32x4_t{c.x, c.y, c.z, c.w}, v); }
+    __device__ static void to_f32(const u32x4_t c, float* v) {
+        const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
@@ -77,7 +79,10 @@ struct WF<FT_FMT_MXFP4_B32> {
     __device__ static int64_t row_bytes(int K) { return (int64_t)K / 2; }
     // 32 codes, low nibble first, times `scale` (exact: a power of two)
     __device__ static void to_f32(const uint4 c, float scale, float* v) {
-        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+        to_f32(u32x4_t{c.x, c.y, c.z, c.w}, scale, v);
+    }
+    __device__ static void to_f32(const u32x4_t c, float scale, float* v) {
+        const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], scale, 0);
