@@ -152,7 +152,7 @@ void free_cache(ft_cache* c) {
     if (c->timing) timing_destroy(c->timing);
     void* bufs[] = {c->pool, c->slot_for_id, c->id_of_slot, c->stamp, c->clock, c->counters, c->errflag,
                     c->wl_counts, c->wl_slot, c->wl_src, c->plan.meta, c->plan.active_slot, c->plan.seg,
-                    c->plan.perm, c->plan.route_pos, c->plan.tile_active, c->plan.tile_row0,
+                    c->plan.perm, c->plan.route_pos, c->plan.tile_active, c->plan.tile_row0, c->plan.tile_first,
                     c->plan.chunk_counts, c->H, c->Y, c->gv_H};
     for (void* b : bufs)
         if (b) (void)hipFree(b);
@@ -175,6 +175,7 @@ hipError_t alloc_plan(ft_cache* c) {
     hipError_t e;
     if ((e = dalloc(&c->plan.tile_active, c->plan.max_tiles))) return e;
     if ((e = dalloc(&c->plan.tile_row0, c->plan.max_tiles))) return e;
+    if ((e = dalloc(&c->plan.tile_first, cap + 1))) return e;
     if ((e = dalloc(&c->plan.chunk_counts, chunks * std::min<int64_t>(keyspace, 8192)))) return e;
     return hipSuccess;
 }

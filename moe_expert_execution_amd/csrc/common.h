@@ -108,6 +108,7 @@ struct PlanBuffers {
     int32_t* route_pos;     // [cap]: sorted row of each route, -1 if not on the GPU
     int32_t* tile_active;   // [max tiles]
     int32_t* tile_row0;     // [max tiles]
+    int32_t* tile_first;    // [cap + 1]: first tile of each active slot (then the tile count)
     int32_t* chunk_counts;  // [chunks x keyspace] (large planner)
     int64_t max_tiles;
 };

@@ -32,6 +32,7 @@ struct GemmArgs {
     const int32_t* perm;
     const int32_t* tile_active;
     const int32_t* tile_row0;
+    const int32_t* tile_first;
     const uint8_t* pool;
     int64_t S;
     int64_t off_gate, off_up, off_down, off_sg, off_su, off_sd;
@@ -129,8 +130,9 @@ __device__ __forceinline__ void gemm_lstore(uint16_t* As, uint16_t* Bs, int tid,
 // (gate0, gate1, up0, up1), so SwiGLU pairs fragment j with j + 2 in-lane.
 // Down: wave column wn owns output columns [128 wn, 128 wn + 128).
 // Workgroups are renumbered so that each XCD (dispatch round-robin over 8)
-// receives a contiguous range of tiles: an expert's A and B tiles then meet in
-// one XCD's L2.
+// receives a contiguous range of blocks, ordered by slot, then N-tile, then
+// M-tile: all blocks of an expert run together in one XCD, where its A rows
+// and B tiles are read from HBM about once and then hit that XCD's L2.
 template <int FMT, bool GU>
 __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLDK];
@@ -144,8 +146,13 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
     if (b >= V) return;
     const int q8 = V >> 3, r8 = V & 7, x8 = b & 7;
     const int lb = x8 * q8 + (x8 < r8 ? x8 : r8) + (b >> 3);
-    const int tile = lb / NT, nt = lb - (lb / NT) * NT;
-    const int ai = a.tile_active[tile];
+    // within one slot's blocks [t0 NT, (t0 + mt) NT): N-tile major, M-tile minor,
+    // so the M-tiles sharing a B tile run side by side
+    const int ai = a.tile_active[lb / NT];
+    const int t0 = a.tile_first[ai], mt = a.tile_first[ai + 1] - t0;
+    const int local = lb - t0 * NT;
+    const int nt = local / mt;
+    const int tile = t0 + (local - nt * mt);
     const int row0 = a.tile_row0[tile];
     const int seg_end = a.seg[ai + 1];
     const int slot = a.active_slot[ai];
@@ -297,6 +304,7 @@ hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     a.perm = c->plan.perm;
     a.tile_active = c->plan.tile_active;
     a.tile_row0 = c->plan.tile_row0;
+    a.tile_first = c->plan.tile_first;
     a.pool = c->pool;
     a.S = c->rl.S;
     a.off_gate = c->rl.off_gate;

@@ -40,6 +40,7 @@ struct PlanArgs {
     int32_t* route_pos;
     int32_t* tile_active;
     int32_t* tile_row0;
+    int32_t* tile_first;
     int32_t* chunk_counts;
     unsigned long long* work;   // [2]: active slots, rows (accumulated)
     // host-branch staging (pinned, device-visible; null = none): the call's
@@ -134,13 +135,17 @@ __device__ void emit_tiles(const PlanArgs& a, int n_active, int* wsum) {
         }
         int tot;
         int off = block_excl_scan(nt, wsum, &tot) + total_tiles;
+        if (i < n_active) a.tile_first[i] = off;
         for (int j = 0; j < nt; ++j) {
             a.tile_active[off + j] = i;
             a.tile_row0[off + j] = r0 + j * a.bm;
         }
         total_tiles += tot;
     }
-    if (threadIdx.x == 0) a.meta[1] = total_tiles;
+    if (threadIdx.x == 0) {
+        a.meta[1] = total_tiles;
+        a.tile_first[n_active] = total_tiles;
+    }
 }
 
 // ---- one-workgroup planner (R <= 1024) ------------------------------------------
@@ -368,6 +373,7 @@ hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base,
     a.route_pos = c->plan.route_pos;
     a.tile_active = c->plan.tile_active;
     a.tile_row0 = c->plan.tile_row0;
+    a.tile_first = c->plan.tile_first;
     a.chunk_counts = c->plan.chunk_counts;
     a.work = c->counters + work_counter;
     if (a.R <= kSmallPlanRoutes) {
