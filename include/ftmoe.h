@@ -48,7 +48,8 @@ enum {
     FT_FMT_MXFP4_B32 = 2     /* e2m1 codes, one e8m0 scale per 32 along K        */
 };
 
-/* Layer geometry.  d_model and d_ff must be multiples of 128. */
+/* Layer geometry.  d_model and d_ff must be multiples of 128, with
+ * d_model <= 32768 and d_ff <= 8192. */
 typedef struct {
     int32_t layers;          /* L: MoE layers held by the host bank              */
     int32_t experts;         /* E: routed experts per layer (<= 4096)            */
@@ -143,7 +144,7 @@ typedef struct {
  * Errors: FT_ERR_ARG (shape, null, N), FT_ERR_NOMEM, FT_ERR_HIP.
  * Synchronises the current device.
  *
- * Record layout (S bytes), every matrix [rows x K] with K contiguous:
+ * Record layout (S bytes), matrices [rows x K] in this order:
  *   BF16       WgT [f x d] | WuT [f x d] | WdT [d x f]                  (bf16)
  *   FP8_B128   codes WgT | WuT | WdT (u8 e4m3fn), then fp32 scales
  *              sg [f/128 x d/128] | su [f/128 x d/128] | sd [d/128 x f/128]
@@ -151,6 +152,14 @@ typedef struct {
  *              (two e2m1 per byte, low nibble = even k), then e8m0 scales
  *              sg [f x d/32] | su [f x d/32] | sd [d x f/32]
  * where FFN(x) = (silu(x WgT^T) * (x WuT^T)) WdT^T.
+ * Panel order: every code matrix and every e8m0 scale matrix is stored in
+ * 32-row panels, panel p (rows 32p .. 32p+31) one contiguous block of
+ * 32 * (row bytes); inside it, unit c of row r — 16 bytes of codes (8 bf16,
+ * 16 e4m3 or 32 e2m1 values along K), or one e8m0 byte — is at unit index
+ * (c / 2) * 64 + (c % 2) * 32 + (r % 32).  So 64 lanes reading 16 bytes each at
+ * consecutive addresses receive one 32-row x 2-unit tile, the operand layout
+ * of a 32x32 matrix-core step, and a streaming reader sees 1 KiB runs.  The
+ * fp8 block scales are row-major.  d and f must be multiples of 128.
  * ------------------------------------------------------------------------- */
 ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, const void* host_bank,
                           int64_t num_slots, int32_t max_tokens, ft_cache** out);

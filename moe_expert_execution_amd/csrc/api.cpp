@@ -26,7 +26,7 @@ void clear_error() { g_err[0] = 0; }
 
 bool record_layout(const ft_shape& s, RecordLayout* o) {
     const int64_t d = s.d_model, f = s.d_ff, fd = d * f;
-    if (d <= 0 || f <= 0 || d % 128 || f % 128) return false;
+    if (d <= 0 || f <= 0 || d % 128 || f % 128 || d > 32768 || f > 8192) return false;
     switch (s.fmt) {
         case FT_FMT_BF16:
             o->off_gate = 0;
@@ -153,7 +153,7 @@ void free_cache(ft_cache* c) {
     void* bufs[] = {c->pool, c->slot_for_id, c->id_of_slot, c->stamp, c->clock, c->counters, c->errflag,
                     c->wl_counts, c->wl_slot, c->wl_src, c->plan.meta, c->plan.active_slot, c->plan.seg,
                     c->plan.perm, c->plan.route_pos, c->plan.tile_active, c->plan.tile_row0, c->plan.tile_first,
-                    c->plan.chunk_counts, c->H, c->Y, c->gv_H};
+                    c->plan.chunk_counts, c->H, c->Y, c->gv_part};
     for (void* b : bufs)
         if (b) (void)hipFree(b);
     hipEvent_t evs[] = {c->ev_ctrl, c->ev_fwd, c->ev_host, c->ev_xlast, c->ev_fence,
@@ -316,7 +316,8 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     CK(dalloc(&c->H, cap * f));
     CK(dalloc(&c->Y, cap * d));
     c->cap_gemv = std::min<int32_t>(max_tokens, kGemvMaxTokens) * shape->top_k;
-    CK(dalloc(&c->gv_H, (int64_t)c->cap_gemv * f));
+    c->gv_kq = gemv_kparts(*shape);
+    CK(dalloc(&c->gv_part, 2ll * c->gv_kq * c->cap_gemv * f));
     CK(hipMemset(c->slot_for_id, 0xFF, sizeof(int32_t) * L * E));
     CK(hipMemset(c->id_of_slot, 0xFF, sizeof(int32_t) * c->N));
     CK(hipMemset(c->stamp, 0, sizeof(uint64_t) * c->N));

@@ -142,7 +142,8 @@ struct ft_cache {
     uint16_t* H;               // [cap x f] bf16 (GEMM path)
     float* Y;                  // [cap x d] fp32
     int32_t cap_gemv;          // rows served by the GEMV path
-    float* gv_H;               // [cap_gemv x f] fp32 (GEMV path)
+    int32_t gv_kq;             // K-parts of the gate/up GEMV
+    float* gv_part;            // [2 x gv_kq x cap_gemv x f] fp32 K-part sums of g and u (GEMV path)
     // streams and events
     hipStream_t xfer;          // transfer stream (fills, full-layer loads)
     hipStream_t hstream;       // host-branch copies and host function
@@ -179,6 +180,7 @@ hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base,
                        const float* w, const uint16_t* x, const HostStaging* stage, const HostSignal* sig,
                        hipStream_t st);
 hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
+int gemv_kparts(const ft_shape& s);
 hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 // P: the host branch's partial sums [T x d] in pinned host memory (null when
 // the call has no host branch).

@@ -4,13 +4,20 @@
 // Gate/up: C[rows x 2*128] = X[rows x d] * [WgT; WuT]^T for 128 neurons at a
 // time, the gate and up halves landing in the same lanes, so the epilogue
 // writes h = silu(g) * u (bf16) without a shuffle.  Down: Y[rows x 256 cols] =
-// H[rows x f] * WdT^T in fp32.  Both operands are K-contiguous and staged
-// through LDS (one buffer, next tile prefetched into registers during the MFMA
-// loop); block-FP8 and MXFP4 weights are dequantised to bf16 as they are
-// written to LDS, so every format issues v_mfma_f32_32x32x16_bf16.
-// The expert FFN with its gate/up and down projections read from one slot
-// record follows "The Expert Cache That Follows the Router", section "One
-// logical expert, two physical levels of memory".
+// H[rows x f] * WdT^T in fp32.
+//
+// Weights are panel-ordered in the slot record: one 16-byte load per lane at
+// consecutive addresses delivers a 32-column x (two 16-byte chunk columns)
+// operand tile, which is exactly the B operand layout of
+// v_mfma_f32_32x32x16_bf16 (lane l: column l % 32, chunk column l / 32).  So
+// the weights go from memory straight into registers — no LDS staging, no
+// shuffles — one K-step ahead of their use; only the activation tile (shared
+// by the four waves) is staged through double-buffered LDS, one barrier per
+// K-step.  Block-FP8 and MXFP4 weights are converted to bf16 in registers
+// right before their MFMA, so every format issues the bf16 MFMA.  The expert
+// FFN with its gate/up and down projections read from one slot record follows
+// "The Expert Cache That Follows the Router", section "One logical expert,
+// two physical levels of memory".
 #include "wfmt.h"
 
 namespace ftmoe {
@@ -42,104 +49,63 @@ namespace {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// B loader: a thread owns CPT 16-byte code chunks of the B tile per K-step.
+// Per format: lane blocks (1 KiB panel runs) per K-step, and where the lane's
+// 8 bf16 of MFMA step ks sit inside the 64-wide K-step (the A side must read
+// the same K positions).
 template <int FMT>
-struct BLoad {
-    static constexpr int EPC = WF<FMT>::EPC;
-    static constexpr int CPR = kBK / EPC;                  // chunks per tile row
-    static constexpr int CPT = kBN * CPR / kGemmThreads;   // chunks per thread
+struct Frag {
+    static constexpr int LBK = 64 / (2 * WF<FMT>::EPC);    // lane blocks per K-step: 4, 2, 1
+    __device__ static int a_koff(int ks, int g) {
+        if constexpr (FMT == FT_FMT_BF16) return ks * 16 + g * 8;
+        else if constexpr (FMT == FT_FMT_FP8_B128) return (ks >> 1) * 32 + g * 16 + (ks & 1) * 8;
+        else return g * 32 + ks * 8;
+    }
 };
 
-// Global loads of K-step kt into registers: 4 A chunks and CPT B chunks (with
-// their block scales for FP8 / MXFP4).
-template <int FMT, bool GU>
-__device__ __forceinline__ void gemm_gload(const GemmArgs& a, const uint8_t* rec, int K, int nt, int tid, int kt,
-                                           const uint16_t* arow0, const uint16_t* arow1, const uint16_t* arow2,
-                                           const uint16_t* arow3, int akc, const uint32_t (&boff)[BLoad<FMT>::CPT],
-                                           u32x4_t& ra0, u32x4_t& ra1, u32x4_t& ra2, u32x4_t& ra3,
-                                           u32x4_t (&rb)[BLoad<FMT>::CPT], float (&rs)[BLoad<FMT>::CPT]) {
-    using BL = BLoad<FMT>;
-    const int kb = kt * kBK;
-    ra0 = *reinterpret_cast<const u32x4_t*>(arow0 + kb + akc);
-    ra1 = *reinterpret_cast<const u32x4_t*>(arow1 + kb + akc);
-    ra2 = *reinterpret_cast<const u32x4_t*>(arow2 + kb + akc);
-    ra3 = *reinterpret_cast<const u32x4_t*>(arow3 + kb + akc);
-#pragma unroll
-    for (int i = 0; i < BL::CPT; ++i) {
-        const int q = tid + kGemmThreads * i;
-        const int kk = kb + (q % BL::CPR) * BL::EPC;
-        rb[i] = *reinterpret_cast<const u32x4_t*>(rec + boff[i] + WF<FMT>::row_bytes(kk));
-        if constexpr (FMT != FT_FMT_BF16) {
-            const int br = q / BL::CPR;
-            const bool up = GU && br >= kBN / 2;
-            const int n = GU ? nt * (kBN / 2) + (up ? br - kBN / 2 : br) : nt * kBN + br;
-            const int64_t so = GU ? (up ? a.off_su : a.off_sg) : a.off_sd;
-            if constexpr (FMT == FT_FMT_FP8_B128)
-                rs[i] = reinterpret_cast<const float*>(rec + so)[(n >> 7) * (K >> 7) + (kk >> 7)];
-            else
-                rs[i] = e8m0_to_f32(rec[so + (int64_t)n * (K >> 5) + (kk >> 5)]);
-        } else {
-            rs[i] = 1.0f;
-        }
-    }
-}
-
-// One K-step's registers into the LDS tiles (B dequantised to bf16).
+// B operand of MFMA step ks from the K-step's lane-block registers.
 template <int FMT>
-__device__ __forceinline__ void gemm_lstore(uint16_t* As, uint16_t* Bs, int tid, int r0, int akc, const u32x4_t& ra0,
-                                            const u32x4_t& ra1, const u32x4_t& ra2, const u32x4_t& ra3,
-                                            const u32x4_t (&rb)[BLoad<FMT>::CPT], const float (&rs)[BLoad<FMT>::CPT]) {
-    using BL = BLoad<FMT>;
-    *reinterpret_cast<u32x4_t*>(&As[(r0)*kLDK + akc]) = ra0;
-    *reinterpret_cast<u32x4_t*>(&As[(r0 + 32) * kLDK + akc]) = ra1;
-    *reinterpret_cast<u32x4_t*>(&As[(r0 + 64) * kLDK + akc]) = ra2;
-    *reinterpret_cast<u32x4_t*>(&As[(r0 + 96) * kLDK + akc]) = ra3;
-#pragma unroll
-    for (int i = 0; i < BL::CPT; ++i) {
-        const int q = tid + kGemmThreads * i;
-        uint16_t* dst = &Bs[(q / BL::CPR) * kLDK + (q % BL::CPR) * BL::EPC];
-        if constexpr (FMT == FT_FMT_BF16) {
-            *reinterpret_cast<u32x4_t*>(dst) = rb[i];
-        } else if constexpr (FMT == FT_FMT_FP8_B128) {
-            float v[16];
-            WF<FMT>::to_f32(rb[i], v);
-            uint32_t p[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                p[j] = (uint32_t)f32_to_bf16_rne(v[2 * j] * rs[i]) |
-                       ((uint32_t)f32_to_bf16_rne(v[2 * j + 1] * rs[i]) << 16);
-            reinterpret_cast<u32x4_t*>(dst)[0] = u32x4_t{p[0], p[1], p[2], p[3]};
-            reinterpret_cast<u32x4_t*>(dst)[1] = u32x4_t{p[4], p[5], p[6], p[7]};
-        } else {
-            float v[32];
-            WF<FMT>::to_f32(rb[i], rs[i], v);
-            uint32_t p[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) p[j] = pack_bf16_trunc(v[2 * j], v[2 * j + 1]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                reinterpret_cast<u32x4_t*>(dst)[j] = u32x4_t{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
-        }
+__device__ __forceinline__ bf16x8_t b_frag(const u32x4_t (&r)[Frag<FMT>::LBK], int ks, float scale) {
+    if constexpr (FMT == FT_FMT_BF16) {
+        return __builtin_bit_cast(bf16x8_t, r[ks]);
+    } else if constexpr (FMT == FT_FMT_FP8_B128) {
+        const u32x4_t w = r[ks >> 1];
+        const uint32_t w0 = (ks & 1) ? w[2] : w[0];
+        const uint32_t w1 = (ks & 1) ? w[3] : w[1];
+        const f32x2_t p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+        const f32x2_t p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+        const f32x2_t p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+        const f32x2_t p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+        const bf16x2_t q0 = __builtin_convertvector(p0 * scale, bf16x2_t);
+        const bf16x2_t q1 = __builtin_convertvector(p1 * scale, bf16x2_t);
+        const bf16x2_t q2 = __builtin_convertvector(p2 * scale, bf16x2_t);
+        const bf16x2_t q3 = __builtin_convertvector(p3 * scale, bf16x2_t);
+        return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+    } else {
+        const uint32_t w = r[0][ks];
+        const bf16x2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+        const bf16x2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+        const bf16x2_t q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+        const bf16x2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+        return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
     }
 }
 
-// Tile (kBM rows of one slot) x (kBN columns) per workgroup; 4 waves in 2 x 2,
-// each computing 64 x 128 with 2 x 4 v_mfma_f32_32x32x16_bf16 accumulators.
-// Gate/up: the kBN columns are 128 gate and the same 128 up neurons; wave
-// column wn owns neurons [64 wn, 64 wn + 64) of both, as N-fragments
-// (gate0, gate1, up0, up1), so SwiGLU pairs fragment j with j + 2 in-lane.
-// Down: wave column wn owns output columns [128 wn, 128 wn + 128).
+// Tile (kBM rows of one slot) x (kBN columns) per workgroup; 4 waves side by
+// side along N, each computing 128 x 64 with 4 x 2 v_mfma_f32_32x32x16_bf16
+// accumulators.  Gate/up: the kBN columns are 128 gate and the same 128 up
+// neurons; wave w owns neurons [32 w, 32 w + 32) of both (B panel 0 gate,
+// panel 1 up), so SwiGLU pairs accumulator 0 with 1 in-lane.  Down: wave w
+// owns output columns [64 w, 64 w + 64), two panels.
 // Workgroups are renumbered so that each XCD (dispatch round-robin over 8)
 // receives a contiguous range of blocks, ordered by slot, then N-tile, then
 // M-tile: all blocks of an expert run together in one XCD, where its A rows
-// and B tiles are read from HBM about once and then hit that XCD's L2.
+// and weight panels are read from HBM about once and then hit that XCD's L2.
 template <int FMT, bool GU>
 __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLDK];
-    using BL = BLoad<FMT>;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid >> 1, wn = wid & 1;
+    using FR = Frag<FMT>;
+    constexpr int LBK = FR::LBK;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLDK];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
     const int NT = GU ? a.f / (kBN / 2) : a.d / kBN;
     const int V = a.meta[1] * NT;                 // valid workgroups
     const int b = blockIdx.x;
@@ -147,7 +113,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
     const int q8 = V >> 3, r8 = V & 7, x8 = b & 7;
     const int lb = x8 * q8 + (x8 < r8 ? x8 : r8) + (b >> 3);
     // within one slot's blocks [t0 NT, (t0 + mt) NT): N-tile major, M-tile minor,
-    // so the M-tiles sharing a B tile run side by side
+    // so the M-tiles sharing a weight panel run side by side
     const int ai = a.tile_active[lb / NT];
     const int t0 = a.tile_first[ai], mt = a.tile_first[ai + 1] - t0;
     const int local = lb - t0 * NT;
@@ -161,118 +127,165 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
     const int K = GU ? a.d : a.f;
     const uint8_t* rec = a.pool + (int64_t)slot * a.S;
     const int64_t rowb = WF<FMT>::row_bytes(K);
+    const int64_t panel_bytes = 32 * rowb;
 
-    // A: 4 chunks of 8 bf16 per thread per K-step (row q >> 3, chunk q & 7)
-    const uint16_t* arow0;
-    const uint16_t* arow1;
-    const uint16_t* arow2;
-    const uint16_t* arow3;
-    {
-        // rows past the tile's end repeat its last row: their outputs are never stored
-        const uint16_t* ap[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int r = (tid + kGemmThreads * i) >> 3;
-            r = r < rows_valid ? r : rows_valid - 1;
-            const int p = row0 + r;
-            ap[i] = GU ? a.x + (int64_t)(a.perm[p] / a.k) * a.d : a.Hin + (int64_t)p * a.f;
-        }
-        arow0 = ap[0];
-        arow1 = ap[1];
-        arow2 = ap[2];
-        arow3 = ap[3];
+    // this wave's two weight panels (+ lane offset); their scale locations
+    const uint8_t* bp[2];
+    int64_t soff[2];
+    int pn[2];
+    if (GU) {
+        pn[0] = pn[1] = nt * 4 + w;
+        bp[0] = rec + a.off_gate + pn[0] * panel_bytes + lane * 16;
+        bp[1] = rec + a.off_up + pn[1] * panel_bytes + lane * 16;
+        soff[0] = a.off_sg;
+        soff[1] = a.off_su;
+    } else {
+        pn[0] = nt * 8 + 2 * w;
+        pn[1] = pn[0] + 1;
+        bp[0] = rec + a.off_down + pn[0] * panel_bytes + lane * 16;
+        bp[1] = rec + a.off_down + pn[1] * panel_bytes + lane * 16;
+        soff[0] = soff[1] = a.off_sd;
     }
-    const int akc = (tid & 7) * 8;
-    // B: chunk i of this thread is tile row (tid + 256 i) / CPR; its record
-    // offset fits 32 bits (a record is at most a few tens of MB)
-    uint32_t boff[BL::CPT];
-#pragma unroll
-    for (int i = 0; i < BL::CPT; ++i) {
-        const int br = (tid + kGemmThreads * i) / BL::CPR;
-        if (GU) {
-            const bool up = br >= kBN / 2;
-            const int n = nt * (kBN / 2) + (up ? br - kBN / 2 : br);
-            boff[i] = (uint32_t)((up ? a.off_up : a.off_gate) + (int64_t)n * rowb);
+    // per-K-step weight scale of panel i: FP8 — the 128 x 128 block's fp32
+    // (uniform over the panel); MXFP4 — the lane's e8m0 byte for its chunk
+    auto scale_of = [&](int i, int kt) -> float {
+        if constexpr (FMT == FT_FMT_FP8_B128) {
+            return reinterpret_cast<const float*>(rec + soff[i])[(pn[i] >> 2) * (K >> 7) + (kt >> 1)];
+        } else if constexpr (FMT == FT_FMT_MXFP4_B32) {
+            return e8m0_to_f32(rec[soff[i] + (int64_t)pn[i] * K + kt * 64 + lane]);
         } else {
-            boff[i] = (uint32_t)(a.off_down + (int64_t)(nt * kBN + br) * rowb);
+            return 1.0f;
         }
-    }
+    };
 
-    f32x16_t acc[2][4];
+    // A: 4 chunks of 8 bf16 per thread per K-step (row (tid >> 3) + 32 i, chunk tid & 7)
+    const uint16_t* ap[4];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int i = 0; i < 4; ++i) {
+        // rows past the tile's end repeat its last row: their outputs are never stored
+        int r = (tid >> 3) + 32 * i;
+        r = r < rows_valid ? r : rows_valid - 1;
+        const int p = row0 + r;
+        ap[i] = (GU ? a.x + (int64_t)(a.perm[p] / a.k) * a.d : a.Hin + (int64_t)p * a.f) + (tid & 7) * 8;
+    }
+    const int a_st = (tid >> 3) * kLDK + (tid & 7) * 8;    // this thread's LDS store offset (row i adds 32 kLDK)
+
+    f32x16_t acc[4][2];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-#define FT_BBASE(ni) (GU ? (((ni) >> 1) * (kBN / 2) + 64 * wn + 32 * ((ni) & 1)) : (128 * wn + 32 * (ni)))
-
     const int KT = K / kBK;
-    const int r0 = tid >> 3;
-
+    u32x4_t br[2][LBK];
+    float bs[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < LBK; ++j) br[i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)j * 1024);
+        bs[i] = scale_of(i, 0);
+    }
     {
-        u32x4_t ra0, ra1, ra2, ra3, rb[BL::CPT];
-        float rs[BL::CPT];
-        gemm_gload<FMT, GU>(a, rec, K, nt, tid, 0, arow0, arow1, arow2, arow3, akc, boff, ra0, ra1, ra2, ra3, rb, rs);
-        gemm_lstore<FMT>(As, Bs, tid, r0, akc, ra0, ra1, ra2, ra3, rb, rs);
+        u32x4_t ra[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(ap[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(&As[0][a_st + 32 * i * kLDK]) = ra[i];
     }
     __syncthreads();
+
+    // A operand of MFMA step ks for the four row blocks, from LDS buffer Ab
+    auto read_a = [&](bf16x8_t (&af)[4], const uint16_t* Ab, int ks) {
+        const int ko = FR::a_koff(ks, g);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            af[mi] = *reinterpret_cast<const bf16x8_t*>(&Ab[(mi * 32 + (lane & 31)) * kLDK + ko]);
+    };
+    bf16x8_t af[2][4];
+    read_a(af[0], As[0], 0);
+
+    // Instruction order is pinned with scheduling barriers: the compiler
+    // would otherwise sink every next-K-step load below the last MFMA.
     for (int kt = 0; kt < KT; ++kt) {
         const bool more = kt + 1 < KT;
-        u32x4_t ra0, ra1, ra2, ra3, rb[BL::CPT];
-        float rs[BL::CPT];
-        if (more)
-            gemm_gload<FMT, GU>(a, rec, K, nt, tid, kt + 1, arow0, arow1, arow2, arow3, akc, boff, ra0, ra1, ra2,
-                                ra3, rb, rs);
+        // next K-step (the last step reloads itself: loads stay unconditional,
+        // so each refill lands in the registers its consumer reads)
+        const int kn = more ? kt + 1 : kt;
+        const uint16_t* Ab = As[kt & 1];
+        u32x4_t ra[4];
 #pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            const int kof = ks * 16 + (lane >> 5) * 8;
-            bf16x8_t af[2], bfr[4];
+        for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(ap[i] + kn * kBK);
+        float bs_next[2];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[(wm * 64 + mi * 32 + (lane & 31)) * kLDK + kof]);
+        for (int i = 0; i < 2; ++i) bs_next[i] = scale_of(i, kn);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                bfr[ni] = *reinterpret_cast<const bf16x8_t*>(&Bs[(FT_BBASE(ni) + (lane & 31)) * kLDK + kof]);
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks < 3) read_a(af[(ks + 1) & 1], Ab, ks + 1);
+            const bf16x8_t b0 = b_frag<FMT>(br[0], ks, bs[0]);
+            const bf16x8_t b1 = b_frag<FMT>(br[1], ks, bs[1]);
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < 4; ++mi) {
+                acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], b0, acc[mi][0], 0, 0, 0);
+                acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], b1, acc[mi][1], 0, 0, 0);
+            }
+            // the lane block this step consumed last is refilled for the next K-step
+            constexpr int kDone = 4 / LBK;                  // MFMA steps per lane block
+            if ((ks % kDone) == kDone - 1) {
+                const int j = ks / kDone;
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+                for (int i = 0; i < 2; ++i)
+                    br[i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(kn * LBK + j) * 1024);
+            }
+            // order inside the step: the next step's LDS reads interleaved with
+            // the first MFMAs, then the rest, then the refill loads
+            if (ks < 3) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);           // global loads
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bs[0] = bs_next[0];
+        bs[1] = bs_next[1];
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(&As[(kt + 1) & 1][a_st + 32 * i * kLDK]) = ra[i];
         }
         __syncthreads();
-        if (more) {
-            gemm_lstore<FMT>(As, Bs, tid, r0, akc, ra0, ra1, ra2, ra3, rb, rs);
-            __syncthreads();
-        }
+        read_a(af[0], As[(kt + 1) & 1], 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // epilogue
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int r = wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int r = mi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
             if (r < rows_valid) {
                 const int64_t p = row0 + r;
                 if (GU) {
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int n = nt * (kBN / 2) + 64 * wn + 32 * j + (lane & 31);
-                        a.Hout[p * a.f + n] = f32_to_bf16_rne(silu(acc[mi][j][v]) * acc[mi][j + 2][v]);
-                    }
+                    const int n = nt * (kBN / 2) + 32 * w + (lane & 31);
+                    a.Hout[p * a.f + n] = f32_to_bf16_rne(silu(acc[mi][0][v]) * acc[mi][1][v]);
                 } else {
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const int c = nt * kBN + FT_BBASE(ni) + (lane & 31);
+                    for (int ni = 0; ni < 2; ++ni) {
+                        const int c = nt * kBN + 64 * w + 32 * ni + (lane & 31);
                         a.Y[p * a.d + c] = acc[mi][ni][v];
                     }
                 }
             }
         }
     }
-#undef FT_BBASE
 }
 
 template <int FMT>

@@ -1,26 +1,33 @@
-// Decode expert FFN: bandwidth-bound split-K GEMVs over the active slots.
+// Decode expert FFN: bandwidth-bound GEMVs over the active slots.
 //
-// Each active slot serves a few token rows (decode: usually one).  Gate/up:
-// every workgroup item is (slot, 8 neurons): the 16 gate and up rows are read
-// with coalesced 16-byte loads, K split over the four waves (each lane one
-// 16-byte chunk of every row per step, so 16 loads are in flight per lane);
-// wave sums and then the four K-quarters are added in a fixed order inside the
-// workgroup — no cross-workgroup reduction, no device-scope fence — and SwiGLU,
-// h = silu(g) * u, is written to fp32 H.  Work items are counted from the
-// device-side number of active slots, so one fixed grid serves any hit/fill
-// mix.  Down: (slot, 16 output columns) items read the down rows and H and
-// write fp32 Y per sorted row.  The expert FFN (gate/up
-// then down, from one slot record) is the one "The Expert Cache That Follows
-// the Router" describes in section "One logical expert, two physical levels of
-// memory"; SwiGLU is this build's activation.
+// Each active slot serves a few token rows (decode: usually one).  Weights are
+// panel-ordered (32 rows per panel; one 16-byte load per lane at consecutive
+// addresses fetches rows 32p..32p+31 at two adjacent chunk columns — a "lane
+// block" of 1 KiB), so every weight load of these kernels is a 1 KiB
+// contiguous run.
+//
+// Gate/up: a workgroup owns (active slot, 32-neuron panel, K-part): its eight
+// waves split the K-part's lane blocks of the gate and the up panel, dot them
+// with the token rows (staged once in LDS), and add the wave partials in a
+// fixed order; the K-part sums of g and u go to a small fp32 buffer.
+// Down: a workgroup owns (active slot, 32 output columns); its prologue forms
+// h = silu(sum g) * (sum u) for the slot's rows in LDS (the K-parts added in a
+// fixed order, rounded to bf16), then four waves split K = f and reduce
+// through LDS into Y.
+// No atomics and no cross-workgroup ordering: results are deterministic.
+// Work items are counted from the device-side number of active slots, so one
+// grid serves any hit/fill mix.  The expert FFN (gate/up then down, from one
+// slot record) is the one "The Expert Cache That Follows the Router"
+// describes in section "One logical expert, two physical levels of memory";
+// SwiGLU is this library's activation.
 #include "wfmt.h"
 
 namespace ftmoe {
 
-constexpr int kGemvThreads = 256;
-constexpr int kGemvBlocks = 1024;
-constexpr int kGemvNeurons = 8;     // per gate/up item: 8 gate + 8 up rows, K split over the 4 waves
-constexpr int kGemvCols = 16;       // per down item (4 waves x 4)
+constexpr int kGuWaves = 8;          // waves per gate/up workgroup
+constexpr int kDnWaves = 4;          // waves per down workgroup
+constexpr int kBatch = 8;            // lane blocks per matrix held in flight per lane
+constexpr int kMaxSpan = 4096;       // K elements of x staged per gate/up workgroup
 
 struct GemvArgs {
     const uint16_t* x;
@@ -32,292 +39,294 @@ struct GemvArgs {
     const uint8_t* pool;
     int64_t S;
     int64_t off_gate, off_up, off_down, off_sg, off_su, off_sd;
-    float* Hf;          // [cap_g][f]
+    float* part;        // [2][kq][cap_g][f]: K-part sums of g (0) and u (1)
     float* Y;           // [cap][d]
     int cap_g;
+    int kq;             // K-parts of gate/up
+    int lbq;            // lane blocks per K-part
 };
+
+// K-parts of the gate/up GEMV for a shape: about eight lane blocks per wave
+// and matrix, and at most kMaxSpan activations staged per workgroup.
+int gemv_kparts(const ft_shape& s) {
+    const int64_t rb = s.fmt == FT_FMT_BF16 ? 2ll * s.d_model : s.fmt == FT_FMT_FP8_B128 ? s.d_model : s.d_model / 2;
+    const int64_t lb = rb / 32;
+    int kq = (int)(lb / (kGuWaves * kBatch));
+    const int need = (int)((s.d_model + kMaxSpan - 1) / kMaxSpan);
+    if (kq < need) kq = need;
+    if (kq < 1) kq = 1;
+    if (kq > 8) kq = 8;
+    return kq;
+}
 
 namespace {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
+__device__ __forceinline__ float swap_halves_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 
-// dot of one weight chunk with EPC activations given as packed bf16 pairs
+// dot of one 16-byte weight chunk with EPC bf16 activations (xw: EPC/2 packed pairs)
 template <int FMT>
-__device__ __forceinline__ float chunk_dot_bf16x(const uint4 w, float scale, const uint32_t* xw);
-
-template <>
-__device__ __forceinline__ float chunk_dot_bf16x<FT_FMT_BF16>(const uint4 w, float, const uint32_t* xw) {
-    float s = dot2_bf16(w.x, xw[0], 0.0f);
-    s = dot2_bf16(w.y, xw[1], s);
-    s = dot2_bf16(w.z, xw[2], s);
-    return dot2_bf16(w.w, xw[3], s);
-}
-
-template <>
-__device__ __forceinline__ float chunk_dot_bf16x<FT_FMT_FP8_B128>(const uint4 w, float scale, const uint32_t* xw) {
-    float v[16];
-    WF<FT_FMT_FP8_B128>::to_f32(w, v);
-    float s = 0.0f;
+__device__ __forceinline__ float chunk_dot(const u32x4_t w, float scale, const uint32_t* xw) {
+    if constexpr (FMT == FT_FMT_BF16) {
+        float s = dot2_bf16(w[0], xw[0], 0.0f);
+        s = dot2_bf16(w[1], xw[1], s);
+        s = dot2_bf16(w[2], xw[2], s);
+        return dot2_bf16(w[3], xw[3], s);
+    } else if constexpr (FMT == FT_FMT_FP8_B128) {
+        // e4m3 values are exact in bf16; the block scale multiplies the chunk sum
+        float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        s = fmaf(v[2 * i], bf16lo(xw[i]), s);
-        s = fmaf(v[2 * i + 1], bf16hi(xw[i]), s);
-    }
-    return s * scale;
-}
-
-template <>
-__device__ __forceinline__ float chunk_dot_bf16x<FT_FMT_MXFP4_B32>(const uint4 w, float scale, const uint32_t* xw) {
-    float v[32];
-    WF<FT_FMT_MXFP4_B32>::to_f32(w, scale, v);
-    float s = 0.0f;
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+            const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+            s = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2_t, xw[2 * i]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2_t, xw[2 * i + 1]), s, false);
+        }
+        return s * scale;
+    } else {
+        // e2m1 times a power-of-two scale is exact in bf16
+        float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        s = fmaf(v[2 * i], bf16lo(xw[i]), s);
-        s = fmaf(v[2 * i + 1], bf16hi(xw[i]), s);
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 0);
+            const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 1);
+            const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 2);
+            const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 3);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p0, __builtin_bit_cast(bf16x2_t, xw[4 * i]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p1, __builtin_bit_cast(bf16x2_t, xw[4 * i + 1]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p2, __builtin_bit_cast(bf16x2_t, xw[4 * i + 2]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p3, __builtin_bit_cast(bf16x2_t, xw[4 * i + 3]), s, false);
+        }
+        return s;
     }
-    return s;
 }
 
-// dot of one weight chunk with EPC fp32 activations
+// Scale of lane block j of a panel for this lane: FP8 — the fp32 scale of the
+// 128 x 128 block (uniform over the panel's 32 rows and the block's two chunk
+// columns); MXFP4 — the lane's own e8m0 byte, stored in the same panel order.
 template <int FMT>
-__device__ __forceinline__ float chunk_dot_f32x(const uint4 w, float scale, const float* h);
-
-template <>
-__device__ __forceinline__ float chunk_dot_f32x<FT_FMT_BF16>(const uint4 w, float, const float* h) {
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        s = fmaf(bf16lo(ww[i]), h[2 * i], s);
-        s = fmaf(bf16hi(ww[i]), h[2 * i + 1], s);
-    }
-    return s;
-}
-
-template <>
-__device__ __forceinline__ float chunk_dot_f32x<FT_FMT_FP8_B128>(const uint4 w, float scale, const float* h) {
-    float v[16];
-    WF<FT_FMT_FP8_B128>::to_f32(w, v);
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s = fmaf(v[i], h[i], s);
-    return s * scale;
-}
-
-template <>
-__device__ __forceinline__ float chunk_dot_f32x<FT_FMT_MXFP4_B32>(const uint4 w, float scale, const float* h) {
-    float v[32];
-    WF<FT_FMT_MXFP4_B32>::to_f32(w, scale, v);
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) s = fmaf(v[i], h[i], s);
-    return s;
-}
-
-// scale of the chunk starting at (row n, column k0) of a [rows x K] matrix
-template <int FMT>
-__device__ __forceinline__ float chunk_scale(const uint8_t* rec, int64_t off_s, int n, int k0, int K) {
+__device__ __forceinline__ float lane_scale(const uint8_t* rec, int64_t off_s, int p, int j, int lane, int K) {
     if constexpr (FMT == FT_FMT_FP8_B128) {
-        return reinterpret_cast<const float*>(rec + off_s)[(n >> 7) * (K >> 7) + (k0 >> 7)];
+        return reinterpret_cast<const float*>(rec + off_s)[(p >> 2) * (K >> 7) + (j >> 2)];
     } else if constexpr (FMT == FT_FMT_MXFP4_B32) {
-        return e8m0_to_f32(rec[off_s + (int64_t)n * (K >> 5) + (k0 >> 5)]);
+        return e8m0_to_f32(rec[off_s + (int64_t)p * K + j * 64 + lane]);
     } else {
         return 1.0f;
     }
 }
 
 template <int FMT, int TG>
-__global__ void __launch_bounds__(kGemvThreads) gemv_gateup_kernel(GemvArgs a) {
+__global__ void __launch_bounds__(kGuWaves * 64) gemv_gateup_kernel(GemvArgs a) {
     constexpr int EPC = WF<FMT>::EPC;
-    constexpr int XW = EPC / 2;     // packed bf16 words of x per chunk
-    constexpr int NN = kGemvNeurons;
-    __shared__ float red[4][NN][2][TG];
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int n_active = a.meta[0];
+    constexpr int XW = EPC / 2;            // packed bf16 pairs of x per chunk
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [TG][span]
+    __shared__ float red[kGuWaves][2][TG][32];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, tid = threadIdx.x;
     const int d = a.d, f = a.f;
-    const int NB = f / NN;
-    const int items = n_active * NB;
-    const int cpr = d / EPC;                 // 16-byte chunks per row
-    const int cpw = (cpr + 3) / 4;           // the K quarter of each wave
-    const int c_begin = wid * cpw;
-    const int c_end = (c_begin + cpw) < cpr ? (c_begin + cpw) : cpr;
+    const int P = f >> 5;
+    const int item = blockIdx.x;
+    const int kq = item % a.kq;
+    const int rest = item / a.kq;
+    const int p = rest % P;
+    const int ai = rest / P;
+    if (ai >= a.meta[0]) return;
+    const int slot = a.active_slot[ai];
+    const int r0 = a.seg[ai];
+    int nrows = a.seg[ai + 1] - r0;
+    nrows = nrows > TG ? TG : nrows;
+    const uint8_t* rec = a.pool + (int64_t)slot * a.S;
     const int64_t rowb = WF<FMT>::row_bytes(d);
+    const int LB = (int)(rowb >> 5);                       // lane blocks per panel
+    const int jq0 = kq * a.lbq;
+    const int jq1 = min(LB, jq0 + a.lbq);
+    const int nq = jq1 - jq0;
+    const int jw0 = jq0 + (wid * nq) / kGuWaves;
+    const int jw1 = jq0 + ((wid + 1) * nq) / kGuWaves;
+    const uint8_t* gp = rec + a.off_gate + (int64_t)p * 32 * rowb + lane * 16;
+    const uint8_t* up = rec + a.off_up + (int64_t)p * 32 * rowb + lane * 16;
 
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        const int ai = item / NB;
-        const int nb = item - ai * NB;
-        const int slot = a.active_slot[ai];
-        const int r0 = a.seg[ai];
-        int nrows = a.seg[ai + 1] - r0;
-        nrows = nrows > TG ? TG : nrows;
-        const uint8_t* rec = a.pool + (int64_t)slot * a.S;
-        const int n0 = nb * NN;
-
-        const uint16_t* xr[TG];
+    // first batch of weight loads before anything else
+    u32x4_t wg[kBatch], wu[kBatch];
 #pragma unroll
-        for (int t = 0; t < TG; ++t) {
-            const int rr = r0 + (t < nrows ? t : nrows - 1);
-            xr[t] = a.x + (int64_t)(a.perm[rr] / a.k) * d;
+    for (int i = 0; i < kBatch; ++i)
+        if (jw0 + i < jw1) {
+            wg[i] = *reinterpret_cast<const u32x4_t*>(gp + (int64_t)(jw0 + i) * 1024);
+            wu[i] = *reinterpret_cast<const u32x4_t*>(up + (int64_t)(jw0 + i) * 1024);
         }
-        float acc[NN][2][TG];
-#pragma unroll
-        for (int i = 0; i < NN; ++i)
-#pragma unroll
-            for (int g = 0; g < 2; ++g)
-#pragma unroll
-                for (int t = 0; t < TG; ++t) acc[i][g][t] = 0.0f;
 
-        for (int c = c_begin + lane; c < c_end; c += 64) {
-            const int k0 = c * EPC;
-            uint4 wv[NN][2];
+    // the token rows' activations of this K-part into LDS
+    const int k0 = 2 * jq0 * EPC;
+    const int span = 2 * nq * EPC;
+    for (int q = tid; q < TG * (span >> 3); q += kGuWaves * 64) {
+        const int t = q / (span >> 3), c8 = q - t * (span >> 3);
+        const int rr = r0 + (t < nrows ? t : nrows - 1);
+        const uint16_t* xr = a.x + (int64_t)(a.perm[rr] / a.k) * d + k0;
+        *reinterpret_cast<u32x4_t*>(&xs[t * span + 8 * c8]) = *reinterpret_cast<const u32x4_t*>(xr + 8 * c8);
+    }
+    __syncthreads();
+
+    float ag[TG], au[TG];
 #pragma unroll
-            for (int i = 0; i < NN; ++i) {
-                wv[i][0] = *reinterpret_cast<const uint4*>(rec + a.off_gate + (int64_t)(n0 + i) * rowb + c * 16);
-                wv[i][1] = *reinterpret_cast<const uint4*>(rec + a.off_up + (int64_t)(n0 + i) * rowb + c * 16);
-            }
-            float sc[NN][2];
+    for (int t = 0; t < TG; ++t) ag[t] = au[t] = 0.0f;
+    for (int j0 = jw0; j0 < jw1; j0 += kBatch) {
+        if (j0 != jw0) {
 #pragma unroll
-            for (int i = 0; i < NN; ++i) {
-                // FP8: the NN neurons share one 128-row scale block; MXFP4: one scale per row
-                const int nr = (FMT == FT_FMT_MXFP4_B32) ? n0 + i : n0;
-                sc[i][0] = chunk_scale<FMT>(rec, a.off_sg, nr, k0, d);
-                sc[i][1] = chunk_scale<FMT>(rec, a.off_su, nr, k0, d);
-            }
-            uint32_t xw[TG][XW];
-#pragma unroll
-            for (int t = 0; t < TG; ++t)
-#pragma unroll
-                for (int q = 0; q < XW / 4; ++q) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(xr[t] + k0 + 8 * q);
-                    xw[t][4 * q] = v.x;
-                    xw[t][4 * q + 1] = v.y;
-                    xw[t][4 * q + 2] = v.z;
-                    xw[t][4 * q + 3] = v.w;
-                }
-#pragma unroll
-            for (int i = 0; i < NN; ++i)
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    if constexpr (FMT == FT_FMT_BF16) {
-#pragma unroll
-                        for (int t = 0; t < TG; ++t) acc[i][g][t] += chunk_dot_bf16x<FMT>(wv[i][g], 1.0f, xw[t]);
-                    } else {
-                        // decode the chunk once, use it for every token
-                        float v[EPC];
-                        if constexpr (FMT == FT_FMT_FP8_B128) {
-                            WF<FMT>::to_f32(wv[i][g], v);
-                        } else {
-                            WF<FMT>::to_f32(wv[i][g], sc[i][g], v);
-                        }
-#pragma unroll
-                        for (int t = 0; t < TG; ++t) {
-                            float sacc = 0.0f;
-#pragma unroll
-                            for (int j = 0; j < XW; ++j) {
-                                sacc = fmaf(v[2 * j], bf16lo(xw[t][j]), sacc);
-                                sacc = fmaf(v[2 * j + 1], bf16hi(xw[t][j]), sacc);
-                            }
-                            acc[i][g][t] += (FMT == FT_FMT_FP8_B128) ? sacc * sc[i][g] : sacc;
-                        }
-                    }
+            for (int i = 0; i < kBatch; ++i)
+                if (j0 + i < jw1) {
+                    wg[i] = *reinterpret_cast<const u32x4_t*>(gp + (int64_t)(j0 + i) * 1024);
+                    wu[i] = *reinterpret_cast<const u32x4_t*>(up + (int64_t)(j0 + i) * 1024);
                 }
         }
-        // K-split partials: wave sums, then the four waves in a fixed order
 #pragma unroll
-        for (int i = 0; i < NN; ++i)
-#pragma unroll
-            for (int g = 0; g < 2; ++g)
+        for (int i = 0; i < kBatch; ++i) {
+            const int j = j0 + i;
+            if (j < jw1) {
+                const float sg = lane_scale<FMT>(rec, a.off_sg, p, j, lane, d);
+                const float su = lane_scale<FMT>(rec, a.off_su, p, j, lane, d);
+                const int xo = (2 * (j - jq0) + (lane >> 5)) * EPC;    // this lane's chunk inside the span
 #pragma unroll
                 for (int t = 0; t < TG; ++t) {
-                    const float v = wave_sum(acc[i][g][t]);
-                    if (lane == 0) red[wid][i][g][t] = v;
+                    uint32_t xw[XW];
+#pragma unroll
+                    for (int q = 0; q < XW / 4; ++q) {
+                        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&xs[t * span + xo + 8 * q]);
+                        xw[4 * q] = v[0];
+                        xw[4 * q + 1] = v[1];
+                        xw[4 * q + 2] = v[2];
+                        xw[4 * q + 3] = v[3];
+                    }
+                    ag[t] += chunk_dot<FMT>(wg[i], sg, xw);
+                    au[t] += chunk_dot<FMT>(wu[i], su, xw);
                 }
-        __syncthreads();
-        const int tid = threadIdx.x;
-        if (tid < NN * nrows) {
-            const int i = tid % NN, t = tid / NN;
-            const float gs = (red[0][i][0][t] + red[1][i][0][t]) + (red[2][i][0][t] + red[3][i][0][t]);
-            const float us = (red[0][i][1][t] + red[1][i][1][t]) + (red[2][i][1][t] + red[3][i][1][t]);
-            a.Hf[(int64_t)(r0 + t) * f + n0 + i] = silu(gs) * us;
+            }
         }
-        __syncthreads();
+    }
+    // lanes l and l + 32 hold the same row's two chunk columns
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+        const float g = swap_halves_sum(ag[t]);
+        const float u = swap_halves_sum(au[t]);
+        if (lane < 32) {
+            red[wid][0][t][lane] = g;
+            red[wid][1][t][lane] = u;
+        }
+    }
+    __syncthreads();
+    if (tid < 2 * TG * 32) {
+        const int n = tid & 31, t = (tid >> 5) % TG, m = tid / (32 * TG);
+        if (t < nrows) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kGuWaves; ++w) s += red[w][m][t][n];
+            a.part[(((int64_t)m * a.kq + kq) * a.cap_g + r0 + t) * f + 32 * p + n] = s;
+        }
     }
 }
 
 template <int FMT, int TG>
-__global__ void __launch_bounds__(kGemvThreads) gemv_down_kernel(GemvArgs a) {
+__global__ void __launch_bounds__(kDnWaves * 64) gemv_down_kernel(GemvArgs a) {
     constexpr int EPC = WF<FMT>::EPC;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int n_active = a.meta[0];
+    extern __shared__ __attribute__((aligned(16))) uint16_t hs[];   // [TG][f] bf16
+    __shared__ float red[kDnWaves][TG][32];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, tid = threadIdx.x;
     const int d = a.d, f = a.f;
-    const int CB = d / kGemvCols;
-    const int cpr = f / EPC;
-    const int items = n_active * CB;
+    const int Q = d >> 5;
+    const int q = blockIdx.x % Q;
+    const int ai = blockIdx.x / Q;
+    if (ai >= a.meta[0]) return;
+    const int slot = a.active_slot[ai];
+    const int r0 = a.seg[ai];
+    int nrows = a.seg[ai + 1] - r0;
+    nrows = nrows > TG ? TG : nrows;
+    const uint8_t* rec = a.pool + (int64_t)slot * a.S;
     const int64_t rowb = WF<FMT>::row_bytes(f);
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        const int ai = item / CB;
-        const int cb = item - ai * CB;
-        const int slot = a.active_slot[ai];
-        const int r0 = a.seg[ai];
-        int nrows = a.seg[ai + 1] - r0;
-        nrows = nrows > TG ? TG : nrows;
-        const uint8_t* rec = a.pool + (int64_t)slot * a.S;
-        const int c0 = cb * kGemvCols + wid * 4;
-        float acc[4][TG];
+    const int LB = (int)(rowb >> 5);
+    const int jw0 = (wid * LB) / kDnWaves;
+    const int jw1 = ((wid + 1) * LB) / kDnWaves;
+    const uint8_t* dp = rec + a.off_down + (int64_t)q * 32 * rowb + lane * 16;
+
+    u32x4_t wd[kBatch];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int t = 0; t < TG; ++t) acc[i][t] = 0.0f;
-        for (int c = lane; c < cpr; c += 64) {
-            const int k0 = c * EPC;
-            uint4 wv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                wv[i] = *reinterpret_cast<const uint4*>(rec + a.off_down + (int64_t)(c0 + i) * rowb + c * 16);
-            float sc[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sc[i] = chunk_scale<FMT>(rec, a.off_sd, FMT == FT_FMT_MXFP4_B32 ? c0 + i : c0, k0, f);
-#pragma unroll
-            for (int t = 0; t < TG; ++t) {
-                const int rr = r0 + (t < nrows ? t : nrows - 1);
-                float h[EPC];
-#pragma unroll
-                for (int q = 0; q < EPC / 4; ++q) {
-                    float4 v = *reinterpret_cast<const float4*>(a.Hf + (int64_t)rr * f + k0 + 4 * q);
-                    h[4 * q] = v.x;
-                    h[4 * q + 1] = v.y;
-                    h[4 * q + 2] = v.z;
-                    h[4 * q + 3] = v.w;
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][t] += chunk_dot_f32x<FMT>(wv[i], sc[i], h);
+    for (int i = 0; i < kBatch; ++i)
+        if (jw0 + i < jw1) wd[i] = *reinterpret_cast<const u32x4_t*>(dp + (int64_t)(jw0 + i) * 1024);
+
+    // h = silu(g) * u (bf16, as the prefill path keeps it) for the slot's
+    // rows, the K-parts added in order
+    for (int i = tid; i < TG * f; i += kDnWaves * 64) {
+        const int t = i / f, n = i - t * f;
+        float h = 0.0f;
+        if (t < nrows) {
+            float g = 0.0f, u = 0.0f;
+            for (int kk = 0; kk < a.kq; ++kk) {
+                g += a.part[((int64_t)kk * a.cap_g + r0 + t) * f + n];
+                u += a.part[(((int64_t)a.kq + kk) * a.cap_g + r0 + t) * f + n];
             }
+            h = silu(g) * u;
+        }
+        hs[i] = f32_to_bf16_rne(h);
+    }
+    __syncthreads();
+
+    float acc[TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) acc[t] = 0.0f;
+    for (int j0 = jw0; j0 < jw1; j0 += kBatch) {
+        if (j0 != jw0) {
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                if (j0 + i < jw1) wd[i] = *reinterpret_cast<const u32x4_t*>(dp + (int64_t)(j0 + i) * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kBatch; ++i) {
+            const int j = j0 + i;
+            if (j < jw1) {
+                const float sc = lane_scale<FMT>(rec, a.off_sd, q, j, lane, f);
+                const int ko = (2 * j + (lane >> 5)) * EPC;
 #pragma unroll
-            for (int t = 0; t < TG; ++t) {
-                float v = wave_sum(acc[i][t]);
-                if (lane == 0 && t < nrows) a.Y[(int64_t)(r0 + t) * d + c0 + i] = v;
+                for (int t = 0; t < TG; ++t) {
+                    uint32_t hw[EPC / 2];
+#pragma unroll
+                    for (int r = 0; r < EPC / 8; ++r) {
+                        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&hs[t * f + ko + 8 * r]);
+                        hw[4 * r] = v[0];
+                        hw[4 * r + 1] = v[1];
+                        hw[4 * r + 2] = v[2];
+                        hw[4 * r + 3] = v[3];
+                    }
+                    acc[t] += chunk_dot<FMT>(wd[i], sc, hw);
+                }
             }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+        const float v = swap_halves_sum(acc[t]);
+        if (lane < 32) red[wid][t][lane] = v;
+    }
+    __syncthreads();
+    if (tid < TG * 32) {
+        const int n = tid & 31, t = tid >> 5;
+        if (t < nrows) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kDnWaves; ++w) s += red[w][t][n];
+            a.Y[(int64_t)(r0 + t) * d + 32 * q + n] = s;
+        }
     }
 }
 
 template <int FMT, int TG>
-hipError_t launch_fmt(const GemvArgs& a, Timing* tm, hipStream_t st) {
+hipError_t launch_fmt(const GemvArgs& a, int max_active, Timing* tm, hipStream_t st) {
+    const size_t xs_bytes = (size_t)TG * 2 * a.lbq * WF<FMT>::EPC * sizeof(uint16_t);
+    const size_t hs_bytes = (size_t)TG * a.f * sizeof(uint16_t);
+    const unsigned g1 = (unsigned)(max_active * (a.f / 32) * a.kq);
+    const unsigned g2 = (unsigned)(max_active * (a.d / 32));
     TimedLaunch t1 = timing_launch(tm, FT_K_GEMV_GU);
-    hipExtLaunchKernelGGL((gemv_gateup_kernel<FMT, TG>), dim3(kGemvBlocks), dim3(kGemvThreads), 0, st, t1.start,
+    hipExtLaunchKernelGGL((gemv_gateup_kernel<FMT, TG>), dim3(g1), dim3(kGuWaves * 64), xs_bytes, st, t1.start,
                           t1.stop, 0, a);
     TimedLaunch t2 = timing_launch(tm, FT_K_GEMV_DOWN);
-    hipExtLaunchKernelGGL((gemv_down_kernel<FMT, TG>), dim3(kGemvBlocks), dim3(kGemvThreads), 0, st, t2.start,
+    hipExtLaunchKernelGGL((gemv_down_kernel<FMT, TG>), dim3(g2), dim3(kDnWaves * 64), hs_bytes, st, t2.start,
                           t2.stop, 0, a);
     return hipGetLastError();
 }
@@ -343,18 +352,27 @@ hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     a.off_sg = c->rl.off_sg;
     a.off_su = c->rl.off_su;
     a.off_sd = c->rl.off_sd;
-    a.Hf = c->gv_H;
+    a.part = c->gv_part;
     a.Y = c->Y;
     a.cap_g = c->cap_gemv;
+    a.kq = c->gv_kq;
+    const int64_t rowb = c->sh.fmt == FT_FMT_BF16 ? 2ll * a.d : c->sh.fmt == FT_FMT_FP8_B128 ? a.d : a.d / 2;
+    a.lbq = (int)(((rowb >> 5) + a.kq - 1) / a.kq);
+    // active slots this call can have: one per route at most, and at most N
+    const int64_t R = (int64_t)T * a.k;
+    const int max_active = (int)(R < c->N ? R : c->N);
+    if (R > a.cap_g) return hipErrorInvalidValue;
     const bool one = T == 1;
     switch (c->sh.fmt) {
         case FT_FMT_BF16:
-            return one ? launch_fmt<FT_FMT_BF16, 1>(a, c->timing, st) : launch_fmt<FT_FMT_BF16, kGemvMaxTokens>(a, c->timing, st);
+            return one ? launch_fmt<FT_FMT_BF16, 1>(a, max_active, c->timing, st)
+                       : launch_fmt<FT_FMT_BF16, kGemvMaxTokens>(a, max_active, c->timing, st);
         case FT_FMT_FP8_B128:
-            return one ? launch_fmt<FT_FMT_FP8_B128, 1>(a, c->timing, st) : launch_fmt<FT_FMT_FP8_B128, kGemvMaxTokens>(a, c->timing, st);
+            return one ? launch_fmt<FT_FMT_FP8_B128, 1>(a, max_active, c->timing, st)
+                       : launch_fmt<FT_FMT_FP8_B128, kGemvMaxTokens>(a, max_active, c->timing, st);
         case FT_FMT_MXFP4_B32:
-            return one ? launch_fmt<FT_FMT_MXFP4_B32, 1>(a, c->timing, st)
-                       : launch_fmt<FT_FMT_MXFP4_B32, kGemvMaxTokens>(a, c->timing, st);
+            return one ? launch_fmt<FT_FMT_MXFP4_B32, 1>(a, max_active, c->timing, st)
+                       : launch_fmt<FT_FMT_MXFP4_B32, kGemvMaxTokens>(a, max_active, c->timing, st);
     }
     return hipErrorInvalidValue;
 }

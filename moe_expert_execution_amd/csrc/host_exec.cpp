@@ -33,7 +33,6 @@ namespace ftmoe {
 namespace {
 
 constexpr int kRing = 256;
-constexpr int kRowBlock = 16;
 
 struct Job {
     int layer = 0, T = 0;
@@ -91,71 +90,105 @@ struct HostBranch {
 
 namespace {
 
-// ---- row decoders: one weight row -> fp32 ------------------------------------
-inline float e4m3_to_f32(uint8_t c) {
-    const uint32_t s = (c & 0x80u) << 24;
-    const uint32_t e = (c >> 3) & 0xF, m = c & 7;
-    float v;
-    if (e == 0) {
-        v = (float)m * (1.0f / 512.0f);
-    } else {
-        v = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
-    }
-    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) | s);
-}
+// ---- weight decoding ------------------------------------------------------------
+// Panel order: rows 32p..32p+31 of a [rows x K] matrix form one contiguous
+// block; inside it the 16-byte unit c of row r sits at unit (c/2)*64 +
+// (c%2)*32 + r%32.  So the 16 rows [32p + 16h, +16) at chunk column c are
+// 256 contiguous bytes: a worker that owns a half panel streams 256-byte runs.
 
 const float kE2M1[16] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f,
                          -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
 
-// Decode row n of a [rows x K] matrix stored at `off` (scales at `soff`).
-void decode_row(const HostBranch* hb, const uint8_t* rec, int64_t off, int64_t soff, int n, int K, float* out) {
+// 16 e4m3 codes -> fp32 (OCP E4M3: bias 7, subnormals m * 2^-9; NaN codes are
+// not produced by the encoder and decode as large finite values here).
+inline __m512 e4m3x16(const uint8_t* p) {
+    const __m512i v = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(p)));
+    const __m512i sgn = _mm512_slli_epi32(_mm512_and_si512(v, _mm512_set1_epi32(0x80)), 24);
+    const __m512i e = _mm512_and_si512(_mm512_srli_epi32(v, 3), _mm512_set1_epi32(0xF));
+    const __m512i m = _mm512_and_si512(v, _mm512_set1_epi32(7));
+    const __m512i nrm = _mm512_or_si512(_mm512_slli_epi32(_mm512_add_epi32(e, _mm512_set1_epi32(120)), 23),
+                                        _mm512_slli_epi32(m, 20));
+    const __m512 sub = _mm512_mul_ps(_mm512_cvtepi32_ps(m), _mm512_set1_ps(1.0f / 512.0f));
+    const __mmask16 isn = _mm512_cmpneq_epi32_mask(e, _mm512_setzero_si512());
+    const __m512 mag = _mm512_mask_mov_ps(sub, isn, _mm512_castsi512_ps(nrm));
+    return _mm512_castsi512_ps(_mm512_or_si512(_mm512_castps_si512(mag), sgn));
+}
+
+// 8 bytes of packed e2m1 (low nibble first) -> 16 fp32 values
+inline __m512 e2m1x16(const uint8_t* p, __m512 lut) {
+    const __m128i b = _mm_loadl_epi64(reinterpret_cast<const __m128i*>(p));
+    const __m512i v = _mm512_cvtepu8_epi32(_mm_unpacklo_epi8(b, b));      // b0 b0 b1 b1 ...
+    const __m512i sh = _mm512_set_epi32(4, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 0);
+    const __m512i idx = _mm512_and_si512(_mm512_srlv_epi32(v, sh), _mm512_set1_epi32(0xF));
+    return _mm512_permutexvar_ps(idx, lut);
+}
+
+// Dots of the 16 rows [32p + 16h, +16) of a panel-ordered [rows x K] matrix
+// (codes at `off`, scales at `soff`) with nt fp32 vectors vec[i] (length K):
+// out[i * 16 + r].  acc is caller scratch of 16 * nt vectors.
+void half_panel_dots(const HostBranch* hb, const uint8_t* rec, int64_t off, int64_t soff, int p, int h, int K,
+                     const float* const* vec, int nt, __m512* acc, float* out) {
+    for (int i = 0; i < 16 * nt; ++i) acc[i] = _mm512_setzero_ps();
     switch (hb->sh.fmt) {
         case FT_FMT_BF16: {
-            const uint16_t* r = reinterpret_cast<const uint16_t*>(rec + off) + (int64_t)n * K;
-            int i = 0;
-            for (; i + 16 <= K; i += 16) {
-                __m256i w16 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(r + i));
-                __m512i w32 = _mm512_slli_epi32(_mm512_cvtepu16_epi32(w16), 16);
-                _mm512_storeu_ps(out + i, _mm512_castsi512_ps(w32));
+            // a zmm holds rows (2q, 2q + 1) x 8 values; acc[i * 16 + q] for q < 8
+            const uint8_t* base = rec + off + (int64_t)p * 32 * (2ll * K) + h * 256;
+            for (int c = 0; c < K / 8; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                __m512 w[8];
+                for (int q = 0; q < 8; ++q) {
+                    const __m256i w16 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(u + 32 * q));
+                    w[q] = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(w16), 16));
+                }
+                for (int i = 0; i < nt; ++i) {
+                    const __m512 xv = _mm512_broadcast_f32x8(_mm256_loadu_ps(vec[i] + 8 * c));
+                    for (int q = 0; q < 8; ++q) acc[i * 16 + q] = _mm512_fmadd_ps(w[q], xv, acc[i * 16 + q]);
+                }
             }
-            for (; i < K; ++i) out[i] = __builtin_bit_cast(float, (uint32_t)r[i] << 16);
-            break;
+            for (int i = 0; i < nt; ++i)
+                for (int q = 0; q < 8; ++q) {
+                    const __m512 a = acc[i * 16 + q];
+                    out[i * 16 + 2 * q] = _mm512_mask_reduce_add_ps(0x00FF, a);
+                    out[i * 16 + 2 * q + 1] = _mm512_mask_reduce_add_ps(0xFF00, a);
+                }
+            return;
         }
         case FT_FMT_FP8_B128: {
-            const uint8_t* r = rec + off + (int64_t)n * K;
-            const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(n >> 7) * (K >> 7);
-            for (int b = 0; b < K; b += 128) {
-                const float s = sc[b >> 7];
-                for (int i = 0; i < 128; ++i) out[b + i] = e4m3_to_f32(r[b + i]) * s;
+            const uint8_t* base = rec + off + (int64_t)p * 32 * K + h * 256;
+            const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
+            for (int c = 0; c < K / 16; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                const float s = sc[(16 * c) >> 7];
+                for (int r = 0; r < 16; ++r) {
+                    const __m512 w = _mm512_mul_ps(e4m3x16(u + 16 * r), _mm512_set1_ps(s));
+                    for (int i = 0; i < nt; ++i)
+                        acc[i * 16 + r] = _mm512_fmadd_ps(w, _mm512_loadu_ps(vec[i] + 16 * c), acc[i * 16 + r]);
+                }
             }
             break;
         }
         case FT_FMT_MXFP4_B32: {
-            const uint8_t* r = rec + off + (int64_t)n * (K / 2);
-            const uint8_t* sc = rec + soff + (int64_t)n * (K >> 5);
-            for (int b = 0; b < K; b += 32) {
-                const float s = ldexpf(1.0f, (int)sc[b >> 5] - 127);
-                for (int i = 0; i < 16; ++i) {
-                    const uint8_t v = r[(b >> 1) + i];
-                    out[b + 2 * i] = kE2M1[v & 0xF] * s;
-                    out[b + 2 * i + 1] = kE2M1[v >> 4] * s;
+            const __m512 lut = _mm512_loadu_ps(kE2M1);
+            const uint8_t* base = rec + off + (int64_t)p * 32 * (K / 2) + h * 256;
+            const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h;     // scale panel: 32 x K/32 bytes
+            for (int c = 0; c < K / 32; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
+                for (int r = 0; r < 16; ++r) {
+                    const __m512 s = _mm512_set1_ps(ldexpf(1.0f, (int)su[r] - 127));
+                    const __m512 w0 = _mm512_mul_ps(e2m1x16(u + 16 * r, lut), s);
+                    const __m512 w1 = _mm512_mul_ps(e2m1x16(u + 16 * r + 8, lut), s);
+                    for (int i = 0; i < nt; ++i) {
+                        __m512 a = _mm512_fmadd_ps(w0, _mm512_loadu_ps(vec[i] + 32 * c), acc[i * 16 + r]);
+                        acc[i * 16 + r] = _mm512_fmadd_ps(w1, _mm512_loadu_ps(vec[i] + 32 * c + 16), a);
+                    }
                 }
             }
             break;
         }
     }
-}
-
-inline float dot_f32(const float* a, const float* b, int n) {
-    __m512 acc0 = _mm512_setzero_ps(), acc1 = _mm512_setzero_ps();
-    int i = 0;
-    for (; i + 32 <= n; i += 32) {
-        acc0 = _mm512_fmadd_ps(_mm512_loadu_ps(a + i), _mm512_loadu_ps(b + i), acc0);
-        acc1 = _mm512_fmadd_ps(_mm512_loadu_ps(a + i + 16), _mm512_loadu_ps(b + i + 16), acc1);
-    }
-    float s = _mm512_reduce_add_ps(_mm512_add_ps(acc0, acc1));
-    for (; i < n; ++i) s += a[i] * b[i];
-    return s;
+    for (int i = 0; i < nt; ++i)
+        for (int r = 0; r < 16; ++r) out[i * 16 + r] = _mm512_reduce_add_ps(acc[i * 16 + r]);
 }
 
 inline float silu(float z) { return z / (1.0f + std::exp(-z)); }
@@ -172,8 +205,26 @@ void barrier(HostBranch* hb, int participants) {
     }
 }
 
-// All participants run this for the current job.
-void run_job(HostBranch* hb, int participants, std::vector<float>& rowbuf) {
+// Per-thread scratch of the host workers.
+struct WorkerScratch {
+    std::vector<__m512> acc;            // 16 * tokens accumulators
+    std::vector<float> g, u, y;         // 16 * tokens dot results
+    std::vector<const float*> vec;      // token vectors
+    void fit(int nt) {
+        if ((int)vec.size() < nt) {
+            acc.resize(16 * (size_t)nt);
+            g.resize(16 * (size_t)nt);
+            u.resize(16 * (size_t)nt);
+            y.resize(16 * (size_t)nt);
+            vec.resize(nt);
+        }
+    }
+};
+
+// All participants run this for the current job.  Work items are half
+// panels: 16 rows of the gate and up matrices (phase 1), then 16 output
+// columns of the down matrix (phase 2).
+void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
     const Job& jb = hb->job;
     const int d = hb->sh.d_model, f = hb->sh.d_ff, E = hb->sh.experts;
     const int64_t S = hb->rl.S;
@@ -182,34 +233,35 @@ void run_job(HostBranch* hb, int participants, std::vector<float>& rowbuf) {
         const int e = jb.experts[xi];
         const int t0 = jb.tok_off[xi], t1 = jb.tok_off[xi + 1], nt = t1 - t0;
         const uint8_t* rec = hb->bank + ((int64_t)jb.layer * E + e) * S;
+        ws.fit(nt);
         // phase 1: h[i][n] = silu(x_i . WgT[n]) * (x_i . WuT[n])
-        const int nblk1 = (f + kRowBlock - 1) / kRowBlock;
+        for (int i = 0; i < nt; ++i) ws.vec[i] = hb->xf.data() + (int64_t)jb.tok[t0 + i] * d;
+        const int nblk1 = f / 16;
         for (;;) {
             const int b = hb->next_block.fetch_add(1, std::memory_order_relaxed);
             if (b >= nblk1) break;
-            for (int n = b * kRowBlock; n < std::min(f, (b + 1) * kRowBlock); ++n) {
-                decode_row(hb, rec, hb->rl.off_gate, hb->rl.off_sg, n, d, rowbuf.data());
-                decode_row(hb, rec, hb->rl.off_up, hb->rl.off_su, n, d, rowbuf.data() + d);
-                for (int i = 0; i < nt; ++i) {
-                    const float* xr = hb->xf.data() + (int64_t)jb.tok[t0 + i] * d;
-                    const float g = dot_f32(xr, rowbuf.data(), d);
-                    const float u = dot_f32(xr, rowbuf.data() + d, d);
-                    hb->hbuf[(int64_t)i * f + n] = silu(g) * u;
-                }
-            }
+            const int p = b >> 1, h = b & 1;
+            half_panel_dots(hb, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.vec.data(), nt, ws.acc.data(),
+                            ws.g.data());
+            half_panel_dots(hb, rec, hb->rl.off_up, hb->rl.off_su, p, h, d, ws.vec.data(), nt, ws.acc.data(),
+                            ws.u.data());
+            for (int i = 0; i < nt; ++i)
+                for (int r = 0; r < 16; ++r)
+                    hb->hbuf[(int64_t)i * f + 16 * b + r] = silu(ws.g[i * 16 + r]) * ws.u[i * 16 + r];
         }
         barrier(hb, participants);
         // phase 2: P[t][c] += w * (h_i . WdT[c])
-        const int nblk2 = (d + kRowBlock - 1) / kRowBlock;
+        for (int i = 0; i < nt; ++i) ws.vec[i] = hb->hbuf.data() + (int64_t)i * f;
+        const int nblk2 = d / 16;
         for (;;) {
             const int b = hb->next_block.fetch_add(1, std::memory_order_relaxed);
             if (b >= nblk2) break;
-            for (int c = b * kRowBlock; c < std::min(d, (b + 1) * kRowBlock); ++c) {
-                decode_row(hb, rec, hb->rl.off_down, hb->rl.off_sd, c, f, rowbuf.data());
-                for (int i = 0; i < nt; ++i) {
-                    const float y = dot_f32(hb->hbuf.data() + (int64_t)i * f, rowbuf.data(), f);
-                    P[(int64_t)jb.tok[t0 + i] * d + c] += jb.wt[t0 + i] * y;
-                }
+            half_panel_dots(hb, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f, ws.vec.data(), nt,
+                            ws.acc.data(), ws.y.data());
+            for (int i = 0; i < nt; ++i) {
+                float* pr = P + (int64_t)jb.tok[t0 + i] * d + 16 * b;
+                const float wt = jb.wt[t0 + i];
+                for (int r = 0; r < 16; ++r) pr[r] += wt * ws.y[i * 16 + r];
             }
         }
         barrier(hb, participants);
@@ -223,7 +275,7 @@ void worker_main(HostBranch* hb, int idx, int cpu) {
         CPU_SET(cpu, &set);
         pthread_setaffinity_np(pthread_self(), sizeof(set), &set);
     }
-    std::vector<float> rowbuf(2 * (size_t)std::max(hb->sh.d_model, hb->sh.d_ff) + 64);
+    WorkerScratch ws;
     uint64_t seen = 0;
     for (;;) {
         // spin briefly, then block
@@ -238,7 +290,7 @@ void worker_main(HostBranch* hb, int idx, int cpu) {
         }
         if (hb->stop.load()) return;
         seen = hb->gen.load(std::memory_order_acquire);
-        run_job(hb, hb->nthreads + 1, rowbuf);
+        run_job(hb, hb->nthreads + 1, ws);
         hb->finished.fetch_add(1, std::memory_order_acq_rel);
     }
     (void)idx;
@@ -299,8 +351,8 @@ void run_call(HostBranch* hb, int layer, int T) {
             hb->gen.fetch_add(1, std::memory_order_acq_rel);
         }
         hb->cv.notify_all();
-        std::vector<float> rowbuf(2 * (size_t)std::max(hb->sh.d_model, hb->sh.d_ff) + 64);
-        run_job(hb, hb->nthreads + 1, rowbuf);
+        static thread_local WorkerScratch ws;
+        run_job(hb, hb->nthreads + 1, ws);
         while (hb->finished.load(std::memory_order_acquire) < hb->nthreads) _mm_pause();
         const auto ns = std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() -
                                                                              t_start).count();

@@ -13,6 +13,12 @@ documented record layout; this module decodes it independently:
          low nibble = even column) then e8m0 scales
          sg [f x d/32] | su [f x d/32] | sd [d x f/32]
 
+Code matrices and e8m0 scale matrices [rows x K] are stored in 32-row
+panels (panel p = rows 32p..32p+31, one contiguous block); inside a panel,
+unit c of row r (16 bytes of codes, or one scale byte, counted along K) sits
+at unit (c // 2) * 64 + (c % 2) * 32 + r % 32.  fp8 block scales are plain
+row-major.  ``unpanel`` undoes the interleave with one reshape/transpose.
+
 The decoded matrices are returned in the orientation of the FFN definition:
 Wg, Wu [d x f] and Wd [f x d], so that FFN(x) = (silu(x Wg) * (x Wu)) Wd.
 """
@@ -64,8 +70,21 @@ def record_size(fmt: str, d: int, f: int) -> int:
     raise ValueError(fmt)
 
 
+def unpanel(phys, rows: int, row_bytes: int, unit: int) -> np.ndarray:
+    """Physical panel-interleaved bytes -> logical row-major [rows x row_bytes]."""
+    U = row_bytes // unit                      # units per row (even)
+    a = np.asarray(phys, dtype=np.uint8).reshape(rows // 32, U // 2, 2, 32, unit)
+    # physical (panel, c // 2, c % 2, r, byte) -> logical (panel, r, c // 2, c % 2, byte)
+    return a.transpose(0, 3, 1, 2, 4).reshape(rows, row_bytes)
+
+
+def _codes(buf, off, rows, row_bytes):
+    phys = np.frombuffer(buf, dtype=np.uint8, count=rows * row_bytes, offset=off)
+    return unpanel(phys, rows, row_bytes, 16)
+
+
 def _bf16_mat(buf, off, rows, cols):
-    u = np.frombuffer(buf, dtype=np.uint16, count=rows * cols, offset=off).reshape(rows, cols)
+    u = np.ascontiguousarray(_codes(buf, off, rows, 2 * cols)).view(np.uint16)
     return bf16_to_f64(u), off + 2 * rows * cols
 
 
@@ -76,7 +95,7 @@ _E2M1_TABLE = e2m1_to_f64(np.arange(16, dtype=np.uint8))
 
 
 def _fp8_mat(codes_buf, off, rows, cols, scales):
-    c = np.frombuffer(codes_buf, dtype=np.uint8, count=rows * cols, offset=off).reshape(rows, cols)
+    c = _codes(codes_buf, off, rows, cols)
     w = _E4M3_TABLE[c]
     # each element scales by the fp32 scale of its 128x128 block
     w = w.reshape(rows // 128, 128, cols // 128, 128) * scales[:, None, :, None]
@@ -84,11 +103,11 @@ def _fp8_mat(codes_buf, off, rows, cols, scales):
 
 
 def _mx_mat(buf, off, rows, cols, soff):
-    packed = np.frombuffer(buf, dtype=np.uint8, count=rows * cols // 2, offset=off).reshape(rows, cols // 2)
+    packed = _codes(buf, off, rows, cols // 2)
     codes = np.empty((rows, cols), dtype=np.uint8)
     codes[:, 0::2] = packed & 0xF
     codes[:, 1::2] = packed >> 4
-    sc = np.frombuffer(buf, dtype=np.uint8, count=rows * cols // 32, offset=soff).reshape(rows, cols // 32)
+    sc = unpanel(np.frombuffer(buf, dtype=np.uint8, count=rows * cols // 32, offset=soff), rows, cols // 32, 1)
     w = _E2M1_TABLE[codes].reshape(rows, cols // 32, 32) * e8m0_to_f64(sc)[:, :, None]
     return w.reshape(rows, cols)
 

@@ -12,5 +12,5 @@ inverse-CDF tables, so every byte is a pure function of its key and index.
 from .configs import CONFIGS, MoEConfig, record_bytes  # noqa: F401
 from .inputs import (  # noqa: F401
     bank, record, router, tokens, ar1_tokens, zipf_routes, f32_to_bf16, bf16_to_f32,
-    normal_table_bf16, normal_table_f32, e8m0_table, FMT_CODES,
+    normal_table_bf16, normal_table_f32, e8m0_table, FMT_CODES, logical_streams,
 )

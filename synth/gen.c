@@ -18,6 +18,12 @@
  *   fp8  : WgT | WuT | WdT codes (e4m3fn, u8) | sg [f/128 x d/128] | su | sd [d/128 x f/128] (f32)
  *   mxfp4: WgT [f x d/2] | WuT | WdT [d x f/2] codes (two e2m1 per byte, low nibble = even k)
  *          | sg [f x d/32] | su | sd [d x f/32] (e8m0, u8)
+ * Every code matrix and every e8m0 scale matrix [rows x K] is stored in
+ * 32-row panels: panel p (rows 32p .. 32p+31) occupies one contiguous block,
+ * and inside it unit c of row r (a unit is 16 bytes of codes, or one scale
+ * byte; c counts along K) sits at unit index (c/2)*64 + (c%2)*32 + (r%32).
+ * The fp8 block scales stay row-major.  The logical matrices (the streams
+ * below, read row-major) do not depend on this layout.
  */
 #include <stdint.h>
 #include <string.h>
@@ -45,37 +51,64 @@ static inline uint16_t lane16(uint64_t key, int64_t i) {
     return (uint16_t)(h >> (16 * (i & 3)));
 }
 
-void sx_fill_u16(uint16_t* out, int64_t n, uint64_t key, const uint16_t* table) {
-    int64_t i = 0;
-    for (; i + 4 <= n; i += 4) {
+/* Elements [i0, i0 + n) of a stream. */
+void sx_fill_u16_at(uint16_t* out, int64_t i0, int64_t n, uint64_t key, const uint16_t* table) {
+    int64_t i = i0, end = i0 + n;
+    for (; i < end && (i & 3); ++i) out[i - i0] = table[lane16(key, i)];
+    for (; i + 4 <= end; i += 4) {
         uint64_t h = sx_mix(key + (uint64_t)(i / 4 + 1) * GOLDEN);
-        out[i] = table[h & 0xFFFF];
-        out[i + 1] = table[(h >> 16) & 0xFFFF];
-        out[i + 2] = table[(h >> 32) & 0xFFFF];
-        out[i + 3] = table[(h >> 48) & 0xFFFF];
+        out[i - i0] = table[h & 0xFFFF];
+        out[i - i0 + 1] = table[(h >> 16) & 0xFFFF];
+        out[i - i0 + 2] = table[(h >> 32) & 0xFFFF];
+        out[i - i0 + 3] = table[(h >> 48) & 0xFFFF];
     }
-    for (; i < n; ++i) out[i] = table[lane16(key, i)];
+    for (; i < end; ++i) out[i - i0] = table[lane16(key, i)];
+}
+
+void sx_fill_u16(uint16_t* out, int64_t n, uint64_t key, const uint16_t* table) {
+    sx_fill_u16_at(out, 0, n, key, table);
+}
+
+void sx_fill_u8_at(uint8_t* out, int64_t i0, int64_t n, uint64_t key, const uint8_t* table) {
+    for (int64_t i = 0; i < n; ++i) out[i] = table[lane16(key, i0 + i)];
 }
 
 void sx_fill_u8(uint8_t* out, int64_t n, uint64_t key, const uint8_t* table) {
-    for (int64_t i = 0; i < n; ++i) out[i] = table[lane16(key, i)];
+    sx_fill_u8_at(out, 0, n, key, table);
+}
+
+void sx_fill_f32_at(float* out, int64_t i0, int64_t n, uint64_t key, const float* table) {
+    for (int64_t i = 0; i < n; ++i) out[i] = table[lane16(key, i0 + i)];
 }
 
 void sx_fill_f32(float* out, int64_t n, uint64_t key, const float* table) {
-    for (int64_t i = 0; i < n; ++i) out[i] = table[lane16(key, i)];
+    sx_fill_f32_at(out, 0, n, key, table);
 }
 
-/* Uniform random bytes (each byte = two uniform e2m1 codes). */
+/* Uniform random bytes [b0, b0 + n) of a stream (each byte = two uniform e2m1 codes). */
+void sx_fill_bytes_at(uint8_t* out, int64_t b0, int64_t n, uint64_t key) {
+    int64_t i = b0, end = b0 + n;
+    while (i < end) {
+        uint64_t h = sx_mix(key + (uint64_t)(i / 8 + 1) * GOLDEN);
+        uint8_t b[8];
+        memcpy(b, &h, 8);
+        int64_t stop = (i / 8 + 1) * 8;
+        if (stop > end) stop = end;
+        for (; i < stop; ++i) out[i - b0] = b[i & 7];
+    }
+}
+
 void sx_fill_bytes(uint8_t* out, int64_t n, uint64_t key) {
-    int64_t i = 0;
-    for (; i + 8 <= n; i += 8) {
-        uint64_t h = sx_mix(key + (uint64_t)(i / 8 + 1) * GOLDEN);
-        memcpy(out + i, &h, 8);
-    }
-    if (i < n) {
-        uint64_t h = sx_mix(key + (uint64_t)(i / 8 + 1) * GOLDEN);
-        memcpy(out + i, &h, (size_t)(n - i));
-    }
+    sx_fill_bytes_at(out, 0, n, key);
+}
+
+/* Store 32 logical rows (row-major, `units` units of `unit` bytes per row,
+ * `units` even) as one panel: unit c of row r goes to unit index
+ * (c/2)*64 + (c%2)*32 + r. */
+static void panel_store(const uint8_t* src, uint8_t* dst, int64_t units, int unit) {
+    for (int r = 0; r < 32; ++r)
+        for (int64_t c = 0; c < units; ++c)
+            memcpy(dst + ((c >> 1) * 64 + (c & 1) * 32 + r) * unit, src + (r * units + c) * unit, (size_t)unit);
 }
 
 /* Harness-side e4m3fn encoder (OCP 8-bit floating point, E4M3 with no infinities,
@@ -144,42 +177,59 @@ typedef struct {
     int64_t next; pthread_mutex_t mu;
 } bank_job;
 
-/* One record.  Tensor ids: 1 gate, 2 up, 3 down; 11, 12, 13 their MX scales. */
-static void gen_record(const bank_job* j, int64_t rec, uint8_t* dst, float* scratch) {
+/* One record.  Tensor ids: 1 gate, 2 up, 3 down; 11, 12, 13 their MX scales.
+ * scratch: 128 * max(d, f) floats; codes: 128 * max(d, f) bytes. */
+static void gen_record(const bank_job* j, int64_t rec, uint8_t* dst, float* scratch, uint8_t* codes) {
     int64_t layer = (rec / j->E) + j->layer_offset, expert = rec % j->E;
     if (j->layer_alias > 0) layer %= j->layer_alias;
     int64_t d = j->d, f = j->f, fd = f * d;
     for (int t = 0; t < 3; ++t) {
         int64_t parts[4] = {j->cfg, t + 1, layer, expert};
         uint64_t key = sx_key(j->seed, parts, 4);
-        int64_t rows = (t < 2) ? f : d, cols = (t < 2) ? d : f;
+        int64_t rows = (t < 2) ? f : d, K = (t < 2) ? d : f;
         if (j->fmt == FMT_BF16) {
-            sx_fill_u16((uint16_t*)(dst + 2 * fd * t), fd, key, j->t_bf16);
+            uint8_t* m = dst + 2 * fd * t;
+            for (int64_t p = 0; p < rows / 32; ++p) {
+                sx_fill_u16_at((uint16_t*)codes, 32 * p * K, 32 * K, key, j->t_bf16);
+                panel_store(codes, m + p * 32 * K * 2, K / 8, 16);
+            }
         } else if (j->fmt == FMT_FP8) {
-            sx_fill_f32(scratch, fd, key, j->t_f32);
-            int64_t nsc = (rows / 128) * (cols / 128);
-            sx_quant_e4m3_128(scratch, rows, cols, dst + fd * t, (float*)(dst + 3 * fd + 4 * nsc * t));
+            uint8_t* m = dst + fd * t;
+            float* sc = (float*)(dst + 3 * fd + 4 * (fd / 16384) * t);
+            for (int64_t b = 0; b < rows / 128; ++b) {
+                sx_fill_f32_at(scratch, 128 * b * K, 128 * K, key, j->t_f32);
+                sx_quant_e4m3_128(scratch, 128, K, codes, sc + b * (K / 128));
+                for (int q = 0; q < 4; ++q) panel_store(codes + q * 32 * K, m + (4 * b + q) * 32 * K, K / 16, 16);
+            }
         } else {
-            sx_fill_bytes(dst + (fd / 2) * t, fd / 2, key);
+            uint8_t* m = dst + (fd / 2) * t;
             int64_t sparts[4] = {j->cfg, t + 11, layer, expert};
             uint64_t skey = sx_key(j->seed, sparts, 4);
-            sx_fill_u8(dst + 3 * fd / 2 + (fd / 32) * t, fd / 32, skey, j->t_e8m0);
+            uint8_t* s = dst + 3 * fd / 2 + (fd / 32) * t;
+            for (int64_t p = 0; p < rows / 32; ++p) {
+                sx_fill_bytes_at(codes, 32 * p * (K / 2), 32 * (K / 2), key);
+                panel_store(codes, m + p * 32 * (K / 2), K / 32, 16);
+                sx_fill_u8_at(codes, 32 * p * (K / 32), 32 * (K / 32), skey, j->t_e8m0);
+                panel_store(codes, s + p * 32 * (K / 32), K / 32, 1);
+            }
         }
     }
 }
 
 static void* bank_worker(void* arg) {
     bank_job* j = (bank_job*)arg;
-    float* scratch = NULL;
-    if (j->fmt == FMT_FP8) scratch = (float*)malloc(sizeof(float) * j->d * j->f);
+    int64_t kmax = j->d > j->f ? j->d : j->f;
+    float* scratch = (float*)malloc(sizeof(float) * 128 * kmax);
+    uint8_t* codes = (uint8_t*)malloc((size_t)(128 * kmax));
     for (;;) {
         pthread_mutex_lock(&j->mu);
         int64_t r = j->next++;
         pthread_mutex_unlock(&j->mu);
         if (r >= j->rec1) break;
-        gen_record(j, r, j->out + (r - j->rec0) * j->stride, scratch);
+        gen_record(j, r, j->out + (r - j->rec0) * j->stride, scratch, codes);
     }
     free(scratch);
+    free(codes);
     return NULL;
 }
 

@@ -40,6 +40,7 @@ def _L():
             lib.sx_fill_u16.argtypes = [vp, i64, u64, vp]
             lib.sx_fill_f32.argtypes = [vp, i64, u64, vp]
             lib.sx_fill_bytes.argtypes = [vp, i64, u64]
+            lib.sx_fill_u8.argtypes = [vp, i64, u64, vp]
             lib.sx_gen_bank.restype = ctypes.c_int
             lib.sx_gen_bank.argtypes = [ctypes.c_int, i64, i64, u64, i64, i64, i64, i64, i64, i64,
                                         vp, i64, vp, vp, vp, ctypes.c_int]
@@ -107,6 +108,40 @@ def fill_u16(n: int, k: int, table: np.ndarray) -> np.ndarray:
 def fill_f32(n: int, k: int, table: np.ndarray) -> np.ndarray:
     out = np.empty(n, dtype=np.float32)
     _L().sx_fill_f32(_ptr(out), n, ctypes.c_uint64(k), _ptr(table))
+    return out
+
+
+def fill_u8(n: int, k: int, table: np.ndarray) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint8)
+    _L().sx_fill_u8(_ptr(out), n, ctypes.c_uint64(k), _ptr(table))
+    return out
+
+
+def fill_bytes(n: int, k: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint8)
+    _L().sx_fill_bytes(_ptr(out), n, ctypes.c_uint64(k))
+    return out
+
+
+def logical_streams(cfg: MoEConfig, layer: int, expert: int):
+    """The generator's draws for one record, row-major, before any packing:
+    [(gate, up, down)] where each entry is, per format,
+      bf16 : bf16 bits [rows x K]
+      fp8  : fp32 values [rows x K] (the record holds their block-FP8 encoding)
+      mxfp4: (packed e2m1 bytes [rows x K/2], e8m0 scale bytes [rows x K/32])
+    with (rows, K) = (f, d) for gate/up and (d, f) for down."""
+    out = []
+    for t in range(3):
+        rows, K = (cfg.f, cfg.d) if t < 2 else (cfg.d, cfg.f)
+        k = key(cfg.seed, cfg.cfg_id, t + 1, layer, expert)
+        if cfg.fmt == "bf16":
+            out.append(fill_u16(rows * K, k, normal_table_bf16(0.02)).reshape(rows, K))
+        elif cfg.fmt == "fp8":
+            out.append(fill_f32(rows * K, k, normal_table_f32(0.02)).reshape(rows, K))
+        else:
+            sk = key(cfg.seed, cfg.cfg_id, t + 11, layer, expert)
+            out.append((fill_bytes(rows * K // 2, k).reshape(rows, K // 2),
+                        fill_u8(rows * K // 32, sk, e8m0_table()).reshape(rows, K // 32)))
     return out
 
 
