@@ -1,5 +1,5 @@
 // Weighted top-k combine: y[t] = sum over the token's GPU routes, j ascending,
-// of w[t,j] * Y[row(t,j)], plus the host branch's partial sum P[t] when the
+// of w[t,j] * Y[row(t,j)] (bf16 expert outputs), plus the host branch's partial sum P[t] when the
 // token has routes executed on the host; accumulated in fp32 and rounded once
 // to bf16.  The GPU and host partial outputs merge into the layer output
 // (METAL MEDIA summary, Figure 2 caption; hyper.ai summary, section 方法).
@@ -12,7 +12,7 @@ constexpr int kCombThreads = 256;
 
 __global__ void __launch_bounds__(kCombThreads)
     combine_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ route_pos,
-                   const float* __restrict__ w, const float* __restrict__ Y, const float* P, int T, int k, int d,
+                   const float* __restrict__ w, const uint16_t* __restrict__ Y, const float* P, int T, int k, int d,
                    uint16_t* __restrict__ y) {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * kCombThreads + threadIdx.x) * 4;
@@ -24,11 +24,11 @@ __global__ void __launch_bounds__(kCombThreads)
         const int p = route_pos[r];
         if (p >= 0) {
             const float wj = w[r];
-            const float4 v = *reinterpret_cast<const float4*>(Y + (int64_t)p * d + c);
-            acc.x = fmaf(wj, v.x, acc.x);
-            acc.y = fmaf(wj, v.y, acc.y);
-            acc.z = fmaf(wj, v.z, acc.z);
-            acc.w = fmaf(wj, v.w, acc.w);
+            const uint2 v = *reinterpret_cast<const uint2*>(Y + (int64_t)p * d + c);
+            acc.x = fmaf(wj, bf16lo(v.x), acc.x);
+            acc.y = fmaf(wj, bf16hi(v.x), acc.y);
+            acc.z = fmaf(wj, bf16lo(v.y), acc.z);
+            acc.w = fmaf(wj, bf16hi(v.y), acc.w);
         } else {
             const int rv = routes[r];
             host |= (rv < 0 && rv != INT32_MIN);

@@ -140,7 +140,7 @@ struct ft_cache {
     // forward scratch
     ftmoe::PlanBuffers plan;
     uint16_t* H;               // [cap x f] bf16 (GEMM path)
-    float* Y;                  // [cap x d] fp32
+    uint16_t* Y;               // [cap x d] bf16 expert outputs, one row per GPU route
     int32_t cap_gemv;          // rows served by the GEMV path
     int32_t gv_kq;             // K-parts of the gate/up GEMV
     float* gv_part;            // [2 x gv_kq x cap_gemv x f] fp32 K-part sums of g and u (GEMV path)

@@ -4,12 +4,12 @@
 // Gate/up: C[rows x 2*128] = X[rows x d] * [WgT; WuT]^T for 128 neurons at a
 // time, the gate and up halves landing in the same lanes, so the epilogue
 // writes h = silu(g) * u (bf16) without a shuffle.  Down: Y[rows x 256 cols] =
-// H[rows x f] * WdT^T in fp32.
+// H[rows x f] * WdT^T, accumulated in fp32 and stored as bf16.
 //
 // Weights are panel-ordered in the slot record: one 16-byte load per lane at
 // consecutive addresses delivers a 32-column x (two 16-byte chunk columns)
-// operand tile, which is exactly the B operand layout of
-// v_mfma_f32_32x32x16_bf16 (lane l: column l % 32, chunk column l / 32).  So
+// operand tile, which is exactly an operand layout of
+// v_mfma_f32_32x32x16_bf16 (lane l: row l % 32, chunk column l / 32).  So
 // the weights go from memory straight into registers — no LDS staging, no
 // shuffles — one K-step ahead of their use; only the activation tile (shared
 // by the four waves) is staged through double-buffered LDS, one barrier per
@@ -31,7 +31,7 @@ struct GemmArgs {
     const uint16_t* x;
     const uint16_t* Hin;   // bf16 [rows x f] (down A)
     uint16_t* Hout;        // bf16 [rows x f] (gate/up C)
-    float* Y;              // fp32 [rows x d]
+    uint16_t* Y;           // bf16 [rows x d]
     int k, d, f;
     const int32_t* meta;
     const int32_t* active_slot;
@@ -47,7 +47,8 @@ struct GemmArgs {
 
 namespace {
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu with a hardware reciprocal (1 ulp): z / (1 + e^-z)
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Per format: lane blocks (1 KiB panel runs) per K-step, and where the lane's
 // 8 bf16 of MFMA step ks sit inside the 64-wide K-step (the A side must read
@@ -228,8 +229,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
             const bf16x8_t b1 = b_frag<FMT>(br[1], ks, bs[1]);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
-                acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], b0, acc[mi][0], 0, 0, 0);
-                acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], b1, acc[mi][1], 0, 0, 0);
+                acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, af[ks & 1][mi], acc[mi][0], 0, 0, 0);
+                acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, af[ks & 1][mi], acc[mi][1], 0, 0, 0);
             }
             // the lane block this step consumed last is refilled for the next K-step
             constexpr int kDone = 4 / LBK;                  // MFMA steps per lane block
@@ -265,25 +266,72 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // epilogue
+    // Epilogue.  The MFMAs compute C^T (weights as the A operand), so lane l
+    // holds row mi*32 + l%32 and, per group q, the four consecutive columns
+    // 8q + 4(l/32) .. +3 of each 32-column panel.  The tile goes through LDS
+    // (free after the last K-step's barrier) so that every global store
+    // instruction writes whole contiguous row segments.
+    const int m = lane & 31;
+    if (GU) {
+        // h = silu(g) * u, the whole 128 x 128 bf16 tile, rows padded by 16 bytes
+        constexpr int LDH = kBN / 2 + 8;
+        uint16_t* Hs = As[0];
+        static_assert(kBM * LDH <= 2 * kBM * kLDK, "h tile must fit the A buffers");
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+        for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = mi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-            if (r < rows_valid) {
-                const int64_t p = row0 + r;
-                if (GU) {
-                    const int n = nt * (kBN / 2) + 32 * w + (lane & 31);
-                    a.Hout[p * a.f + n] = f32_to_bf16_rne(silu(acc[mi][0][v]) * acc[mi][1][v]);
-                } else {
+            for (int q = 0; q < 4; ++q) {
+                float h[4];
 #pragma unroll
-                    for (int ni = 0; ni < 2; ++ni) {
-                        const int c = nt * kBN + 64 * w + 32 * ni + (lane & 31);
-                        a.Y[p * a.d + c] = acc[mi][ni][v];
-                    }
-                }
+                for (int j = 0; j < 4; ++j) h[j] = silu(acc[mi][0][4 * q + j]) * acc[mi][1][4 * q + j];
+                uint2 o;
+                o.x = (uint32_t)f32_to_bf16_rne(h[0]) | ((uint32_t)f32_to_bf16_rne(h[1]) << 16);
+                o.y = (uint32_t)f32_to_bf16_rne(h[2]) | ((uint32_t)f32_to_bf16_rne(h[3]) << 16);
+                *reinterpret_cast<uint2*>(&Hs[(mi * 32 + m) * LDH + 32 * w + 8 * q + 4 * g]) = o;
             }
+        __syncthreads();
+        // 16 lanes per 256-byte row, 16 rows per pass
+#pragma unroll
+        for (int it = 0; it < kBM / 16; ++it) {
+            const int r = it * 16 + (tid >> 4), c = (tid & 15) * 8;
+            if (r < rows_valid)
+                *reinterpret_cast<u32x4_t*>(a.Hout + (int64_t)(row0 + r) * a.f + nt * (kBN / 2) + c) =
+                    *reinterpret_cast<const u32x4_t*>(&Hs[r * LDH + c]);
+        }
+    } else {
+        // per wave: 32 rows x 64 bf16 columns at a time, rows padded by 16 bytes
+        constexpr int LDY = 64 + 8;
+        uint16_t* Ys = As[0] + w * 32 * LDY;
+        static_assert(4 * 32 * LDY <= 2 * kBM * kLDK, "y tiles must fit the A buffers");
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint2 o;
+                    o.x = (uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q]) |
+                          ((uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 1]) << 16);
+                    o.y = (uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 2]) |
+                          ((uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 3]) << 16);
+                    *reinterpret_cast<uint2*>(&Ys[m * LDY + 32 * ni + 8 * q + 4 * g]) = o;
+                }
+            // the wave reads back what it wrote (LDS operations of a wave stay in order)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // 8 lanes per 128-byte row, 8 rows per pass
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int rr = it * 8 + (lane >> 3), c = (lane & 7) * 8;
+                const int r = mi * 32 + rr;
+                if (r < rows_valid)
+                    *reinterpret_cast<u32x4_t*>(a.Y + (int64_t)(row0 + r) * a.d + nt * kBN + 64 * w + c) =
+                        *reinterpret_cast<const u32x4_t*>(&Ys[rr * LDY + c]);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 }

@@ -13,7 +13,7 @@
 // Down: a workgroup owns (active slot, 32 output columns); its prologue forms
 // h = silu(sum g) * (sum u) for the slot's rows in LDS (the K-parts added in a
 // fixed order, rounded to bf16), then four waves split K = f and reduce
-// through LDS into Y.
+// through LDS into Y (bf16).
 // No atomics and no cross-workgroup ordering: results are deterministic.
 // Work items are counted from the device-side number of active slots, so one
 // grid serves any hit/fill mix.  The expert FFN (gate/up then down, from one
@@ -40,7 +40,7 @@ struct GemvArgs {
     int64_t S;
     int64_t off_gate, off_up, off_down, off_sg, off_su, off_sd;
     float* part;        // [2][kq][cap_g][f]: K-part sums of g (0) and u (1)
-    float* Y;           // [cap][d]
+    uint16_t* Y;        // [cap][d] bf16
     int cap_g;
     int kq;             // K-parts of gate/up
     int lbq;            // lane blocks per K-part
@@ -311,7 +311,7 @@ __global__ void __launch_bounds__(kDnWaves * 64) gemv_down_kernel(GemvArgs a) {
             float s = 0.0f;
 #pragma unroll
             for (int w = 0; w < kDnWaves; ++w) s += red[w][t][n];
-            a.Y[(int64_t)(r0 + t) * d + 32 * q + n] = s;
+            a.Y[(int64_t)(r0 + t) * d + 32 * q + n] = f32_to_bf16_rne(s);
         }
     }
 }
