@@ -179,15 +179,21 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-    const int KT = K / kBK;
-    u32x4_t br[2][LBK];
-    float bs[2];
+    const int KT = K / kBK;        // even: K is a multiple of 128
+    // Two sets of weight registers, for even and odd K-steps: step kt reads
+    // set kt % 2 and then refills it with K-step kt + 2, so every weight load
+    // has two K-steps to arrive and lands in the registers its consumer reads.
+    u32x4_t br[2][2][LBK];
+    float bs[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int j = 0; j < LBK; ++j) br[i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)j * 1024);
-        bs[i] = scale_of(i, 0);
-    }
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int j = 0; j < LBK; ++j)
+                br[s2][i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(s2 * LBK + j) * 1024);
+            bs[s2][i] = scale_of(i, s2);
+        }
     {
         u32x4_t ra[4];
 #pragma unroll
@@ -207,38 +213,38 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
     bf16x8_t af[2][4];
     read_a(af[0], As[0], 0);
 
-    // Instruction order is pinned with scheduling barriers: the compiler
-    // would otherwise sink every next-K-step load below the last MFMA.
-    for (int kt = 0; kt < KT; ++kt) {
+    // One K-step.  Instruction order is pinned with scheduling barriers: the
+    // compiler would otherwise sink every prefetch below the last MFMA.
+    // Loads stay unconditional (the last steps reload a valid K-step), so each
+    // refill lands in the registers its consumer reads.
+    auto kstep = [&](int kt, u32x4_t (&brs)[2][LBK], float (&bss)[2]) {
         const bool more = kt + 1 < KT;
-        // next K-step (the last step reloads itself: loads stay unconditional,
-        // so each refill lands in the registers its consumer reads)
-        const int kn = more ? kt + 1 : kt;
+        const int kn = more ? kt + 1 : kt;                // A tile staged for the next step
+        const int kw = kt + 2 < KT ? kt + 2 : KT - 1;     // weights refilled for two steps ahead
         const uint16_t* Ab = As[kt & 1];
         u32x4_t ra[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(ap[i] + kn * kBK);
         float bs_next[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) bs_next[i] = scale_of(i, kn);
+        for (int i = 0; i < 2; ++i) bs_next[i] = scale_of(i, kw);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             if (ks < 3) read_a(af[(ks + 1) & 1], Ab, ks + 1);
-            const bf16x8_t b0 = b_frag<FMT>(br[0], ks, bs[0]);
-            const bf16x8_t b1 = b_frag<FMT>(br[1], ks, bs[1]);
+            const bf16x8_t b0 = b_frag<FMT>(brs[0], ks, bss[0]);
+            const bf16x8_t b1 = b_frag<FMT>(brs[1], ks, bss[1]);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
                 acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, af[ks & 1][mi], acc[mi][0], 0, 0, 0);
                 acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, af[ks & 1][mi], acc[mi][1], 0, 0, 0);
             }
-            // the lane block this step consumed last is refilled for the next K-step
-            constexpr int kDone = 4 / LBK;                  // MFMA steps per lane block
+            constexpr int kDone = 4 / LBK;                // MFMA steps per lane block
             if ((ks % kDone) == kDone - 1) {
                 const int j = ks / kDone;
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    br[i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(kn * LBK + j) * 1024);
+                    brs[i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(kw * LBK + j) * 1024);
             }
             // order inside the step: the next step's LDS reads interleaved with
             // the first MFMAs, then the rest, then the refill loads
@@ -255,8 +261,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);           // global loads
             __builtin_amdgcn_sched_barrier(0);
         }
-        bs[0] = bs_next[0];
-        bs[1] = bs_next[1];
+        bss[0] = bs_next[0];
+        bss[1] = bs_next[1];
         if (more) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(&As[(kt + 1) & 1][a_st + 32 * i * kLDK]) = ra[i];
@@ -264,6 +270,10 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
         __syncthreads();
         read_a(af[0], As[(kt + 1) & 1], 0);
         __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kt = 0; kt < KT; kt += 2) {
+        kstep(kt, br[0], bs[0]);
+        kstep(kt + 1, br[1], bs[1]);
     }
 
     // Epilogue.  The MFMAs compute C^T (weights as the A operand), so lane l

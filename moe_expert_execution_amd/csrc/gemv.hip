@@ -6,7 +6,7 @@
 // block" of 1 KiB), so every weight load of these kernels is a 1 KiB
 // contiguous run.
 //
-// Gate/up: a workgroup owns (active slot, 32-neuron panel, K-part): its eight
+// Gate/up: a workgroup owns (active slot, 32-neuron panel, K-part): its four
 // waves split the K-part's lane blocks of the gate and the up panel, dot them
 // with the token rows (staged once in LDS), and add the wave partials in a
 // fixed order; the K-part sums of g and u go to a small fp32 buffer.
@@ -24,10 +24,12 @@
 
 namespace ftmoe {
 
-constexpr int kGuWaves = 8;          // waves per gate/up workgroup
+constexpr int kGuWaves = 4;          // waves per gate/up workgroup
 constexpr int kDnWaves = 4;          // waves per down workgroup
-constexpr int kBatch = 8;            // lane blocks per matrix held in flight per lane
+constexpr int kBatch = 8;            // gate/up: lane blocks per matrix held in flight per lane
+constexpr int kDnBatch = 16;         // down: lane blocks held in flight per lane
 constexpr int kMaxSpan = 4096;       // K elements of x staged per gate/up workgroup
+constexpr int kMaxKq = 8;            // most K-parts of gate/up
 
 struct GemvArgs {
     const uint16_t* x;
@@ -46,22 +48,24 @@ struct GemvArgs {
     int lbq;            // lane blocks per K-part
 };
 
-// K-parts of the gate/up GEMV for a shape: about eight lane blocks per wave
-// and matrix, and at most kMaxSpan activations staged per workgroup.
+// K-parts of the gate/up GEMV for a shape: at most kBatch lane blocks per wave
+// and matrix (all in flight at once), and at most kMaxSpan activations staged
+// per workgroup.
 int gemv_kparts(const ft_shape& s) {
     const int64_t rb = s.fmt == FT_FMT_BF16 ? 2ll * s.d_model : s.fmt == FT_FMT_FP8_B128 ? s.d_model : s.d_model / 2;
     const int64_t lb = rb / 32;
-    int kq = (int)(lb / (kGuWaves * kBatch));
+    int kq = (int)((lb + kGuWaves * kBatch - 1) / (kGuWaves * kBatch));
     const int need = (int)((s.d_model + kMaxSpan - 1) / kMaxSpan);
     if (kq < need) kq = need;
     if (kq < 1) kq = 1;
-    if (kq > 8) kq = 8;
+    if (kq > kMaxKq) kq = kMaxKq;
     return kq;
 }
 
 namespace {
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu with a hardware reciprocal (1 ulp): z / (1 + e^-z)
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 __device__ __forceinline__ float swap_halves_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 
@@ -119,7 +123,9 @@ __device__ __forceinline__ float lane_scale(const uint8_t* rec, int64_t off_s, i
 template <int FMT, int TG>
 __global__ void __launch_bounds__(kGuWaves * 64) gemv_gateup_kernel(GemvArgs a) {
     constexpr int EPC = WF<FMT>::EPC;
-    constexpr int XW = EPC / 2;            // packed bf16 pairs of x per chunk
+    constexpr int XW = EPC / 2;                                  // packed bf16 pairs of x per chunk
+    constexpr int XPT = TG * (kMaxSpan / 8) / (kGuWaves * 64);    // 16-byte x chunks per thread
+    constexpr int NB = TG == 1 ? kBatch : kBatch / 2;            // lane blocks per matrix in flight
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [TG][span]
     __shared__ float red[kGuWaves][2][TG][32];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, tid = threadIdx.x;
@@ -130,10 +136,13 @@ __global__ void __launch_bounds__(kGuWaves * 64) gemv_gateup_kernel(GemvArgs a) 
     const int rest = item / a.kq;
     const int p = rest % P;
     const int ai = rest / P;
-    if (ai >= a.meta[0]) return;
+    // independent metadata loads (ai is below the buffers' capacity)
+    const int n_active = a.meta[0];
     const int slot = a.active_slot[ai];
     const int r0 = a.seg[ai];
-    int nrows = a.seg[ai + 1] - r0;
+    const int r1 = a.seg[ai + 1];
+    if (ai >= n_active) return;
+    int nrows = r1 - r0;
     nrows = nrows > TG ? TG : nrows;
     const uint8_t* rec = a.pool + (int64_t)slot * a.S;
     const int64_t rowb = WF<FMT>::row_bytes(d);
@@ -146,40 +155,64 @@ __global__ void __launch_bounds__(kGuWaves * 64) gemv_gateup_kernel(GemvArgs a) 
     const uint8_t* gp = rec + a.off_gate + (int64_t)p * 32 * rowb + lane * 16;
     const uint8_t* up = rec + a.off_up + (int64_t)p * 32 * rowb + lane * 16;
 
-    // first batch of weight loads before anything else
-    u32x4_t wg[kBatch], wu[kBatch];
+    // the token rows' activations of this K-part (one call of T = 1 has the
+    // single row x[0]; otherwise the sorted rows' tokens come from perm)
+    const int k0 = 2 * jq0 * EPC;
+    const int span = 2 * nq * EPC;
+    const int c8n = span >> 3;
+    const uint16_t* xr[TG];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
+    for (int t = 0; t < TG; ++t) {
+        if (TG == 1) {
+            xr[t] = a.x + k0;
+        } else {
+            const int rr = r0 + (t < nrows ? t : nrows - 1);
+            xr[t] = a.x + (int64_t)(a.perm[rr] / a.k) * d + k0;
+        }
+    }
+    u32x4_t xv[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int q = tid + kGuWaves * 64 * i;
+        if (q < TG * c8n) {
+            const int t = q / c8n, c8 = q - t * c8n;
+            xv[i] = *reinterpret_cast<const u32x4_t*>(xr[t] + 8 * c8);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // then the weights: the whole K range of this wave in flight at once
+    u32x4_t wg[NB], wu[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
         if (jw0 + i < jw1) {
             wg[i] = *reinterpret_cast<const u32x4_t*>(gp + (int64_t)(jw0 + i) * 1024);
             wu[i] = *reinterpret_cast<const u32x4_t*>(up + (int64_t)(jw0 + i) * 1024);
         }
-
-    // the token rows' activations of this K-part into LDS
-    const int k0 = 2 * jq0 * EPC;
-    const int span = 2 * nq * EPC;
-    for (int q = tid; q < TG * (span >> 3); q += kGuWaves * 64) {
-        const int t = q / (span >> 3), c8 = q - t * (span >> 3);
-        const int rr = r0 + (t < nrows ? t : nrows - 1);
-        const uint16_t* xr = a.x + (int64_t)(a.perm[rr] / a.k) * d + k0;
-        *reinterpret_cast<u32x4_t*>(&xs[t * span + 8 * c8]) = *reinterpret_cast<const u32x4_t*>(xr + 8 * c8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int q = tid + kGuWaves * 64 * i;
+        if (q < TG * c8n) {
+            const int t = q / c8n, c8 = q - t * c8n;
+            *reinterpret_cast<u32x4_t*>(&xs[t * span + 8 * c8]) = xv[i];
+        }
     }
     __syncthreads();
 
     float ag[TG], au[TG];
 #pragma unroll
     for (int t = 0; t < TG; ++t) ag[t] = au[t] = 0.0f;
-    for (int j0 = jw0; j0 < jw1; j0 += kBatch) {
+    for (int j0 = jw0; j0 < jw1; j0 += NB) {
         if (j0 != jw0) {
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i)
+            for (int i = 0; i < NB; ++i)
                 if (j0 + i < jw1) {
                     wg[i] = *reinterpret_cast<const u32x4_t*>(gp + (int64_t)(j0 + i) * 1024);
                     wu[i] = *reinterpret_cast<const u32x4_t*>(up + (int64_t)(j0 + i) * 1024);
                 }
         }
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
+        for (int i = 0; i < NB; ++i) {
             const int j = j0 + i;
             if (j < jw1) {
                 const float sg = lane_scale<FMT>(rec, a.off_sg, p, j, lane, d);
@@ -227,6 +260,7 @@ __global__ void __launch_bounds__(kGuWaves * 64) gemv_gateup_kernel(GemvArgs a) 
 template <int FMT, int TG>
 __global__ void __launch_bounds__(kDnWaves * 64) gemv_down_kernel(GemvArgs a) {
     constexpr int EPC = WF<FMT>::EPC;
+    constexpr int HPT = 4;                 // h elements per thread whose K-part sums load before the weights
     extern __shared__ __attribute__((aligned(16))) uint16_t hs[];   // [TG][f] bf16
     __shared__ float red[kDnWaves][TG][32];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, tid = threadIdx.x;
@@ -234,10 +268,12 @@ __global__ void __launch_bounds__(kDnWaves * 64) gemv_down_kernel(GemvArgs a) {
     const int Q = d >> 5;
     const int q = blockIdx.x % Q;
     const int ai = blockIdx.x / Q;
-    if (ai >= a.meta[0]) return;
+    const int n_active = a.meta[0];
     const int slot = a.active_slot[ai];
     const int r0 = a.seg[ai];
-    int nrows = a.seg[ai + 1] - r0;
+    const int r1 = a.seg[ai + 1];
+    if (ai >= n_active) return;
+    int nrows = r1 - r0;
     nrows = nrows > TG ? TG : nrows;
     const uint8_t* rec = a.pool + (int64_t)slot * a.S;
     const int64_t rowb = WF<FMT>::row_bytes(f);
@@ -246,14 +282,46 @@ __global__ void __launch_bounds__(kDnWaves * 64) gemv_down_kernel(GemvArgs a) {
     const int jw1 = ((wid + 1) * LB) / kDnWaves;
     const uint8_t* dp = rec + a.off_down + (int64_t)q * 32 * rowb + lane * 16;
 
-    u32x4_t wd[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-        if (jw0 + i < jw1) wd[i] = *reinterpret_cast<const u32x4_t*>(dp + (int64_t)(jw0 + i) * 1024);
-
     // h = silu(g) * u (bf16, as the prefill path keeps it) for the slot's
-    // rows, the K-parts added in order
-    for (int i = tid; i < TG * f; i += kDnWaves * 64) {
+    // rows, the K-parts added in order.  The first HPT elements' K-part sums
+    // are loaded before the weights so that forming h waits for them only.
+    const int nh = TG * f;
+    float pg[HPT], pu[HPT];
+#pragma unroll
+    for (int e = 0; e < HPT; ++e) {
+        pg[e] = pu[e] = 0.0f;
+        const int i = tid + kDnWaves * 64 * e;
+        const int t = i / f, n = i - t * f;
+        if (i < nh && t < nrows) {
+            // all K-part loads issued together (a runtime-bounded loop would
+            // wait for each pair in turn)
+            float vg[kMaxKq], vu[kMaxKq];
+#pragma unroll
+            for (int kk = 0; kk < kMaxKq; ++kk)
+                if (kk < a.kq) {
+                    vg[kk] = a.part[((int64_t)kk * a.cap_g + r0 + t) * f + n];
+                    vu[kk] = a.part[(((int64_t)a.kq + kk) * a.cap_g + r0 + t) * f + n];
+                }
+#pragma unroll
+            for (int kk = 0; kk < kMaxKq; ++kk)
+                if (kk < a.kq) {
+                    pg[e] += vg[kk];
+                    pu[e] += vu[kk];
+                }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t wd[kDnBatch];
+#pragma unroll
+    for (int i = 0; i < kDnBatch; ++i)
+        if (jw0 + i < jw1) wd[i] = *reinterpret_cast<const u32x4_t*>(dp + (int64_t)(jw0 + i) * 1024);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < HPT; ++e) {
+        const int i = tid + kDnWaves * 64 * e;
+        if (i < nh) hs[i] = f32_to_bf16_rne(silu(pg[e]) * pu[e]);
+    }
+    for (int i = tid + kDnWaves * 64 * HPT; i < nh; i += kDnWaves * 64) {
         const int t = i / f, n = i - t * f;
         float h = 0.0f;
         if (t < nrows) {
@@ -271,14 +339,14 @@ __global__ void __launch_bounds__(kDnWaves * 64) gemv_down_kernel(GemvArgs a) {
     float acc[TG];
 #pragma unroll
     for (int t = 0; t < TG; ++t) acc[t] = 0.0f;
-    for (int j0 = jw0; j0 < jw1; j0 += kBatch) {
+    for (int j0 = jw0; j0 < jw1; j0 += kDnBatch) {
         if (j0 != jw0) {
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i)
+            for (int i = 0; i < kDnBatch; ++i)
                 if (j0 + i < jw1) wd[i] = *reinterpret_cast<const u32x4_t*>(dp + (int64_t)(j0 + i) * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
+        for (int i = 0; i < kDnBatch; ++i) {
             const int j = j0 + i;
             if (j < jw1) {
                 const float sc = lane_scale<FMT>(rec, a.off_sd, q, j, lane, f);
