@@ -129,7 +129,8 @@ def decode_bench(args):
             "avg_launch_us": ms_gu / max(n_gu, 1) * 1e3, "launches": n_gu,
         },
         "decode_kernels": {
-            "gemv_down": {"achieved_gbs": dn_gbs, "avg_launch_us": ms_dn / max(n_dn, 1) * 1e3},
+            # per layer call (a call may launch a SwiGLU finalize kernel before the down GEMV)
+            "gemv_down": {"achieved_gbs": dn_gbs, "avg_launch_us": ms_dn / max(n_gu, 1) * 1e3},
             "gemv_pair": {"achieved_gbs": both_gbs, "frac": both_gbs / HBM_PEAK_GBS},
             "gpu_experts_per_layer_step": experts / max(n_gu, 1),
         },
@@ -256,6 +257,111 @@ def prefill_bench(args):
     bank.close()
     return res
 
+def expert_bytes(fmt, d, f):
+    """Algorithmic bytes of one expert's gate+up banks and of its down bank (codes and scales)."""
+    if fmt == "bf16":
+        return 2 * f * d * 2, d * f * 2
+    if fmt == "fp8":
+        sc = (f // 128) * (d // 128) * 4
+        return 2 * f * d + 2 * sc, d * f + sc
+    return 2 * f * d // 2 + 2 * f * d // 32, d * f // 2 + d * f // 32
+
+
+def formats_bench(args):
+    """Block-FP8 and MXFP4 layers with one layer resident (STREAMED buffer 0, 2E slots): the decode GEMV at
+    T = 1 over fresh tokens (each call routes to other experts, so successive calls read different records
+    and the working set is the whole layer, far above the Infinity Cache), and the grouped GEMM at the
+    prefill token counts of each configuration."""
+    import numpy as np
+    import torch
+
+    import moe_expert_execution_amd as M
+    import synth
+    from moe_expert_execution_amd.tensors import PinnedBank, SlotCache
+
+    out = {}
+    stream = torch.cuda.current_stream().cuda_stream
+    for name, Ts in (("fp8", (64, 2048)), ("mxfp4", (4096,))):
+        cfg = synth.CONFIGS[name].with_(layers=1, layer_alias=0)
+        E, k, d, f, S = cfg.E, cfg.k, cfg.d, cfg.f, cfg.S
+        t = time.time()
+        bank = PinnedBank(E * S)
+        synth.bank(cfg, out=bank.records(S), nthreads=min(16, len(os.sched_getaffinity(0))))
+        log(f"{name} bank {E * S / 1e9:.1f} GB in {time.time() - t:.1f}s")
+        Tmax = max(Ts)
+        sc = SlotCache(1, E, k, d, f, name, bank.ptr, 2 * E, Tmax, cfg.bp_mbps, cfg.bh_mbps)
+        h, shp = sc.handle, sc.shape
+        wr = torch.from_numpy(synth.router(cfg, 0).view(np.int16)).cuda()
+        y = torch.empty((Tmax, d), dtype=torch.int16, device="cuda")
+        gu_b, dn_b = expert_bytes(name, d, f)
+        res = {"workload": f"one {name} layer resident: d={d}, E={E}, top-{k}, f={f}"}
+
+        def routed(T, tag):
+            x = torch.from_numpy(synth.tokens(cfg, T, tag).view(np.int16)).cuda()
+            ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+            M.ft_moe_route(shp, x.data_ptr(), wr.data_ptr(), T, ids.data_ptr(), w.data_ptr(), stream)
+            return x, ids, w
+
+        def fwd(x, ids, w, T):
+            M.ft_moe_forward(h, 0, M.FT_MODE_STREAMED, x.data_ptr(), ids.data_ptr(), w.data_ptr(), T, y.data_ptr(),
+                             stream)
+
+        # decode GEMV: 96 single tokens, each routed afresh
+        x1, ids1, w1 = routed(96, 11)
+        fwd(x1[:1], ids1[:1], w1[:1], 1)          # loads the layer into buffer 0
+        torch.cuda.synchronize()
+        M.ft_cache_set_timing(h, True)
+        for i in range(96):
+            fwd(x1[i:i + 1], ids1[i:i + 1], w1[i:i + 1], 1)
+        torch.cuda.synchronize()
+        tm = M.ft_cache_timing(h)
+        n = max(tm.launches[M.FT_K_GEMV_GU], 1)
+        ex = tm.gemv_experts / n
+        gu_us = tm.ms[M.FT_K_GEMV_GU] / n * 1e3
+        dn_us = tm.ms[M.FT_K_GEMV_DOWN] / n * 1e3
+        res["gemv_T1"] = {"experts_per_launch": ex,
+                          "gateup_us": gu_us, "gateup_gbs": ex * gu_b / gu_us / 1e3,
+                          "gateup_frac": ex * gu_b / gu_us / 1e3 / HBM_PEAK_GBS,
+                          "down_us": dn_us, "down_gbs": ex * dn_b / dn_us / 1e3}
+        M.ft_cache_set_timing(h, False)
+        # grouped GEMM
+        for T in Ts:
+            x, ids, w = routed(T, 12)
+            fwd(x, ids, w, T)
+            torch.cuda.synchronize()
+            reps = 10
+            M.ft_cache_set_timing(h, True)
+            for _ in range(reps):
+                fwd(x, ids, w, T)
+            torch.cuda.synchronize()
+            tm = M.ft_cache_timing(h)
+            rows = tm.gemm_rows / reps
+            act = tm.gemm_experts / reps
+            ms_gu = tm.ms[M.FT_K_GEMM_GU] / reps
+            ms_dn = tm.ms[M.FT_K_GEMM_DOWN] / reps
+            fl = 2.0 * rows * 3 * d * f
+            by = act * (gu_b + dn_b)
+            ms = ms_gu + ms_dn
+            tf = fl / (ms / 1e3) / 1e12
+            gbs = by / (ms / 1e3) / 1e9
+            t_roof = max(fl / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), by / (HBM_PEAK_GBS * 1e9)) * 1e3
+            res[f"gemm_T{T}"] = {"rows": rows, "active_experts": act, "gateup_ms": ms_gu, "down_ms": ms_dn,
+                                 "tflops": tf, "mfma_frac_bf16": tf / MFMA_PEAK_TFLOPS["bf16"],
+                                 "weight_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                                 "t_roofline_ms": t_roof, "roofline_frac": t_roof / ms}
+            M.ft_cache_set_timing(h, False)
+        st = M.ft_cache_stats(h)
+        assert st.error_flags == 0
+        log(f"{name}: GEMV T=1 gate/up {res['gemv_T1']['gateup_gbs']:.0f} GB/s "
+            f"({res['gemv_T1']['gateup_frac']:.1%}), " +
+            ", ".join(f"GEMM T={T} {res[f'gemm_T{T}']['tflops']:.0f} TFLOP/s / {res[f'gemm_T{T}']['weight_gbs']:.0f}"
+                      f" GB/s ({res[f'gemm_T{T}']['roofline_frac']:.1%} of roofline time)" for T in Ts))
+        out[name] = res
+        sc.close()
+        bank.close()
+    return out
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -266,6 +372,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (kernel work)")
+    ap.add_argument("--formats", action="store_true",
+                    help="only run the block-FP8 and MXFP4 kernel measurements (one resident layer each)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -290,6 +398,9 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n}))
         return
 
+    if args.formats:
+        print(json.dumps({"formats": formats_bench(args)}), flush=True)
+        return
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_bench(args)}), flush=True)
         return

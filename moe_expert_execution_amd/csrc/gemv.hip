@@ -42,6 +42,7 @@ struct GemvArgs {
     int64_t S;
     int64_t off_gate, off_up, off_down, off_sg, off_su, off_sd;
     float* part;        // [2][kq][cap_g][f]: K-part sums of g (0) and u (1)
+    uint16_t* hb;       // [cap_g][f] bf16 h, when formed once by the finalize kernel
     uint16_t* Y;        // [cap][d] bf16
     int cap_g;
     int kq;             // K-parts of gate/up
@@ -51,6 +52,15 @@ struct GemvArgs {
 // K-parts of the gate/up GEMV for a shape: at most kBatch lane blocks per wave
 // and matrix (all in flight at once), and at most kMaxSpan activations staged
 // per workgroup.
+// Whether h is formed once by a separate kernel rather than in every down
+// workgroup's prologue: when the down workgroups' repeated reads of the K-part
+// sums (d/32 workgroups x 2 kq f fp32 per expert) would exceed the down
+// weights themselves (d f bytes-per-element).
+bool gemv_finalize(const ft_shape& s, int kq) {
+    const double bpe = s.fmt == FT_FMT_BF16 ? 2.0 : s.fmt == FT_FMT_FP8_B128 ? 1.0 : 0.5;
+    return kq >= 4.0 * bpe;
+}
+
 int gemv_kparts(const ft_shape& s) {
     const int64_t rb = s.fmt == FT_FMT_BF16 ? 2ll * s.d_model : s.fmt == FT_FMT_FP8_B128 ? s.d_model : s.d_model / 2;
     const int64_t lb = rb / 32;
@@ -257,7 +267,49 @@ __global__ void __launch_bounds__(kGuWaves * 64) gemv_gateup_kernel(GemvArgs a) 
     }
 }
 
-template <int FMT, int TG>
+// h = silu(sum g) * (sum u) in bf16 for every GPU row, the K-parts added in
+// order; 1,024 elements of one active slot's rows per workgroup.
+template <int TG>
+__global__ void __launch_bounds__(256) gemv_swiglu_kernel(GemvArgs a) {
+    const int f = a.f;
+    const int nch = (TG * f + 1023) / 1024;
+    const int ai = blockIdx.x / nch, ch = blockIdx.x - ai * nch;
+    const int n_active = a.meta[0];
+    const int r0 = a.seg[ai];
+    const int r1 = a.seg[ai + 1];
+    if (ai >= n_active) return;
+    int nrows = r1 - r0;
+    nrows = nrows > TG ? TG : nrows;
+    float vg[4][kMaxKq], vu[4][kMaxKq];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = ch * 1024 + e * 256 + threadIdx.x;
+        const int t = i / f, n = i - t * f;
+#pragma unroll
+        for (int kk = 0; kk < kMaxKq; ++kk)
+            if (kk < a.kq && t < nrows) {
+                vg[e][kk] = a.part[((int64_t)kk * a.cap_g + r0 + t) * f + n];
+                vu[e][kk] = a.part[(((int64_t)a.kq + kk) * a.cap_g + r0 + t) * f + n];
+            }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = ch * 1024 + e * 256 + threadIdx.x;
+        const int t = i / f, n = i - t * f;
+        if (t < nrows) {
+            float g = 0.0f, u = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < kMaxKq; ++kk)
+                if (kk < a.kq) {
+                    g += vg[e][kk];
+                    u += vu[e][kk];
+                }
+            a.hb[(int64_t)(r0 + t) * f + n] = f32_to_bf16_rne(silu(g) * u);
+        }
+    }
+}
+
+template <int FMT, int TG, bool FIN>
 __global__ void __launch_bounds__(kDnWaves * 64) gemv_down_kernel(GemvArgs a) {
     constexpr int EPC = WF<FMT>::EPC;
     constexpr int HPT = 4;                 // h elements per thread whose K-part sums load before the weights
@@ -281,58 +333,82 @@ __global__ void __launch_bounds__(kDnWaves * 64) gemv_down_kernel(GemvArgs a) {
     const int jw0 = (wid * LB) / kDnWaves;
     const int jw1 = ((wid + 1) * LB) / kDnWaves;
     const uint8_t* dp = rec + a.off_down + (int64_t)q * 32 * rowb + lane * 16;
-
-    // h = silu(g) * u (bf16, as the prefill path keeps it) for the slot's
-    // rows, the K-parts added in order.  The first HPT elements' K-part sums
-    // are loaded before the weights so that forming h waits for them only.
-    const int nh = TG * f;
-    float pg[HPT], pu[HPT];
-#pragma unroll
-    for (int e = 0; e < HPT; ++e) {
-        pg[e] = pu[e] = 0.0f;
-        const int i = tid + kDnWaves * 64 * e;
-        const int t = i / f, n = i - t * f;
-        if (i < nh && t < nrows) {
-            // all K-part loads issued together (a runtime-bounded loop would
-            // wait for each pair in turn)
-            float vg[kMaxKq], vu[kMaxKq];
-#pragma unroll
-            for (int kk = 0; kk < kMaxKq; ++kk)
-                if (kk < a.kq) {
-                    vg[kk] = a.part[((int64_t)kk * a.cap_g + r0 + t) * f + n];
-                    vu[kk] = a.part[(((int64_t)a.kq + kk) * a.cap_g + r0 + t) * f + n];
-                }
-#pragma unroll
-            for (int kk = 0; kk < kMaxKq; ++kk)
-                if (kk < a.kq) {
-                    pg[e] += vg[kk];
-                    pu[e] += vu[kk];
-                }
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
     u32x4_t wd[kDnBatch];
+
+    // h (bf16, as the prefill path keeps it) for the slot's rows.  FIN: it was
+    // formed by the finalize kernel and is copied in; otherwise it is formed
+    // here from the K-part sums, added in order.  Either way its loads are
+    // issued before the weights, so building h waits for them only.
+    const int nh = TG * f;
+    if constexpr (FIN) {
+        constexpr int CPT = TG * (8192 / 8) / (kDnWaves * 64);    // 16-byte h chunks per thread, f <= 8192
+        u32x4_t hv[CPT];
 #pragma unroll
-    for (int i = 0; i < kDnBatch; ++i)
-        if (jw0 + i < jw1) wd[i] = *reinterpret_cast<const u32x4_t*>(dp + (int64_t)(jw0 + i) * 1024);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int e = 0; e < HPT; ++e) {
-        const int i = tid + kDnWaves * 64 * e;
-        if (i < nh) hs[i] = f32_to_bf16_rne(silu(pg[e]) * pu[e]);
-    }
-    for (int i = tid + kDnWaves * 64 * HPT; i < nh; i += kDnWaves * 64) {
-        const int t = i / f, n = i - t * f;
-        float h = 0.0f;
-        if (t < nrows) {
-            float g = 0.0f, u = 0.0f;
-            for (int kk = 0; kk < a.kq; ++kk) {
-                g += a.part[((int64_t)kk * a.cap_g + r0 + t) * f + n];
-                u += a.part[(((int64_t)a.kq + kk) * a.cap_g + r0 + t) * f + n];
-            }
-            h = silu(g) * u;
+        for (int e = 0; e < CPT; ++e) {
+            const int c8 = tid + kDnWaves * 64 * e;
+            const int t = (8 * c8) / f;
+            hv[e] = u32x4_t{0u, 0u, 0u, 0u};
+            if (8 * c8 < nh && t < nrows)
+                hv[e] = *reinterpret_cast<const u32x4_t*>(a.hb + (int64_t)(r0 + t) * f + (8 * c8 - t * f));
         }
-        hs[i] = f32_to_bf16_rne(h);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kDnBatch; ++i)
+            if (jw0 + i < jw1) wd[i] = *reinterpret_cast<const u32x4_t*>(dp + (int64_t)(jw0 + i) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            const int c8 = tid + kDnWaves * 64 * e;
+            if (8 * c8 < nh) *reinterpret_cast<u32x4_t*>(&hs[8 * c8]) = hv[e];
+        }
+    } else {
+        float pg[HPT], pu[HPT];
+#pragma unroll
+        for (int e = 0; e < HPT; ++e) {
+            pg[e] = pu[e] = 0.0f;
+            const int i = tid + kDnWaves * 64 * e;
+            const int t = i / f, n = i - t * f;
+            if (i < nh && t < nrows) {
+                // all K-part loads issued together (a runtime-bounded loop would
+                // wait for each pair in turn)
+                float vg[kMaxKq], vu[kMaxKq];
+#pragma unroll
+                for (int kk = 0; kk < kMaxKq; ++kk)
+                    if (kk < a.kq) {
+                        vg[kk] = a.part[((int64_t)kk * a.cap_g + r0 + t) * f + n];
+                        vu[kk] = a.part[(((int64_t)a.kq + kk) * a.cap_g + r0 + t) * f + n];
+                    }
+#pragma unroll
+                for (int kk = 0; kk < kMaxKq; ++kk)
+                    if (kk < a.kq) {
+                        pg[e] += vg[kk];
+                        pu[e] += vu[kk];
+                    }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kDnBatch; ++i)
+            if (jw0 + i < jw1) wd[i] = *reinterpret_cast<const u32x4_t*>(dp + (int64_t)(jw0 + i) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < HPT; ++e) {
+            const int i = tid + kDnWaves * 64 * e;
+            if (i < nh) hs[i] = f32_to_bf16_rne(silu(pg[e]) * pu[e]);
+        }
+        for (int i = tid + kDnWaves * 64 * HPT; i < nh; i += kDnWaves * 64) {
+            const int t = i / f, n = i - t * f;
+            float h = 0.0f;
+            if (t < nrows) {
+                float g = 0.0f, u = 0.0f;
+                for (int kk = 0; kk < a.kq; ++kk) {
+                    g += a.part[((int64_t)kk * a.cap_g + r0 + t) * f + n];
+                    u += a.part[(((int64_t)a.kq + kk) * a.cap_g + r0 + t) * f + n];
+                }
+                h = silu(g) * u;
+            }
+            hs[i] = f32_to_bf16_rne(h);
+        }
     }
     __syncthreads();
 
@@ -385,7 +461,7 @@ __global__ void __launch_bounds__(kDnWaves * 64) gemv_down_kernel(GemvArgs a) {
 }
 
 template <int FMT, int TG>
-hipError_t launch_fmt(const GemvArgs& a, int max_active, Timing* tm, hipStream_t st) {
+hipError_t launch_fmt(const GemvArgs& a, int max_active, bool fin, Timing* tm, hipStream_t st) {
     const size_t xs_bytes = (size_t)TG * 2 * a.lbq * WF<FMT>::EPC * sizeof(uint16_t);
     const size_t hs_bytes = (size_t)TG * a.f * sizeof(uint16_t);
     const unsigned g1 = (unsigned)(max_active * (a.f / 32) * a.kq);
@@ -393,9 +469,18 @@ hipError_t launch_fmt(const GemvArgs& a, int max_active, Timing* tm, hipStream_t
     TimedLaunch t1 = timing_launch(tm, FT_K_GEMV_GU);
     hipExtLaunchKernelGGL((gemv_gateup_kernel<FMT, TG>), dim3(g1), dim3(kGuWaves * 64), xs_bytes, st, t1.start,
                           t1.stop, 0, a);
-    TimedLaunch t2 = timing_launch(tm, FT_K_GEMV_DOWN);
-    hipExtLaunchKernelGGL((gemv_down_kernel<FMT, TG>), dim3(g2), dim3(kDnWaves * 64), hs_bytes, st, t2.start,
-                          t2.stop, 0, a);
+    if (fin) {
+        TimedLaunch t3 = timing_launch(tm, FT_K_GEMV_DOWN);
+        const unsigned g3 = (unsigned)(max_active * ((TG * a.f + 1023) / 1024));
+        hipExtLaunchKernelGGL((gemv_swiglu_kernel<TG>), dim3(g3), dim3(256), 0, st, t3.start, t3.stop, 0, a);
+        TimedLaunch t2 = timing_launch(tm, FT_K_GEMV_DOWN);
+        hipExtLaunchKernelGGL((gemv_down_kernel<FMT, TG, true>), dim3(g2), dim3(kDnWaves * 64), hs_bytes, st,
+                              t2.start, t2.stop, 0, a);
+    } else {
+        TimedLaunch t2 = timing_launch(tm, FT_K_GEMV_DOWN);
+        hipExtLaunchKernelGGL((gemv_down_kernel<FMT, TG, false>), dim3(g2), dim3(kDnWaves * 64), hs_bytes, st,
+                              t2.start, t2.stop, 0, a);
+    }
     return hipGetLastError();
 }
 
@@ -421,6 +506,7 @@ hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     a.off_su = c->rl.off_su;
     a.off_sd = c->rl.off_sd;
     a.part = c->gv_part;
+    a.hb = c->H;
     a.Y = c->Y;
     a.cap_g = c->cap_gemv;
     a.kq = c->gv_kq;
@@ -431,16 +517,17 @@ hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     const int max_active = (int)(R < c->N ? R : c->N);
     if (R > a.cap_g) return hipErrorInvalidValue;
     const bool one = T == 1;
+    const bool fin = gemv_finalize(c->sh, a.kq);
     switch (c->sh.fmt) {
         case FT_FMT_BF16:
-            return one ? launch_fmt<FT_FMT_BF16, 1>(a, max_active, c->timing, st)
-                       : launch_fmt<FT_FMT_BF16, kGemvMaxTokens>(a, max_active, c->timing, st);
+            return one ? launch_fmt<FT_FMT_BF16, 1>(a, max_active, fin, c->timing, st)
+                       : launch_fmt<FT_FMT_BF16, kGemvMaxTokens>(a, max_active, fin, c->timing, st);
         case FT_FMT_FP8_B128:
-            return one ? launch_fmt<FT_FMT_FP8_B128, 1>(a, max_active, c->timing, st)
-                       : launch_fmt<FT_FMT_FP8_B128, kGemvMaxTokens>(a, max_active, c->timing, st);
+            return one ? launch_fmt<FT_FMT_FP8_B128, 1>(a, max_active, fin, c->timing, st)
+                       : launch_fmt<FT_FMT_FP8_B128, kGemvMaxTokens>(a, max_active, fin, c->timing, st);
         case FT_FMT_MXFP4_B32:
-            return one ? launch_fmt<FT_FMT_MXFP4_B32, 1>(a, max_active, c->timing, st)
-                       : launch_fmt<FT_FMT_MXFP4_B32, kGemvMaxTokens>(a, max_active, c->timing, st);
+            return one ? launch_fmt<FT_FMT_MXFP4_B32, 1>(a, max_active, fin, c->timing, st)
+                       : launch_fmt<FT_FMT_MXFP4_B32, kGemvMaxTokens>(a, max_active, fin, c->timing, st);
     }
     return hipErrorInvalidValue;
 }
