@@ -26,6 +26,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0}
+FP64_PEAK_TFLOPS = 78.6          # MI355X fp64 (vector and matrix)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -54,6 +55,19 @@ def measured_traffic(kernel_key):
     if d.get("source_sha") != kernel_source_sha() or d.get("kernel") != kernel_key:
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+def time_route(M, shp, x, wr, T, ids, w, stream, reps=10):
+    """Average time of one ft_moe_route call (torch events on the stream it runs on)."""
+    import torch
+    M.ft_moe_route(shp, x.data_ptr(), wr.data_ptr(), T, ids.data_ptr(), w.data_ptr(), stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        M.ft_moe_route(shp, x.data_ptr(), wr.data_ptr(), T, ids.data_ptr(), w.data_ptr(), stream)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def decode_bench(args):
@@ -207,6 +221,7 @@ def prefill_bench(args):
     for l in range(L):
         M.ft_moe_route(shp, x.data_ptr(), wr[l].data_ptr(), T, ids[l].data_ptr(), w[l].data_ptr(), stream)
     torch.cuda.synchronize()
+    route_ms = time_route(M, shp, x, wr[0], T, ids[0], w[0], stream)
 
     def fwd(l, flags=M.FT_PREFETCH_NEXT):
         M.ft_moe_forward(h, l, M.FT_MODE_STREAMED | flags, x.data_ptr(), ids[l].data_ptr(), w[l].data_ptr(), T,
@@ -243,6 +258,9 @@ def prefill_bench(args):
     bytes_stream = L * E * S
     res = {
         "workload": f"prefill chunk T={T}, d={d}, E={E}, top-{k}, f={f}, bf16",
+        "route": {"ms": route_ms, "gflop_fp64": 2.0 * T * d * E / 1e9,
+                  "tflops_fp64": 2.0 * T * d * E / (route_ms / 1e3) / 1e12,
+                  "frac_fp64_peak": 2.0 * T * d * E / (route_ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS},
         "gemm": {"dtype": "bf16", "peak_tflops": MFMA_PEAK_TFLOPS["bf16"],
                  "gateup_tflops": tf_gu, "down_tflops": tf_dn, "pair_tflops": tf_pair,
                  "frac": tf_pair / MFMA_PEAK_TFLOPS["bf16"], "gateup_ms": ms_gu, "down_ms": ms_dn,
@@ -251,7 +269,8 @@ def prefill_bench(args):
                    "pcie_gbs": bytes_stream / t_stream / 1e9, "tokens_per_s": T / t_stream,
                    "compute_only_s": L * t_layer, "gpu_busy_frac": L * t_layer / t_stream},
     }
-    log(f"prefill: GEMM pair {tf_pair:.0f} TFLOP/s ({res['gemm']['frac']:.1%} of bf16 peak), layer "
+    log(f"prefill: route {route_ms * 1e3:.0f} us ({res['route']['tflops_fp64']:.1f} TFLOP/s fp64); "
+        f"GEMM pair {tf_pair:.0f} TFLOP/s ({res['gemm']['frac']:.1%} of bf16 peak), layer "
         f"{t_layer * 1e3:.2f} ms; stream {res['stream']['pcie_gbs']:.1f} GB/s over {L} layers in {t_stream:.2f}s")
     sc.close()
     bank.close()
@@ -328,6 +347,7 @@ def formats_bench(args):
         # grouped GEMM
         for T in Ts:
             x, ids, w = routed(T, 12)
+            r_ms = time_route(M, shp, x, wr, T, ids, w, stream)
             fwd(x, ids, w, T)
             torch.cuda.synchronize()
             reps = 10
@@ -346,7 +366,9 @@ def formats_bench(args):
             tf = fl / (ms / 1e3) / 1e12
             gbs = by / (ms / 1e3) / 1e9
             t_roof = max(fl / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), by / (HBM_PEAK_GBS * 1e9)) * 1e3
-            res[f"gemm_T{T}"] = {"rows": rows, "active_experts": act, "gateup_ms": ms_gu, "down_ms": ms_dn,
+            res[f"gemm_T{T}"] = {"route_ms": r_ms,
+                                 "route_frac_fp64_peak": 2.0 * T * d * E / (r_ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS,
+                                 "rows": rows, "active_experts": act, "gateup_ms": ms_gu, "down_ms": ms_dn,
                                  "tflops": tf, "mfma_frac_bf16": tf / MFMA_PEAK_TFLOPS["bf16"],
                                  "weight_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                                  "t_roofline_ms": t_roof, "roofline_frac": t_roof / ms}

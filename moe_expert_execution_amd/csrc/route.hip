@@ -267,6 +267,179 @@ __global__ void __launch_bounds__(64) route_select_kernel(int T, int E, int k, i
     }
 }
 
+
+// One wave selects the k largest of the logits zl (lane l holds experts
+// l + 64 j; taken marks slots to skip), ties to the lower expert, and writes
+// the ids and the softmax of the chosen logits (fp64, stored fp32).
+__device__ void topk_softmax_wave(double (&zl)[kRouteMaxE / 64], bool (&taken)[kRouteMaxE / 64], int lane, int k,
+                                  int32_t* __restrict__ ids, float* __restrict__ w) {
+    double zsel[kMaxTopK];
+    int esel[kMaxTopK];
+    for (int r = 0; r < k; ++r) {
+        double bz = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxE / 64; ++j) {
+            const int ee = lane + 64 * j;
+            if (!taken[j] && (zl[j] > bz || (zl[j] == bz && ee < be))) {
+                bz = zl[j];
+                be = ee;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const double oz = __shfl_xor(bz, off, 64);
+            const int oe = __shfl_xor(be, off, 64);
+            if (oz > bz || (oz == bz && oe < be)) {
+                bz = oz;
+                be = oe;
+            }
+        }
+        zsel[r] = bz;
+        esel[r] = be;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxE / 64; ++j)
+            if (lane + 64 * j == be) taken[j] = true;
+    }
+    if (lane == 0) {
+        double s = 0.0, ex[kMaxTopK];
+        for (int r = 0; r < k; ++r) {
+            ex[r] = exp(zsel[r] - zsel[0]);
+            s += ex[r];
+        }
+        for (int r = 0; r < k; ++r) {
+            ids[r] = esel[r];
+            w[r] = (float)(ex[r] / s);
+        }
+    }
+}
+
+// Many tokens, E in {64, 128, 256}: the logits are a [T x d] x [d x E] product
+// on the fp64 matrix cores (v_mfma_f64_16x16x4_f64; bf16 inputs are exact in
+// fp64, the sums are fp64).  A workgroup covers 16 tokens x all E experts with
+// 2 E / 64 waves: wave (h, e64) computes 16 tokens x 64 experts over the K half
+// h of each 128-wide K-chunk, and the two halves' logits are added in a fixed
+// order at the end (two waves per SIMD keep the fp64 matrix pipe busy).  Per
+// chunk the activations [16 x 128] and the router rows [128 x E] are staged in
+// LDS as they are (the next chunk is prefetched into registers meanwhile).
+// Lane group g = l / 16 takes k in [16 g, 16 g + 16) of its 64-wide half, so
+// MFMA step s contracts k = 16 g + s over the four groups; column c = l % 16
+// of matrix tile nt is expert 4 c + nt of the wave's 64, so one 8-byte LDS
+// read gives a lane its four tiles' router values for a step.  The logits then
+// go through LDS to the one-wave-per-token selection.
+template <int EE>
+__global__ void __launch_bounds__(2 * EE, 1)
+    route_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int k,
+                      int32_t* __restrict__ ids, float* __restrict__ w) {
+    constexpr int NW = EE / 64;            // waves per K half, one per 64 experts
+    constexpr int NT = 2 * NW * 64;        // threads
+    constexpr int KC = 128;
+    constexpr int LDX = KC + 8;            // padded activation row (bf16)
+    constexpr int LDW = EE + 8;            // padded router row (bf16)
+    constexpr int XC = 16 * KC / 8;        // 16-byte pieces of a chunk: activations
+    constexpr int WC = KC * EE / 8;        //                                router rows
+    constexpr int XPT = (XC + NT - 1) / NT, WPT = WC / NT;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // kept in registers (no stack copy)
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef double f64x4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) uint16_t xs[16 * LDX];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[KC * LDW];
+    __shared__ double zs[16][EE];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int kh = wid / NW, wv = wid % NW;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int t0 = blockIdx.x * 16;
+    f64x4 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+    u32x4_t rx[XPT], rw[WPT];
+    auto gload = [&](int c0) {
+#pragma unroll
+        for (int e = 0; e < XPT; ++e) {
+            const int i = tid + NT * e;
+            const int t = i / (KC / 8), c8 = i - t * (KC / 8);
+            rx[e] = u32x4_t{0u, 0u, 0u, 0u};
+            if (i < XC && t0 + t < T) rx[e] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)(t0 + t) * d + c0 + 8 * c8);
+        }
+#pragma unroll
+        for (int e = 0; e < WPT; ++e) {
+            const int i = tid + NT * e;
+            const int kk = i / (EE / 8), e8 = i - kk * (EE / 8);
+            rw[e] = *reinterpret_cast<const u32x4_t*>(wr + (int64_t)(c0 + kk) * EE + 8 * e8);
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int e = 0; e < XPT; ++e) {
+            const int i = tid + NT * e;
+            const int t = i / (KC / 8), c8 = i - t * (KC / 8);
+            if (i < XC) *reinterpret_cast<u32x4_t*>(&xs[t * LDX + 8 * c8]) = rx[e];
+        }
+#pragma unroll
+        for (int e = 0; e < WPT; ++e) {
+            const int i = tid + NT * e;
+            const int kk = i / (EE / 8), e8 = i - kk * (EE / 8);
+            *reinterpret_cast<u32x4_t*>(&ws[kk * LDW + 8 * e8]) = rw[e];
+        }
+    };
+    gload(0);
+    lstore();
+    __syncthreads();
+    for (int c0 = 0; c0 < d; c0 += KC) {
+        const bool more = c0 + KC < d;
+        if (more) gload(c0 + KC);
+        const uint16_t* xr = &xs[c16 * LDX + 64 * kh + 16 * g];
+        const u32x4_t xa0 = *reinterpret_cast<const u32x4_t*>(xr);
+        const u32x4_t xa1 = *reinterpret_cast<const u32x4_t*>(xr + 8);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const uint32_t xw = s < 8 ? xa0[s >> 1] : xa1[(s - 8) >> 1];
+            const double a = (double)__uint_as_float((s & 1) ? (xw & 0xFFFF0000u) : (xw << 16));
+            const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(&ws[(64 * kh + 16 * g + s) * LDW + wv * 64 + 4 * c16]);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const uint32_t u = bb[nt >> 1];
+                const double b = (double)__uint_as_float((nt & 1) ? (u & 0xFFFF0000u) : (u << 16));
+                acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[nt], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+        if (more) {
+            lstore();
+            __syncthreads();
+        }
+    }
+    // accumulator element v of lane l: token 4 v + l / 16; tile nt column l % 16 = expert 4 (l % 16) + nt.
+    // The K halves are added in a fixed order: half 0, then half 1.
+    if (kh == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) zs[4 * v + g][wv * 64 + 4 * c16 + nt] = acc[nt][v];
+    }
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) zs[4 * v + g][wv * 64 + 4 * c16 + nt] += acc[nt][v];
+    }
+    __syncthreads();
+    for (int t = wid; t < 16; t += 2 * NW) {
+        if (t0 + t >= T) break;
+        double zl[kRouteMaxE / 64];
+        bool taken[kRouteMaxE / 64];
+#pragma unroll
+        for (int j = 0; j < kRouteMaxE / 64; ++j) {
+            const int ee = lane + 64 * j;
+            zl[j] = ee < EE ? zs[t][ee] : -INFINITY;
+            taken[j] = ee >= EE;
+        }
+        topk_softmax_wave(zl, taken, lane, k, ids + (int64_t)(t0 + t) * k, w + (int64_t)(t0 + t) * k);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int d, int E, int k, int32_t* ids, float* w,
@@ -281,6 +454,16 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int d, int
             hipLaunchKernelGGL(route_partial_kernel<kRouteSmallT>, dim3(kRouteDS), dim3(kRouteThreads), 0, st, x, wr,
                                T, d, E);
         hipLaunchKernelGGL(route_select_kernel, dim3(T), dim3(64), 0, st, T, E, k, ids, w);
+        return hipGetLastError();
+    }
+    if (d % 128 == 0 && (E == 64 || E == 128 || E == 256)) {
+        const dim3 grid((T + 15) / 16);
+        if (E == 64)
+            hipLaunchKernelGGL(route_mfma_kernel<64>, grid, dim3(128), 0, st, x, wr, T, d, k, ids, w);
+        else if (E == 128)
+            hipLaunchKernelGGL(route_mfma_kernel<128>, grid, dim3(256), 0, st, x, wr, T, d, k, ids, w);
+        else
+            hipLaunchKernelGGL(route_mfma_kernel<256>, grid, dim3(512), 0, st, x, wr, T, d, k, ids, w);
         return hipGetLastError();
     }
     int blocks = (T + kRouteTokens - 1) / kRouteTokens;

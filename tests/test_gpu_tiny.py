@@ -37,10 +37,17 @@ def test_route_tiny_bit_exact():
 
 
 @gpu
-@pytest.mark.parametrize("cfgname,T", [("decode", 1), ("decode", 300), ("mxfp4", 37), ("tiny", 5)])
-def test_route_shapes_bit_exact(cfgname, T):
+@pytest.mark.parametrize("cfgname,T,E", [("decode", 1, None), ("decode", 300, None), ("mxfp4", 37, None),
+                                         ("tiny", 5, None), ("decode", 1531, None), ("fp8", 1000, None),
+                                         ("decode", 77, 64), ("decode", 40, 96)])
+def test_route_shapes_bit_exact(cfgname, T, E):
+    """Routing ids bit-exact and weights to fp32 rounding against the oracle, for
+    the small-T path, the matrix-core path (E in {64, 128, 256}; ragged last
+    workgroup) and the general path (E = 96)."""
     cuda()
     cfg = synth.CONFIGS[cfgname]
+    if E is not None:
+        cfg = cfg.with_(E=E)
     x = synth.tokens(cfg, T, 11)
     wr = synth.router(cfg, 3)
     ids, w = _route_gpu(cfg, x, wr, T)
