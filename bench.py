@@ -164,6 +164,38 @@ def decode_bench(args):
         f"({gu_gbs / HBM_PEAK_GBS:.1%}), pair {both_gbs:.0f} GB/s, miss rate {res['cache']['miss_rate']:.2f}, "
         f"fill {res['branches']['fill_gbs']:.1f} GB/s, host {res['branches']['host_gbs']:.1f} GB/s "
         f"({delta['host_seconds']:.2f}s busy of {elapsed:.2f}s)")
+    if not args.no_measured_profile:
+        # the same decode run again from a cold cache, with q* fed by this machine's measured B_P / B_H
+        M.ft_cache_set_timing(h, False)
+        prof = M.ft_cache_profile(h, 16)          # leaves the cache empty (cold)
+        try:
+            from moe_expert_execution_amd import bwprofile
+            bwprofile.save("bf16", bwprofile.gpu_key(), prof.bp_mbps, prof.bh_mbps,
+                           directory=os.path.join(ROOT, "gpurun_out", "bwprofile"))
+        except Exception as exc:          # the store is a convenience; the measurement stands
+            log(f"profile not stored: {exc}")
+        M.ft_cache_set_profile(h, prof)
+        for s_ in range(args.warmup):
+            step(s_)
+        torch.cuda.synchronize()
+        p0 = M.ft_cache_stats(h).as_dict()
+        t0 = time.perf_counter()
+        for s_ in range(args.warmup, steps):
+            step(s_)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        p1 = M.ft_cache_stats(h).as_dict()
+        calls = max(p1["calls"] - p0["calls"], 1)
+        res["measured_profile"] = {
+            "bp_mbps": prof.bp_mbps, "bh_mbps": prof.bh_mbps,
+            "tokens_per_s": args.steps / el, "ms_per_step": el / args.steps * 1e3,
+            "fills_per_call": (p1["fills"] - p0["fills"]) / calls,
+            "host_experts_per_call": (p1["cpu_experts"] - p0["cpu_experts"]) / calls,
+            "miss_rate": (p1["misses"] - p0["misses"]) / max(p1["unique"] - p0["unique"], 1),
+        }
+        log(f"decode with the measured profile B_P/B_H {prof.bp_mbps / 1e3:.1f}/{prof.bh_mbps / 1e3:.1f} GB/s: "
+            f"{args.steps / el:.1f} tok/s, fills {res['measured_profile']['fills_per_call']:.2f} and host experts "
+            f"{res['measured_profile']['host_experts_per_call']:.2f} per layer call")
     sc.close()
     return res, bank, cfg
 
@@ -393,6 +425,8 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-measured-profile", action="store_true",
+                    help="skip the second decode run with the measured B_P / B_H")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (kernel work)")
     ap.add_argument("--formats", action="store_true",
                     help="only run the block-FP8 and MXFP4 kernel measurements (one resident layer each)")
@@ -448,6 +482,7 @@ def main():
         "decode_kernels": dec["decode_kernels"],
         "cache": dec["cache"],
         "branches": dec["branches"],
+        "measured_profile": dec.get("measured_profile"),
         "prefill": pre,
     }
     print(json.dumps(line), flush=True)

@@ -251,6 +251,32 @@ ft_status ft_moe_forward(ft_cache* cache, int32_t layer, int32_t mode, const uin
  * ------------------------------------------------------------------------- */
 ft_status ft_cache_resize(ft_cache* cache, int64_t new_num_slots);
 
+/* ---------------------------------------------------------------------------
+ * ft_cache_profile — measure this machine's B_P and B_H on the real paths
+ * ("Making Large MoE Models Practical on a Single Machine", section 7: the
+ * split uses measured, not nominal, bandwidths; the txtmix.com FreeToken
+ * article's quick start: one bandwidth benchmark per GPU and expert format).
+ * B_P: the fill kernel pulls `records` layer-0 records from the pinned host
+ * bank into slots 0 .. records-1, max_tokens * k records per launch (best of
+ * three passes, HIP events).  B_H: the host workers run `records` records as
+ * host experts of up to max_tokens tokens per call (two passes after a
+ * warm-up, the workers' own clock).  Each pass reads records of its own
+ * (pass p: p * records + i, modulo E), so no pass is timed on data a previous
+ * one left in a host cache.  Both are record bytes / time in MB/s, written to `out`
+ * (max_fetch copied from the cache's profile).  Safe point: the caller
+ * guarantees no work is pending on this cache.  The slots are overwritten, so
+ * the cache restarts empty (every map entry absent, stamps 0, clock 1); the
+ * cache's own profile is not changed (see ft_cache_set_profile).
+ * records: 1 .. min(E, num_slots).  Synchronises.
+ * Errors: FT_ERR_ARG, FT_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+ft_status ft_cache_profile(ft_cache* cache, int32_t records, ft_profile* out);
+
+/* Replace the cache's B_P / B_H / max_fetch (for example with a measured
+ * profile).  Later classify calls compute q* from it; calls already enqueued
+ * keep the profile they were launched with.  Errors: FT_ERR_ARG. */
+ft_status ft_cache_set_profile(ft_cache* cache, const ft_profile* profile);
+
 /* Counters and sticky error flags (synchronises). */
 ft_status ft_cache_stats(const ft_cache* cache, ft_stats* out);
 

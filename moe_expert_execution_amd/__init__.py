@@ -73,6 +73,8 @@ _SIGS = {
     "ft_cache_classify": (i32, [vp, i32, vp, i32, ctypes.POINTER(FtClassifyOut), vp]),
     "ft_moe_forward": (i32, [vp, i32, i32, vp, vp, vp, i32, vp, vp]),
     "ft_cache_resize": (i32, [vp, i64]),
+    "ft_cache_profile": (i32, [vp, i32, ctypes.POINTER(FtProfile)]),
+    "ft_cache_set_profile": (i32, [vp, ctypes.POINTER(FtProfile)]),
     "ft_cache_stats": (i32, [vp, ctypes.POINTER(FtStats)]),
     "ft_cache_snapshot": (i32, [vp, vp, vp, vp, vp]),
     "ft_cache_set_timing": (i32, [vp, i32]),
@@ -161,6 +163,16 @@ def ft_moe_forward(h: int, layer: int, mode: int, x: int, routes: int, w: int, T
 
 def ft_cache_resize(h: int, num_slots: int) -> None:
     _check(lib().ft_cache_resize(h, num_slots))
+
+
+def ft_cache_profile(h: int, records: int) -> FtProfile:
+    out = FtProfile()
+    _check(lib().ft_cache_profile(h, records, ctypes.byref(out)))
+    return out
+
+
+def ft_cache_set_profile(h: int, prof: FtProfile) -> None:
+    _check(lib().ft_cache_set_profile(h, ctypes.byref(prof)))
 
 
 def ft_cache_stats(h: int) -> FtStats:

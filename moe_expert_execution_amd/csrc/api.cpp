@@ -537,6 +537,107 @@ ft_status ft_cache_resize(ft_cache* c, int64_t new_num_slots) {
     return FT_OK;
 }
 
+ft_status ft_cache_set_profile(ft_cache* c, const ft_profile* p) {
+    clear_error();
+    FT_REQUIRE(c && p, "null pointer");
+    FT_REQUIRE(p->bp_mbps > 0 && p->bh_mbps > 0, "bandwidths must be positive");
+    FT_REQUIRE(p->max_fetch >= -1, "max_fetch must be -1 or >= 0");
+    c->prof = *p;
+    return FT_OK;
+}
+
+ft_status ft_cache_profile(ft_cache* c, int32_t records, ft_profile* out) {
+    clear_error();
+    FT_REQUIRE(c && out, "null pointer");
+    const int64_t lim = std::min<int64_t>(c->sh.experts, c->N);
+    FT_REQUIRE(records >= 1 && records <= lim, "records must be in 1..min(E, num_slots) = %lld", (long long)lim);
+    ft_status fs = flush_fill_sync(c);
+    if (fs != FT_OK) return fs;
+    FT_HIP(hipDeviceSynchronize());
+    const int64_t S = c->rl.S;
+    const int k = c->sh.top_k;
+    const int batch = c->cap;                 // worklist and host-staging capacity
+    const int E = c->sh.experts;
+    // Every fill repetition and host pass reads its own records (pass p reads
+    // layer-0 records p*records .. p*records + records - 1, modulo E), so that
+    // neither path is timed on data a previous pass left in a host cache.
+    auto rec_of = [&](int pass, int i) { return (int32_t)(((int64_t)pass * records + i) % E); };
+    // B_P: the fill kernel pulls `records` records into slots 0 .. records-1,
+    // in launches of at most `batch` records
+    hipEvent_t e0, e1;
+    FT_HIP(hipEventCreate(&e0));
+    FT_HIP(hipEventCreate(&e1));
+    double best_ms = 1e30;
+    for (int rep = 0; rep < 3; ++rep) {
+        double ms_rep = 0.0;
+        for (int b0 = 0; b0 < records; b0 += batch) {
+            const int n = std::min(batch, records - b0);
+            std::vector<int32_t> idx(n);
+            std::vector<int32_t> src(n);
+            for (int i = 0; i < n; ++i) {
+                idx[i] = b0 + i;
+                src[i] = rec_of(rep, b0 + i);
+            }
+            const int32_t counts[4] = {n, 0, n, n};
+            FT_HIP(hipMemcpy(c->wl_slot, idx.data(), sizeof(int32_t) * n, hipMemcpyHostToDevice));
+            FT_HIP(hipMemcpy(c->wl_src, src.data(), sizeof(int32_t) * n, hipMemcpyHostToDevice));
+            FT_HIP(hipMemcpy(c->wl_counts, counts, sizeof(counts), hipMemcpyHostToDevice));
+            TimedLaunch tl;
+            tl.start = e0;
+            tl.stop = e1;
+            FT_HIP(launch_fill(c, 0, tl));
+            FT_HIP(hipEventSynchronize(e1));
+            float ms = 0.0f;
+            FT_HIP(hipEventElapsedTime(&ms, e0, e1));
+            ms_rep += ms;
+        }
+        best_ms = std::min(best_ms, ms_rep);
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    const double bp = (double)records * S / (best_ms / 1e3) / 1e6;
+    // B_H: the host workers run the same records as host routes of up to
+    // max_tokens tokens per call (zero activations; the time does not depend on values)
+    HostStaging hs = host_branch_staging(c->host);
+    auto host_pass = [&](int pass) {
+        for (int b0 = 0; b0 < records; b0 += batch) {
+            const int n = std::min(batch, records - b0);
+            const int T = (n + k - 1) / k;
+            memset(hs.x, 0, sizeof(uint16_t) * (size_t)T * c->sh.d_model);
+            for (int r = 0; r < T * k; ++r) {
+                hs.routes[r] = r < n ? -(1 + rec_of(pass, b0 + r)) : INT32_MIN;
+                hs.w[r] = 1.0f / k;
+            }
+            host_branch_run_sync(c->host, 0, T);
+        }
+    };
+    uint64_t b0c, b1c, x0, x1;
+    double s0, s1;
+    host_pass(3);                      // warm-up (worker wake-up), records not timed
+    host_branch_counters(c->host, &b0c, &s0, &x0);
+    host_pass(4);
+    host_pass(5);
+    host_branch_counters(c->host, &b1c, &s1, &x1);
+    const double bh = (double)(b1c - b0c) / std::max(s1 - s0, 1e-9) / 1e6;
+    // the pool's slots were overwritten: the cache restarts empty
+    const int64_t nids = (int64_t)c->sh.layers * c->sh.experts;
+    const uint64_t one = 1;
+    FT_HIP(hipMemset(c->slot_for_id, 0xFF, sizeof(int32_t) * nids));
+    FT_HIP(hipMemset(c->id_of_slot, 0xFF, sizeof(int32_t) * c->N));
+    FT_HIP(hipMemset(c->stamp, 0, sizeof(uint64_t) * c->N));
+    FT_HIP(hipMemcpy(c->clock, &one, sizeof(one), hipMemcpyHostToDevice));
+    FT_HIP(hipMemset(c->wl_counts, 0, sizeof(int32_t) * 4));
+    c->buf_layer[0] = c->buf_layer[1] = -1;
+    c->release_recorded[0] = c->release_recorded[1] = false;
+    c->xfer_pending = false;
+    c->streaming = false;
+    FT_HIP(hipDeviceSynchronize());
+    out->bp_mbps = (uint32_t)std::min(bp, 4.0e9);
+    out->bh_mbps = (uint32_t)std::min(bh, 4.0e9);
+    out->max_fetch = c->prof.max_fetch;
+    return FT_OK;
+}
+
 ft_status ft_cache_stats(const ft_cache* c, ft_stats* o) {
     clear_error();
     FT_REQUIRE(c && o, "null pointer");

@@ -84,6 +84,9 @@ HostSignal host_branch_prepare(HostBranch* hb, int32_t layer, int32_t T);
 // (staging must already hold routes, w and x for those tokens).
 hipError_t host_branch_enqueue(HostBranch* hb, int32_t layer, int32_t T, hipStream_t stream);
 int host_branch_threads(HostBranch* hb);
+// Run one host-branch call on the calling thread (staging must hold its routes,
+// weights and activations); no GPU work may be pending on the host branch.
+void host_branch_run_sync(HostBranch* hb, int32_t layer, int32_t T);
 // bytes of expert records the workers read, and seconds spent in host calls with work
 void host_branch_counters(HostBranch* hb, uint64_t* bytes, double* seconds, uint64_t* experts);
 

@@ -465,6 +465,8 @@ HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const
     return hb;
 }
 
+void host_branch_run_sync(HostBranch* hb, int32_t layer, int32_t T) { run_call(hb, layer, T); }
+
 HostSignal host_branch_prepare(HostBranch* hb, int32_t layer, int32_t T) {
     HostSignal s{};
     s.mailbox = hb->use_mailbox;

@@ -87,6 +87,8 @@ def test_argument_errors_without_device_work(lib):
     assert lib.ft_cache_classify(None, 0, 1, 1, None, None) == M.FT_ERR_ARG
     assert lib.ft_moe_forward(None, 0, 0, 1, 1, 1, 1, 1, None) == M.FT_ERR_ARG
     assert lib.ft_cache_resize(None, 4) == M.FT_ERR_ARG
+    assert lib.ft_cache_profile(None, 4, ctypes.byref(M.profile(1, 1))) == M.FT_ERR_ARG
+    assert lib.ft_cache_set_profile(None, ctypes.byref(M.profile(1, 1))) == M.FT_ERR_ARG
     assert lib.ft_cache_destroy(None) == M.FT_OK
 
 
@@ -94,3 +96,17 @@ def test_multi_gpu_bench_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bandwidth_profile_store_is_keyed_by_format_and_gpu(tmp_path):
+    from moe_expert_execution_amd import bwprofile as B
+    d = str(tmp_path)
+    assert B.load("bf16", "gpu-a", d) is None
+    B.save("bf16", "gpu-a", 52000, 104000, d)
+    B.save("fp8", "gpu-a", 51000, 99000, d)
+    assert B.load("bf16", "gpu-a", d) == (52000, 104000)
+    assert B.load("fp8", "gpu-a", d) == (51000, 99000)
+    assert B.load("mxfp4", "gpu-a", d) is None      # another format: not measured
+    assert B.load("bf16", "gpu-b", d) is None       # another GPU: not this profile
+    B.save("bf16", "gpu-a", 53000, 100000, d)
+    assert B.load("bf16", "gpu-a", d) == (53000, 100000)
