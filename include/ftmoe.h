@@ -140,8 +140,10 @@ typedef struct {
  *   "One logical expert, two physical levels of memory").  It must stay valid
  *   and unchanged until ft_cache_destroy.
  * num_slots: N complete records allocated in HBM (1..32768).
- * max_tokens: largest T any later call will pass (sizes internal buffers).
- * Errors: FT_ERR_ARG (shape, null, N), FT_ERR_NOMEM, FT_ERR_HIP.
+ * max_tokens: largest T any later call will pass (sizes internal buffers),
+ *   1..65535, with max_tokens * top_k * d_ff * 2 below 4 GiB (the expert
+ *   GEMMs reach activation rows through 32-bit byte offsets).
+ * Errors: FT_ERR_ARG (shape, null, N, max_tokens), FT_ERR_NOMEM, FT_ERR_HIP.
  * Synchronises the current device.
  *
  * Record layout (S bytes), matrices [rows x K] in this order:

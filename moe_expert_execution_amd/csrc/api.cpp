@@ -265,6 +265,8 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     FT_REQUIRE(num_slots >= 1 && num_slots <= kMaxSlots, "num_slots must be in 1..%d", kMaxSlots);
     FT_REQUIRE(max_tokens >= 1 && max_tokens <= 65535, "max_tokens must be in 1..65535");
     FT_REQUIRE((int64_t)max_tokens * shape->top_k <= (1 << 24), "max_tokens * top_k too large");
+    FT_REQUIRE((int64_t)max_tokens * shape->top_k * shape->d_ff * 2 <= 0xFFFFFFFFll,
+               "max_tokens * top_k * d_ff * 2 must be below 4 GiB");
 
     ft_cache* c = new (std::nothrow) ft_cache();
     if (!c) return FT_ERR_NOMEM;

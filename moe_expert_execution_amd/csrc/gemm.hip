@@ -11,18 +11,21 @@
 // operand tile, which is exactly an operand layout of
 // v_mfma_f32_32x32x16_bf16 (lane l: row l % 32, chunk column l / 32).  So
 // the weights go from memory straight into registers — no LDS staging, no
-// shuffles — one K-step ahead of their use; only the activation tile (shared
-// by the four waves) is staged through double-buffered LDS, one barrier per
-// K-step.  Block-FP8 and MXFP4 weights are converted to bf16 in registers
-// right before their MFMA, so every format issues the bf16 MFMA.  The expert
+// shuffles — two K-steps ahead of their use; only the activation tile (shared
+// by the four waves) is staged through LDS, loaded straight into a 4-deep
+// ring of buffers, one barrier per K-step.  Block-FP8 and MXFP4 weights are
+// converted to bf16 in registers right before their MFMA, so every format
+// issues the bf16 MFMA.  The expert
 // FFN with its gate/up and down projections read from one slot record follows
 // "The Expert Cache That Follows the Router", section "One logical expert,
 // two physical levels of memory".
+#include <type_traits>
+
 #include "wfmt.h"
 
 namespace ftmoe {
 
-constexpr int kBM = 128, kBN = 256, kBK = 64, kLDK = kBK + 8;
+constexpr int kBM = 128, kBN = 256, kBK = 64, kStages = 4;
 constexpr int kGemmThreads = 256;
 
 int gemm_tile_m() { return kBM; }
@@ -33,6 +36,7 @@ struct GemmArgs {
     uint16_t* Hout;        // bf16 [rows x f] (gate/up C)
     uint16_t* Y;           // bf16 [rows x d]
     int k, d, f;
+    uint32_t x_bytes, h_bytes;   // extents of x and H (their rows are reached by 32-bit offsets)
     const int32_t* meta;
     const int32_t* active_slot;
     const int32_t* seg;
@@ -56,6 +60,8 @@ __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcp
 template <int FMT>
 struct Frag {
     static constexpr int LBK = 64 / (2 * WF<FMT>::EPC);    // lane blocks per K-step: 4, 2, 1
+    // a weight scale as stored: fp32 bits (FP8), an e8m0 byte (MXFP4)
+    using SRaw = std::conditional_t<FMT == FT_FMT_MXFP4_B32, uint8_t, uint32_t>;
     __device__ static int a_koff(int ks, int g) {
         if constexpr (FMT == FT_FMT_BF16) return ks * 16 + g * 8;
         else if constexpr (FMT == FT_FMT_FP8_B128) return (ks >> 1) * 32 + g * 16 + (ks & 1) * 8;
@@ -63,12 +69,15 @@ struct Frag {
     }
 };
 
-// B operand of MFMA step ks from the K-step's lane-block registers.
+// B operand of MFMA step ks from the K-step's lane-block registers; `sraw` is
+// the scale as loaded (FP8: fp32 bits, MXFP4: the e8m0 byte), decoded here so
+// that its load is waited for only where it is used.
 template <int FMT>
-__device__ __forceinline__ bf16x8_t b_frag(const u32x4_t (&r)[Frag<FMT>::LBK], int ks, float scale) {
+__device__ __forceinline__ bf16x8_t b_frag(const u32x4_t (&r)[Frag<FMT>::LBK], int ks, typename Frag<FMT>::SRaw sraw) {
     if constexpr (FMT == FT_FMT_BF16) {
         return __builtin_bit_cast(bf16x8_t, r[ks]);
     } else if constexpr (FMT == FT_FMT_FP8_B128) {
+        const float scale = __uint_as_float(sraw);
         const u32x4_t w = r[ks >> 1];
         const uint32_t w0 = (ks & 1) ? w[2] : w[0];
         const uint32_t w1 = (ks & 1) ? w[3] : w[1];
@@ -82,6 +91,7 @@ __device__ __forceinline__ bf16x8_t b_frag(const u32x4_t (&r)[Frag<FMT>::LBK], i
         const bf16x2_t q3 = __builtin_convertvector(p3 * scale, bf16x2_t);
         return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
     } else {
+        const float scale = e8m0_to_f32(sraw);
         const uint32_t w = r[0][ks];
         const bf16x2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
         const bf16x2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
@@ -89,6 +99,14 @@ __device__ __forceinline__ bf16x8_t b_frag(const u32x4_t (&r)[Frag<FMT>::LBK], i
         const bf16x2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
         return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
     }
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order); the other counters are left alone.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
 // Tile (kBM rows of one slot) x (kBN columns) per workgroup; 4 waves side by
@@ -101,12 +119,23 @@ __device__ __forceinline__ bf16x8_t b_frag(const u32x4_t (&r)[Frag<FMT>::LBK], i
 // receives a contiguous range of blocks, ordered by slot, then N-tile, then
 // M-tile: all blocks of an expert run together in one XCD, where its A rows
 // and weight panels are read from HBM about once and then hit that XCD's L2.
+//
+// The activation tile goes from memory straight into LDS
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's base +
+// 16 x lane) through a ring of kStages K-step buffers, kStages - 1 steps ahead
+// of its use.  A buffer is 128 rows x 128 bytes; 16-byte chunk c of row r sits
+// at position c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), so that the 16 (or 8)
+// rows one ds_read_b128 serves per cycle fall in distinct banks.  Waits are
+// explicit (vmcnt + s_barrier): a __syncthreads would also drain the weight
+// loads that are in flight for later steps.
 template <int FMT, bool GU>
 __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
     using FR = Frag<FMT>;
     constexpr int LBK = FR::LBK;
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLDK];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
+    constexpr int NB = 2 * LBK;                   // weight loads per wave per K-step
+    __shared__ __attribute__((aligned(1024))) uint16_t As[kStages][kBM * kBK];
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int NT = GU ? a.f / (kBN / 2) : a.d / kBN;
     const int V = a.meta[1] * NT;                 // valid workgroups
     const int b = blockIdx.x;
@@ -147,29 +176,47 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
         bp[1] = rec + a.off_down + pn[1] * panel_bytes + lane * 16;
         soff[0] = soff[1] = a.off_sd;
     }
-    // per-K-step weight scale of panel i: FP8 — the 128 x 128 block's fp32
-    // (uniform over the panel); MXFP4 — the lane's e8m0 byte for its chunk
-    auto scale_of = [&](int i, int kt) -> float {
+    // per-K-step weight scale of panel i, as stored: FP8 — the 128 x 128
+    // block's fp32 (uniform over the panel); MXFP4 — the lane's e8m0 byte for
+    // its chunk
+    auto scale_of = [&](int i, int kt) -> typename FR::SRaw {
         if constexpr (FMT == FT_FMT_FP8_B128) {
-            return reinterpret_cast<const float*>(rec + soff[i])[(pn[i] >> 2) * (K >> 7) + (kt >> 1)];
+            return reinterpret_cast<const uint32_t*>(rec + soff[i])[(pn[i] >> 2) * (K >> 7) + (kt >> 1)];
         } else if constexpr (FMT == FT_FMT_MXFP4_B32) {
-            return e8m0_to_f32(rec[soff[i] + (int64_t)pn[i] * K + kt * 64 + lane]);
+            return rec[soff[i] + (int64_t)pn[i] * K + kt * 64 + lane];
         } else {
-            return 1.0f;
+            return 0;
         }
     };
 
-    // A: 4 chunks of 8 bf16 per thread per K-step (row (tid >> 3) + 32 i, chunk tid & 7)
-    const uint16_t* ap[4];
+    // A: wave w fills rows [32 w, 32 w + 32) of a buffer with 4 loads, load i
+    // covering the 1 KiB of rows 32 w + 8 i .. + 7: lane l takes row
+    // 32 w + 8 i + l / 8 at physical chunk l % 8, i.e. logical chunk
+    // (l % 8) ^ (l / 8) ^ (i & 1).  Rows past the tile's end repeat its last
+    // row: their outputs are never stored.  The loads are buffer loads (byte
+    // offsets from x or H, the K-step in the scalar offset); the hardware
+    // returns zeros for any offset past the buffer's extent.
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(GU ? a.x : a.Hin), 0, (int)(GU ? a.x_bytes : a.h_bytes), 0x00020000);
+    uint32_t avo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // rows past the tile's end repeat its last row: their outputs are never stored
-        int r = (tid >> 3) + 32 * i;
+        int r = 32 * w + 8 * i + (lane >> 3);
         r = r < rows_valid ? r : rows_valid - 1;
         const int p = row0 + r;
-        ap[i] = (GU ? a.x + (int64_t)(a.perm[p] / a.k) * a.d : a.Hin + (int64_t)p * a.f) + (tid & 7) * 8;
+        const int c = (lane & 7) ^ (lane >> 3) ^ (i & 1);
+        const uint32_t row = GU ? (uint32_t)(a.perm[p] / a.k) * (uint32_t)a.d : (uint32_t)p * (uint32_t)a.f;
+        avo[i] = (row + (uint32_t)c * 8u) * 2u;
     }
-    const int a_st = (tid >> 3) * kLDK + (tid & 7) * 8;    // this thread's LDS store offset (row i adds 32 kLDK)
+    const int KT = K / kBK;        // even: K is a multiple of 128
+    auto load_a = [&](int kt, int stage) {
+        const int ks = kt < KT ? kt : KT - 1;       // past the end: reload the last step (never read)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                arsrc, (__attribute__((address_space(3))) void*)(&As[stage][(4 * w + i) * 512]), 16, avo[i],
+                ks * kBK * 2, 0, 0);
+    };
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -179,12 +226,11 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-    const int KT = K / kBK;        // even: K is a multiple of 128
     // Two sets of weight registers, for even and odd K-steps: step kt reads
     // set kt % 2 and then refills it with K-step kt + 2, so every weight load
     // has two K-steps to arrive and lands in the registers its consumer reads.
     u32x4_t br[2][2][LBK];
-    float bs[2][2];
+    typename FR::SRaw bs[2][2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -194,44 +240,45 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
                 br[s2][i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(s2 * LBK + j) * 1024);
             bs[s2][i] = scale_of(i, s2);
         }
-    {
-        u32x4_t ra[4];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(ap[i]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(&As[0][a_st + 32 * i * kLDK]) = ra[i];
-    }
-    __syncthreads();
+    for (int s = 0; s < kStages - 1; ++s) load_a(s, s);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // A operand of MFMA step ks for the four row blocks, from LDS buffer Ab
-    auto read_a = [&](bf16x8_t (&af)[4], const uint16_t* Ab, int ks) {
-        const int ko = FR::a_koff(ks, g);
+    // A operand of MFMA step ks for the four row blocks, from buffer `stage`
+    const int m = lane & 31;
+    const int fm = (m & 7) ^ ((m >> 3) & 1);
+    auto read_a = [&](bf16x8_t (&af)[4], int stage, int ks) {
+        const int c = FR::a_koff(ks, g) >> 3;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
-            af[mi] = *reinterpret_cast<const bf16x8_t*>(&Ab[(mi * 32 + (lane & 31)) * kLDK + ko]);
+            af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[stage][(mi * 32 + m) * kBK + ((c ^ fm) << 3)]);
     };
     bf16x8_t af[2][4];
-    read_a(af[0], As[0], 0);
 
-    // One K-step.  Instruction order is pinned with scheduling barriers: the
-    // compiler would otherwise sink every prefetch below the last MFMA.
-    // Loads stay unconditional (the last steps reload a valid K-step), so each
-    // refill lands in the registers its consumer reads.
-    auto kstep = [&](int kt, u32x4_t (&brs)[2][LBK], float (&bss)[2]) {
-        const bool more = kt + 1 < KT;
-        const int kn = more ? kt + 1 : kt;                // A tile staged for the next step
-        const int kw = kt + 2 < KT ? kt + 2 : KT - 1;     // weights refilled for two steps ahead
-        const uint16_t* Ab = As[kt & 1];
-        u32x4_t ra[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(ap[i] + kn * kBK);
-        float bs_next[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) bs_next[i] = scale_of(i, kw);
+    // One K-step.  Vector-memory operations of a wave complete in issue order,
+    // so "A of step kt has landed" is a count of the loads issued after it:
+    // the prologue issues B(0), B(1), A(0), A(1), A(2); each step issues
+    // A(kt + 3) and then its NB weight refills (scale loads, if any, come
+    // after them and only make the count conservative).  After every wave has seen
+    // its own loads land, one barrier publishes the buffer, and also tells
+    // that every wave is done reading the buffer the new A load overwrites.
+    // Instruction order is pinned with scheduling barriers: the compiler would
+    // otherwise sink every prefetch below the last MFMA.
+    auto kstep = [&](int kt, int stage, u32x4_t (&brs)[2][LBK], typename FR::SRaw (&bss)[2]) {
+        if (kt >= 3) vm_wait<8 + 3 * NB>();
+        else if (kt == 2) vm_wait<8 + 2 * NB>();
+        else if (kt == 1) vm_wait<8 + NB>();
+        else vm_wait<8>();
+        __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        load_a(kt + kStages - 1, (stage + kStages - 1) % kStages);
+        const int kw = kt + 2 < KT ? kt + 2 : KT - 1;     // weights refilled for two steps ahead
+        __builtin_amdgcn_sched_barrier(0);
+        read_a(af[0], stage, 0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            if (ks < 3) read_a(af[(ks + 1) & 1], Ab, ks + 1);
+            if (ks < 3) read_a(af[(ks + 1) & 1], stage, ks + 1);
             const bf16x8_t b0 = b_frag<FMT>(brs[0], ks, bss[0]);
             const bf16x8_t b1 = b_frag<FMT>(brs[1], ks, bss[1]);
 #pragma unroll
@@ -246,8 +293,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
                 for (int i = 0; i < 2; ++i)
                     brs[i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(kw * LBK + j) * 1024);
             }
-            // order inside the step: the next step's LDS reads interleaved with
-            // the first MFMAs, then the rest, then the refill loads
+            // order inside the step: the next MFMA step's LDS reads interleaved
+            // with the first MFMAs, then the rest, then the refill loads
             if (ks < 3) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -261,32 +308,34 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);           // global loads
             __builtin_amdgcn_sched_barrier(0);
         }
-        bss[0] = bs_next[0];
-        bss[1] = bs_next[1];
-        if (more) {
+        // the refilled set's scales, loaded straight into the registers that
+        // step kw reads (a copy would have to wait for the load)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(&As[(kt + 1) & 1][a_st + 32 * i * kLDK]) = ra[i];
-        }
-        __syncthreads();
-        read_a(af[0], As[(kt + 1) & 1], 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 2; ++i) bss[i] = scale_of(i, kw);
     };
-    for (int kt = 0; kt < KT; kt += 2) {
-        kstep(kt, br[0], bs[0]);
-        kstep(kt + 1, br[1], bs[1]);
+    static_assert(kStages == 4, "the step unrolling below pairs stages with weight register sets");
+    for (int kt = 0; kt < KT; kt += 4) {
+        kstep(kt, 0, br[0], bs[0]);
+        kstep(kt + 1, 1, br[1], bs[1]);
+        if (kt + 2 < KT) {
+            kstep(kt + 2, 2, br[0], bs[0]);
+            kstep(kt + 3, 3, br[1], bs[1]);
+        }
     }
+    // the ring's last (unused) loads must land before the buffers are reused
+    vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
 
     // Epilogue.  The MFMAs compute C^T (weights as the A operand), so lane l
     // holds row mi*32 + l%32 and, per group q, the four consecutive columns
     // 8q + 4(l/32) .. +3 of each 32-column panel.  The tile goes through LDS
-    // (free after the last K-step's barrier) so that every global store
+    // (free once the ring has drained) so that every global store
     // instruction writes whole contiguous row segments.
-    const int m = lane & 31;
     if (GU) {
         // h = silu(g) * u, the whole 128 x 128 bf16 tile, rows padded by 16 bytes
         constexpr int LDH = kBN / 2 + 8;
-        uint16_t* Hs = As[0];
-        static_assert(kBM * LDH <= 2 * kBM * kLDK, "h tile must fit the A buffers");
+        uint16_t* Hs = &As[0][0];
+        static_assert(kBM * LDH <= kStages * kBM * kBK, "h tile must fit the A buffers");
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -311,8 +360,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
     } else {
         // per wave: 32 rows x 64 bf16 columns at a time, rows padded by 16 bytes
         constexpr int LDY = 64 + 8;
-        uint16_t* Ys = As[0] + w * 32 * LDY;
-        static_assert(4 * 32 * LDY <= 2 * kBM * kLDK, "y tiles must fit the A buffers");
+        uint16_t* Ys = &As[0][0] + w * 32 * LDY;
+        static_assert(4 * 32 * LDY <= kStages * kBM * kBK, "y tiles must fit the A buffers");
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -369,6 +418,9 @@ hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     a.k = c->sh.top_k;
     a.d = c->sh.d_model;
     a.f = c->sh.d_ff;
+    // creation keeps both below 4 GiB
+    a.x_bytes = (uint32_t)((int64_t)T * a.d * 2);
+    a.h_bytes = (uint32_t)((int64_t)c->cap * a.f * 2);
     a.meta = c->plan.meta;
     a.active_slot = c->plan.active_slot;
     a.seg = c->plan.seg;
