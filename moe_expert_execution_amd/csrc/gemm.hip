@@ -255,30 +255,40 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
             af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[stage][(mi * 32 + m) * kBK + ((c ^ fm) << 3)]);
     };
     bf16x8_t af[2][4];
+    // A(0) has landed once only A(1) and A(2) may be outstanding
+    vm_wait<8>();
+    __builtin_amdgcn_s_barrier();
+    read_a(af[0], 0, 0);
 
     // One K-step.  Vector-memory operations of a wave complete in issue order,
-    // so "A of step kt has landed" is a count of the loads issued after it:
-    // the prologue issues B(0), B(1), A(0), A(1), A(2); each step issues
-    // A(kt + 3) and then its NB weight refills (scale loads, if any, come
-    // after them and only make the count conservative).  After every wave has seen
-    // its own loads land, one barrier publishes the buffer, and also tells
-    // that every wave is done reading the buffer the new A load overwrites.
-    // Instruction order is pinned with scheduling barriers: the compiler would
-    // otherwise sink every prefetch below the last MFMA.
+    // so "A of step kt + 1 has landed" is a count of the loads issued after
+    // it.  A step issues RP weight refills, then (before its last MFMA
+    // group) A(kt + 3), then the last NB - RP refills (scale loads come after
+    // them and only make the count conservative); the prologue issued B(0),
+    // B(1), A(0), A(1), A(2).  After every wave has seen its own loads land,
+    // one barrier publishes buffer kt + 1; it also tells that every wave has
+    // finished step kt - 1, the last reader of the buffer A(kt + 3) refills.
+    // Putting it before the last MFMA group lets the next step's first LDS
+    // reads overlap this step's last MFMAs.  Instruction order is pinned with
+    // scheduling barriers: the compiler would otherwise sink every prefetch
+    // below the last MFMA.
+    constexpr int RP = 2 * (LBK - 1);             // refills issued before A(kt + 3)
     auto kstep = [&](int kt, int stage, u32x4_t (&brs)[2][LBK], typename FR::SRaw (&bss)[2]) {
-        if (kt >= 3) vm_wait<8 + 3 * NB>();
-        else if (kt == 2) vm_wait<8 + 2 * NB>();
-        else if (kt == 1) vm_wait<8 + NB>();
-        else vm_wait<8>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(kt + kStages - 1, (stage + kStages - 1) % kStages);
         const int kw = kt + 2 < KT ? kt + 2 : KT - 1;     // weights refilled for two steps ahead
-        __builtin_amdgcn_sched_barrier(0);
-        read_a(af[0], stage, 0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            if (ks < 3) read_a(af[(ks + 1) & 1], stage, ks + 1);
+            if (ks < 3) {
+                read_a(af[(ks + 1) & 1], stage, ks + 1);
+            } else {
+                if (kt >= 2) vm_wait<2 * NB + 4>();
+                else if (kt == 1) vm_wait<NB + 4 + RP>();
+                else vm_wait<4 + RP>();
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                load_a(kt + 3, (stage + 3) % kStages);
+                __builtin_amdgcn_sched_barrier(0);
+                read_a(af[0], (stage + 1) % kStages, 0);
+            }
             const bf16x8_t b0 = b_frag<FMT>(brs[0], ks, bss[0]);
             const bf16x8_t b1 = b_frag<FMT>(brs[1], ks, bss[1]);
 #pragma unroll
@@ -293,19 +303,15 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
                 for (int i = 0; i < 2; ++i)
                     brs[i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(kw * LBK + j) * 1024);
             }
-            // order inside the step: the next MFMA step's LDS reads interleaved
+            // order inside the group: the next group's LDS reads interleaved
             // with the first MFMAs, then the rest, then the refill loads
-            if (ks < 3) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            } else {
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
             }
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);           // global loads
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);       // global loads
             __builtin_amdgcn_sched_barrier(0);
         }
         // the refilled set's scales, loaded straight into the registers that
