@@ -433,6 +433,33 @@ def formats_bench(args):
     return out
 
 
+def miss_replay_bench():
+    """Decode-time miss rate vs cache capacity for four placement policies on
+    identical traces: the decode workload's AR(1) routing (64 prompt steps,
+    then 256 decode steps over 48 layers) and a Zipf(1.1) popularity (one
+    layer of 256 experts; a 512-token prompt, then 2048 decode steps)."""
+    import synth
+    from moe_expert_execution_amd import replay as R
+    out = {}
+    t0 = time.perf_counter()
+    cfg = synth.CONFIGS["decode"]
+    prompt, trace = R.record_decode_trace(cfg, 64, 256)
+    out["ar1"] = {"workload": f"decode AR(1) routing, L={cfg.layers}, E={cfg.E}, top-{cfg.k}, 256 steps after a "
+                              f"64-step prompt; profile {cfg.bp_mbps // 1000}/{cfg.bh_mbps // 1000} GB/s",
+                  "rows": R.miss_table(prompt, trace, cfg.E, cfg.k, cfg.bp_mbps, cfg.bh_mbps, extra_slots=(cfg.slots,))}
+    cfg = synth.CONFIGS["fp8"]
+    prompt, trace = R.record_zipf_trace(cfg, 512, 2048)
+    out["zipf"] = {"workload": f"Zipf(1.1) popularity, L=1, E={cfg.E}, top-{cfg.k}, 2048 steps after a 512-token "
+                               f"prompt; profile {cfg.bp_mbps // 1000}/{cfg.bh_mbps // 1000} GB/s",
+                   "rows": R.miss_table(prompt, trace, cfg.E, cfg.k, cfg.bp_mbps, cfg.bh_mbps, extra_slots=(cfg.slots,))}
+    for name, v in out.items():
+        log(f"miss replay {name}: " + "; ".join(
+            f"{r['capacity']:.0%} ft {r['freetoken']:.2f} lru {r['lru']:.2f} prefill {r['prefill']:.2f} "
+            f"load {r['load']:.2f}" for r in v["rows"]))
+    log(f"miss replay took {time.perf_counter() - t0:.1f}s")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +473,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (kernel work)")
     ap.add_argument("--formats", action="store_true",
                     help="only run the block-FP8 and MXFP4 kernel measurements (one resident layer each)")
+    ap.add_argument("--miss-replay", action="store_true",
+                    help="only replay routing traces through the placement policies (miss rate vs capacity)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -472,6 +501,9 @@ def main():
 
     if args.formats:
         print(json.dumps({"formats": formats_bench(args)}), flush=True)
+        return
+    if args.miss_replay:
+        print(json.dumps({"miss_replay": miss_replay_bench()}), flush=True)
         return
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_bench(args)}), flush=True)
