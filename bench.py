@@ -433,6 +433,82 @@ def formats_bench(args):
     return out
 
 
+def buffer_ablation_bench(Ts=(4096, 8192, 16384)):
+    """The prefill stream (24 layers of the prefill configuration from pinned
+    host banks) with the full-layer double buffer and with one buffer, at
+    several chunk lengths: tokens/s of each and the one-buffer slowdown."""
+    import numpy as np
+    import torch
+
+    import moe_expert_execution_amd as M
+    import synth
+    from moe_expert_execution_amd.tensors import PinnedBank, SlotCache
+
+    cfg = synth.CONFIGS["prefill"]
+    L, E, k, d, f, S = cfg.stream_layers, cfg.E, cfg.k, cfg.d, cfg.f, cfg.S
+    Tm = max(Ts)
+    bank = PinnedBank(L * E * S)
+    synth.bank(cfg.with_(layers=L), out=bank.records(S), nthreads=min(16, len(os.sched_getaffinity(0))))
+    sc = SlotCache(L, E, k, d, f, "bf16", bank.ptr, 2 * E, Tm, cfg.bp_mbps, cfg.bh_mbps)
+    h, shp = sc.handle, sc.shape
+    stream = torch.cuda.current_stream().cuda_stream
+    x = torch.from_numpy(synth.tokens(cfg, Tm, 7).view(np.int16)).cuda()
+    ids = torch.empty((L, Tm, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, Tm, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((Tm, d), dtype=torch.int16, device="cuda")
+    for l in range(L):     # routing is per token: the first T rows are the routes of a T-token chunk
+        wr = torch.from_numpy(synth.router(cfg, l).view(np.int16)).cuda()
+        M.ft_moe_route(shp, x.data_ptr(), wr.data_ptr(), Tm, ids[l].data_ptr(), w[l].data_ptr(), stream)
+    torch.cuda.synchronize()
+
+    def stream_pass(T, flags):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for l in range(L):
+            M.ft_moe_forward(h, l, M.FT_MODE_STREAMED | M.FT_PREFETCH_NEXT | flags, x.data_ptr(), ids[l].data_ptr(),
+                             w[l].data_ptr(), T, y.data_ptr(), stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    stream_pass(Ts[0], 0)      # warm-up
+    rows = []
+    for T in Ts:
+        t2 = stream_pass(T, 0)
+        t1 = stream_pass(T, M.FT_SINGLE_BUFFER)
+        rows.append({"T": T, "two_buffers_s": t2, "one_buffer_s": t1, "two_buffers_tokens_per_s": T / t2,
+                     "one_buffer_tokens_per_s": T / t1, "one_buffer_slowdown": 1.0 - t2 / t1,
+                     "pcie_gbs_two_buffers": L * E * S / t2 / 1e9})
+        log(f"buffer ablation T={T}: two buffers {T / t2:.0f} tok/s ({t2:.3f}s), one buffer {T / t1:.0f} tok/s "
+            f"({t1:.3f}s): {1.0 - t2 / t1:.1%} slower")
+    # prefill-warms-decode variant: after a streamed chunk, decode control over
+    # the same layers' AR(1) routing, with the streamed layers left volatile
+    # (the default) or registered as residents (FT_WARM_DECODE)
+    from moe_expert_execution_amd import replay as R
+    _, trace = R.record_decode_trace(cfg.with_(layers=L), 0, 32)
+    dev_trace = torch.from_numpy(trace).cuda()
+    warm = {}
+    for name, flag in (("volatile", 0), ("warm", M.FT_WARM_DECODE)):
+        for l in range(L):
+            M.ft_moe_forward(h, l, M.FT_MODE_STREAMED | M.FT_PREFETCH_NEXT | flag, x.data_ptr(), ids[l].data_ptr(),
+                             w[l].data_ptr(), Ts[0], y.data_ptr(), stream)
+        s0 = M.ft_cache_stats(h)
+        work = dev_trace.clone()
+        for st_ in range(trace.shape[0]):
+            for l in range(L):
+                M.ft_cache_classify(h, l, work[st_, l].data_ptr(), 1, None, stream)
+        s1 = M.ft_cache_stats(h)
+        warm[name] = {"misses": s1.misses - s0.misses, "unique": s1.unique - s0.unique,
+                      "miss_rate": (s1.misses - s0.misses) / (s1.unique - s0.unique)}
+    log(f"decode after a streamed prefill ({trace.shape[0]} steps x {L} layers, {2 * E} slots): miss rate "
+        f"{warm['volatile']['miss_rate']:.3f} with volatile buffers, {warm['warm']['miss_rate']:.3f} with the last "
+        f"two layers registered")
+    assert M.ft_cache_stats(h).error_flags == 0
+    sc.close()
+    bank.close()
+    return {"workload": f"prefill stream, {L} layers of d={d}, E={E}, top-{k}, f={f}, bf16 from pinned host banks",
+            "rows": rows, "decode_after_prefill": warm}
+
+
 def miss_replay_bench():
     """Decode-time miss rate vs cache capacity for four placement policies on
     identical traces: the decode workload's AR(1) routing (64 prompt steps,
@@ -473,6 +549,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (kernel work)")
     ap.add_argument("--formats", action="store_true",
                     help="only run the block-FP8 and MXFP4 kernel measurements (one resident layer each)")
+    ap.add_argument("--buffer-ablation", action="store_true",
+                    help="only stream the prefill layers with two buffers and with one, at T = 4k, 8k, 16k")
     ap.add_argument("--miss-replay", action="store_true",
                     help="only replay routing traces through the placement policies (miss rate vs capacity)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -504,6 +582,9 @@ def main():
         return
     if args.miss_replay:
         print(json.dumps({"miss_replay": miss_replay_bench()}), flush=True)
+        return
+    if args.buffer_ablation:
+        print(json.dumps({"buffer_ablation": buffer_ablation_bench()}), flush=True)
         return
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_bench(args)}), flush=True)

@@ -80,7 +80,9 @@ enum { FT_HIT = 0, FT_FILL = 1, FT_CPU = 2 };
 enum {
     FT_MODE_CACHED = 0,      /* consume routes rewritten by ft_cache_classify    */
     FT_MODE_STREAMED = 1,    /* compute from the full-layer buffer of `layer`    */
-    FT_PREFETCH_NEXT = 0x100 /* STREAMED: also enqueue layer+1's load            */
+    FT_PREFETCH_NEXT = 0x100,/* STREAMED: also enqueue layer+1's load            */
+    FT_SINGLE_BUFFER = 0x200,/* STREAMED: one full-layer buffer (the ablation)  */
+    FT_WARM_DECODE = 0x400   /* STREAMED: the streamed layer stays resident     */
 };
 
 /* Output of one classify call: caller-owned DEVICE arrays of `capacity`
@@ -235,8 +237,19 @@ ft_status ft_cache_classify(ft_cache* cache, int32_t layer, int32_t* ids, int32_
  *   fence).  With FT_PREFETCH_NEXT the load of layer+1 into the other buffer
  *   is enqueued after this layer's compute is issued, so that it overlaps it
  *   ("Making Large MoE Models Practical on a Single Machine", section 2).
+ *   With FT_SINGLE_BUFFER (needs num_slots >= E) every layer uses buffer 0,
+ *   so a layer's load waits for the previous layer's compute and no transfer
+ *   overlaps compute: the one-buffer ablation of the txtmix article's
+ *   "prefill 不是稀疏的" section (its −19/−25/−26% at 4k/8k/16k tokens).
+ *   With FT_WARM_DECODE the layer's experts in the buffer become decode
+ *   residents after its compute (a variant: the pages leave buffer contents
+ *   volatile but note that a full-layer prefill may warm experts for the
+ *   next phase, "The Expert Cache That Follows the Router", paragraph on the
+ *   costs of flexibility): expert e in ascending order is registered when it
+ *   is resident nowhere, at slot b*E + e with stamp clock + e; the clock
+ *   then advances by E.  Reloading the buffer evicts them again.
  * x [T x d] bf16, routes [T x k] int32, w [T x k] fp32, y [T x d] bf16: device.
- * Errors: FT_ERR_ARG, FT_ERR_STATE, FT_ERR_HIP.
+ * Errors: FT_ERR_ARG (also flags with CACHED mode), FT_ERR_STATE, FT_ERR_HIP.
  * ------------------------------------------------------------------------- */
 ft_status ft_moe_forward(ft_cache* cache, int32_t layer, int32_t mode, const uint16_t* x,
                          const int32_t* routes, const float* w, int32_t T, uint16_t* y, void* stream);

@@ -19,7 +19,7 @@ FT_OK, FT_ERR_ARG, FT_ERR_NOMEM, FT_ERR_HIP, FT_ERR_STATE, FT_ERR_UNSUPPORTED = 
 FT_FMT_BF16, FT_FMT_FP8_B128, FT_FMT_MXFP4_B32 = 0, 1, 2
 FMT = {"bf16": FT_FMT_BF16, "fp8": FT_FMT_FP8_B128, "mxfp4": FT_FMT_MXFP4_B32}
 FT_HIT, FT_FILL, FT_CPU = 0, 1, 2
-FT_MODE_CACHED, FT_MODE_STREAMED, FT_PREFETCH_NEXT = 0, 1, 0x100
+FT_MODE_CACHED, FT_MODE_STREAMED, FT_PREFETCH_NEXT, FT_SINGLE_BUFFER, FT_WARM_DECODE = 0, 1, 0x100, 0x200, 0x400
 ROUTE_INVALID = -(2 ** 31)
 
 i32, i64, u32, u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p

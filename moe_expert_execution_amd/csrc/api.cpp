@@ -399,7 +399,8 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
     FT_REQUIRE(x && routes && w && y, "null pointer");
     const int m = mode & 0xFF;
     FT_REQUIRE(m == FT_MODE_CACHED || m == FT_MODE_STREAMED, "unknown mode %d", m);
-    FT_REQUIRE((mode & ~0x1FF) == 0, "unknown flags");
+    FT_REQUIRE((mode & ~(0xFF | FT_PREFETCH_NEXT | FT_SINGLE_BUFFER | FT_WARM_DECODE)) == 0, "unknown flags");
+    FT_REQUIRE(m == FT_MODE_STREAMED || (mode & ~0xFF) == 0, "flags apply to STREAMED mode only");
     hipStream_t st = (hipStream_t)stream;
     const int k = c->sh.top_k;
     const int64_t d = c->sh.d_model;
@@ -432,19 +433,22 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         FT_HIP(launch_combine(c, routes, w, T, hs.P, y, st));
         return FT_OK;
     }
-    // STREAMED: full-layer buffer layer % 2
+    // STREAMED: full-layer buffer layer % 2 (buffer 0 for every layer with
+    // FT_SINGLE_BUFFER, whose loads then wait for the previous layer's compute)
     ft_status fs = flush_fill(c, st);
     if (fs != FT_OK) return fs;
     const int E = c->sh.experts;
-    if (c->N < 2 * (int64_t)E) {
-        set_error("STREAMED mode needs num_slots >= 2E (%lld < %d)", (long long)c->N, 2 * E);
+    const bool single = (mode & FT_SINGLE_BUFFER) != 0;
+    const int64_t need = single ? (int64_t)E : 2 * (int64_t)E;
+    if (c->N < need) {
+        set_error("STREAMED mode needs num_slots >= %lld (%lld slots)", (long long)need, (long long)c->N);
         return FT_ERR_STATE;
     }
     if (!gemv && (int64_t)T * k > kSmallPlanRoutes && E > 8192) {
         set_error("too many experts for the chunked planner");
         return FT_ERR_UNSUPPORTED;
     }
-    const int b = layer % 2;
+    const int b = single ? 0 : layer % 2;
     if (c->buf_layer[b] != layer) {
         ft_status s = enqueue_load(c, layer, b, st);
         if (s != FT_OK) return s;
@@ -454,10 +458,11 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
                        nullptr, st));
     FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
     FT_HIP(launch_combine(c, routes, w, T, nullptr, y, st));
+    if (mode & FT_WARM_DECODE) FT_HIP(launch_register(c, layer, b, st));
     FT_HIP(hipEventRecord(c->release[b], st));
     c->release_recorded[b] = true;
     if ((mode & FT_PREFETCH_NEXT) && layer + 1 < c->sh.layers) {
-        const int nb = (layer + 1) % 2;
+        const int nb = single ? 0 : (layer + 1) % 2;
         if (c->buf_layer[nb] != layer + 1) {
             ft_status s = enqueue_load(c, layer + 1, nb, st);
             if (s != FT_OK) return s;

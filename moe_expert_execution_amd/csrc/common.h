@@ -171,6 +171,7 @@ hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, 
                            hipStream_t st);
 hipError_t launch_fill(ft_cache* c, hipStream_t st, TimedLaunch tl = TimedLaunch());
 hipError_t launch_invalidate(ft_cache* c, int buf, hipStream_t st);
+hipError_t launch_register(ft_cache* c, int layer, int buf, hipStream_t st);
 hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t S, const int32_t* src_slots,
                                 int n, hipStream_t st);
 // plan: routes -> active slots, sorted rows, tiles.  slot_base >= 0 means routes

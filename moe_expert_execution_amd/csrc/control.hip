@@ -341,6 +341,33 @@ __global__ void invalidate_kernel(int32_t s0, int32_t E, int32_t* slot_for_id, i
     if (threadIdx.x == 0) atomicAdd(&counters[C_STREAMED], 1ull);
 }
 
+// Prefill-warms-decode variant: the layer just computed from a full-layer
+// buffer (slots s0 .. s0 + E - 1, expert e in slot s0 + e) becomes a set of
+// decode residents.  Expert e is registered when it is resident nowhere and
+// its buffer slot is free (the load cleared it), with stamp clock + e; the
+// clock then advances by E.  One workgroup; the flat ids are distinct, so the
+// threads touch distinct entries.
+__global__ void register_kernel(int32_t layer, int32_t s0, int32_t E, int32_t* slot_for_id, int32_t* id_of_slot,
+                                uint64_t* stamp, uint64_t* clock, int32_t* errflag) {
+    __shared__ uint64_t clk;
+    if (threadIdx.x == 0) clk = *clock;
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int32_t u = layer * E + e, s = s0 + e;
+        if (slot_for_id[u] < 0 && id_of_slot[s] < 0) {
+            slot_for_id[u] = s;
+            id_of_slot[s] = u;
+            stamp[s] = clk + (uint64_t)e;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint64_t nc = clk + (uint64_t)E;
+        if (nc >= kStampLimit) atomicOr(errflag, 2);
+        *clock = nc;
+    }
+}
+
 // new_pool[i] = old_pool[src_slots[i]] for i < n (whole records).
 __global__ void __launch_bounds__(kFillThreads)
     gather_kernel(const uint8_t* __restrict__ old_pool, uint8_t* __restrict__ new_pool, int64_t S,
@@ -402,6 +429,12 @@ hipError_t launch_fill(ft_cache* c, hipStream_t st, TimedLaunch tl) {
 hipError_t launch_invalidate(ft_cache* c, int buf, hipStream_t st) {
     hipLaunchKernelGGL(invalidate_kernel, dim3(1), dim3(256), 0, st, (int32_t)(buf * c->sh.experts),
                        (int32_t)c->sh.experts, c->slot_for_id, c->id_of_slot, c->stamp, c->counters);
+    return hipGetLastError();
+}
+
+hipError_t launch_register(ft_cache* c, int layer, int buf, hipStream_t st) {
+    hipLaunchKernelGGL(register_kernel, dim3(1), dim3(256), 0, st, (int32_t)layer, (int32_t)(buf * c->sh.experts),
+                       (int32_t)c->sh.experts, c->slot_for_id, c->id_of_slot, c->stamp, c->clock, c->errflag);
     return hipGetLastError();
 }
 

@@ -32,7 +32,8 @@ Readings where the pages are silent (each is a choice of this reference):
 Full-layer buffers ("The Expert Cache That Follows the Router", paragraph on
 prefill buffers, and the hostile-sequence paragraph): buffer b is slots
 [b*E, (b+1)*E); loading a layer into it clears the old owners' maps and
-recency.  Streamed contents are not registered as residents.
+recency.  Streamed contents are not registered as residents, except in the
+prefill-warms-decode variant (register_buffer).
 
 Resize (METAL MEDIA summary item 4; hyper.ai 方法, elastic lifetime): at a safe
 point the cache is rebuilt for a new slot count.  Reading: keep the
@@ -134,10 +135,12 @@ class SlotCacheSim:
 
     # -- full-layer buffers ----------------------------------------------
     def buffer_slots(self, buf: int) -> range:
-        if self.N < 2 * self.E:
-            raise ValueError("full-layer buffers need at least 2E slots")
+        """Slots of full-layer buffer `buf` (buffer 1 exists only with >= 2E
+        slots; the one-buffer variant uses buffer 0 alone and needs >= E)."""
         if buf not in (0, 1):
             raise ValueError("buffer must be 0 or 1")
+        if self.N < (buf + 1) * self.E:
+            raise ValueError("full-layer buffer %d needs at least %d slots" % (buf, (buf + 1) * self.E))
         return range(buf * self.E, (buf + 1) * self.E)
 
     def stream_load(self, buf: int) -> None:
@@ -148,6 +151,22 @@ class SlotCacheSim:
                 self.slot_for_id[old] = -1
             self.id_of_slot[s] = -1
             self.stamp[s] = 0
+
+    def register_buffer(self, buf: int, layer: int) -> None:
+        """Prefill-warms-decode variant (a reading: the pages keep buffer
+        contents volatile, and also say a full-layer prefill may warm experts
+        for the next phase): after `layer` was computed from buffer `buf`,
+        expert e (ascending) becomes a resident in slot buf*E + e with stamp
+        clock + e, unless it is already resident elsewhere or the slot is
+        taken; then the clock advances by E."""
+        E = self.E
+        for e, s in enumerate(self.buffer_slots(buf)):
+            u = layer * E + e
+            if self.slot_for_id[u] < 0 and self.id_of_slot[s] < 0:
+                self.slot_for_id[u] = s
+                self.id_of_slot[s] = u
+                self.stamp[s] = self.clock + e
+        self.clock += E
 
     # -- elastic resize ----------------------------------------------------
     def resize(self, new_slots: int) -> List[Tuple[int, int]]:

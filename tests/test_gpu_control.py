@@ -274,3 +274,68 @@ def test_hostile_invalidation_sequence_gpu():
     finally:
         sc.close()
         bank.close()
+
+
+@gpu
+def test_warm_decode_variant_gpu():
+    """Prefill-warms-decode variant: layers streamed with FT_WARM_DECODE become
+    residents exactly as the oracle's register_buffer says (maps, stamps and
+    clock bit-exact), decode then hits them and computes the right layer, and
+    a later miss takes the empty slots first."""
+    cuda()
+    cfg = synth.CONFIGS["tiny"].with_(layers=3, E=4, k=2, slots=10, bp_mbps=60000, bh_mbps=60000)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, 16, cfg.bp_mbps,
+                   cfg.bh_mbps)
+    sim = OC.SlotCacheSim(cfg.layers, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+    st = torch.cuda.current_stream().cuda_stream
+    n_ids = cfg.layers * cfg.E
+
+    def same_state(what):
+        sfi, ios, stamp, clock = M.ft_cache_snapshot(sc.handle, n_ids, cfg.slots)
+        o_sfi, o_ios, o_stamp, o_clock = sim.arrays()
+        assert np.array_equal(sfi, o_sfi) and np.array_equal(ios, o_ios), what
+        assert np.array_equal(stamp, o_stamp) and clock == o_clock, what
+
+    try:
+        x = synth.tokens(cfg, 2, 3)
+        ids = np.array([[0, 1], [3, 1]], dtype=np.int32)
+        w = np.array([[0.5, 0.5], [0.25, 0.75]], np.float32)
+        xd, wd = dev_u16(x), dev(w)
+
+        def decode_call(layer):
+            idd = dev(ids)
+            y = torch.zeros((2, cfg.d), dtype=torch.int16, device="cuda")
+            M.ft_cache_classify(sc.handle, layer, idd.data_ptr(), 2, None, st)
+            M.ft_moe_forward(sc.handle, layer, M.FT_MODE_CACHED, xd.data_ptr(), idd.data_ptr(), wd.data_ptr(), 2,
+                             y.data_ptr(), st)
+            r = sim.classify(layer, ids)
+            torch.cuda.synchronize()
+            assert np.array_equal(idd.cpu().numpy(), r.routes), f"routes of layer {layer}"
+            assert_close_rel(bf16_bits_to_f64(y), OM.moe_layer(x, ids, w, expert_fn(recs, cfg, layer)), 2e-2,
+                             f"decode layer {layer}")
+            return r
+
+        decode_call(0)
+        same_state("after the first decode call")
+        for layer in (1, 2):
+            idd = dev(ids)
+            y2 = torch.zeros((2, cfg.d), dtype=torch.int16, device="cuda")
+            M.ft_moe_forward(sc.handle, layer, M.FT_MODE_STREAMED | M.FT_WARM_DECODE, xd.data_ptr(), idd.data_ptr(),
+                             wd.data_ptr(), 2, y2.data_ptr(), st)
+            sim.stream_load(layer % 2)
+            sim.register_buffer(layer % 2, layer)
+            torch.cuda.synchronize()
+            same_state(f"after streaming layer {layer}")
+        r = decode_call(1)
+        assert r.hits == 3 and r.m == 0
+        r = decode_call(0)
+        assert r.hits == 0 and r.q == 3 and [v for v, _ in r.fills] == [8, 9, 6]   # empties, then the oldest stamp
+        same_state("after decode on the warmed cache")
+        for v, u in r.fills:
+            assert np.array_equal(M.ft_cache_read_slot(sc.handle, v, cfg.S), recs[u])
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()

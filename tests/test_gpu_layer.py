@@ -100,6 +100,45 @@ def test_prefill_streamed_bf16():
 
 
 @gpu
+def test_prefill_streamed_single_buffer():
+    """The one-buffer ablation: three layers through buffer 0 alone on a cache
+    of exactly E slots (T = 300, every row against the oracle); the double
+    buffer is refused on that cache, and flags are refused in CACHED mode."""
+    cuda()
+    cfg = synth.CONFIGS["prefill"].with_(layers=3, slots=128)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.E, 300, cfg.bp_mbps, cfg.bh_mbps)
+    st = torch.cuda.current_stream().cuda_stream
+    try:
+        T = 300
+        x = synth.tokens(cfg, T, 9, T)
+        xd = dev_u16(x)
+        y = torch.zeros((T, cfg.d), dtype=torch.int16, device="cuda")
+        ids0, w0, _ = OR.route(x, synth.router(cfg, 0), cfg.k)
+        i0, w0d = dev(ids0.astype(np.int32)), dev(w0)
+        lib = M.lib()
+        assert lib.ft_moe_forward(sc.handle, 0, M.FT_MODE_STREAMED, xd.data_ptr(), i0.data_ptr(), w0d.data_ptr(), T,
+                                  y.data_ptr(), st) == M.FT_ERR_STATE
+        assert lib.ft_moe_forward(sc.handle, 0, M.FT_MODE_CACHED | M.FT_SINGLE_BUFFER, xd.data_ptr(), i0.data_ptr(),
+                                  w0d.data_ptr(), T, y.data_ptr(), st) == M.FT_ERR_ARG
+        for l in range(cfg.layers):
+            ids, w, _ = OR.route(x, synth.router(cfg, l), cfg.k)
+            idd, wd = dev(ids.astype(np.int32)), dev(w)
+            M.ft_moe_forward(sc.handle, l, M.FT_MODE_STREAMED | M.FT_SINGLE_BUFFER | M.FT_PREFETCH_NEXT,
+                             xd.data_ptr(), idd.data_ptr(), wd.data_ptr(), T, y.data_ptr(), st)
+            torch.cuda.synchronize()
+            rows = np.arange(T)
+            ref = oracle_rows(x, ids, w, expert_fn(recs, cfg, l, maxsize=130), rows)
+            assert_close_rel(bf16_bits_to_f64(y), ref, TOL["bf16"], f"single buffer layer {l}")
+        s = M.ft_cache_stats(sc.handle)
+        assert s.error_flags == 0 and s.layers_streamed == cfg.layers
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
 @pytest.mark.parametrize("T,steps,nsample", [(1, 6, 1), (64, 3, 4), (2048, 1, 4)])
 def test_fp8_cached(T, steps, nsample):
     """Block-FP8 shape (d=4096, E=256, top-8, f=2048, e4m3 + 128x128 scales),

@@ -134,7 +134,57 @@ def test_stream_invalidation_clears_owners():
     r = sim.classify(0, np.array([[0, 1]]))
     assert r.hits == 0 and r.m == 2
     with pytest.raises(ValueError):
-        SlotCacheSim(1, 4, 7, 1, 1).stream_load(0)
+        SlotCacheSim(1, 4, 7, 1, 1).stream_load(1)     # buffer 1 needs 2E slots
+    with pytest.raises(ValueError):
+        SlotCacheSim(1, 4, 3, 1, 1).stream_load(0)     # buffer 0 needs E
+    SlotCacheSim(1, 4, 4, 1, 1).stream_load(0)         # the one-buffer variant
+
+
+def _check_maps(sim):
+    res = sim.residents()
+    for u, s in res.items():
+        assert sim.id_of_slot[s] == u
+    for s, u in enumerate(sim.id_of_slot):
+        assert u < 0 or sim.slot_for_id[u] == s
+    stamps = [sim.stamp[s] for s in res.values()]
+    assert len(set(stamps)) == len(stamps) and all(0 < t < sim.clock for t in stamps)
+
+
+def test_warm_registers_the_streamed_layer_as_residents():
+    E = 4
+    sim = SlotCacheSim(3, E, 2 * E + 2, 60000, 60000)
+    r = sim.classify(0, np.array([[0, 1]]))               # fills take slots 0, 1
+    assert [v for v, _ in r.fills] == [0, 1] and sim.clock == 3
+    sim.stream_load(1)                                    # layer 1 into buffer 1, then registered
+    sim.register_buffer(1, 1)
+    assert {u: sim.slot_for_id[u] for u in range(4, 8)} == {4: 4, 5: 5, 6: 6, 7: 7}
+    assert [sim.stamp[s] for s in range(4, 8)] == [3, 4, 5, 6] and sim.clock == 7
+    sim.stream_load(0)                                    # layer 2 into buffer 0 evicts layer 0's fills
+    sim.register_buffer(0, 2)
+    assert sim.slot_for_id[0] == sim.slot_for_id[1] == -1
+    assert sim.residents() == {4: 4, 5: 5, 6: 6, 7: 7, 8: 0, 9: 1, 10: 2, 11: 3}
+    _check_maps(sim)
+    r = sim.classify(1, np.array([[0, 3]]))
+    assert r.cls == [HIT, HIT] and r.slot == [4, 7]
+    r = sim.classify(0, np.array([[0]]))                  # a miss: the empty slots 8, 9 go first
+    assert r.cls == [FILL] and r.fills == [(8, 0)]
+    _check_maps(sim)
+
+
+def test_warm_skips_experts_resident_elsewhere():
+    E = 4
+    sim = SlotCacheSim(2, E, 2 * E + 1, 60000, 60000)
+    sim.classify(1, np.array([[2]]))                      # layer 1 expert 2 (flat 6) filled into slot 0
+    assert sim.slot_for_id[6] == 0
+    sim.stream_load(1)
+    clock = sim.clock
+    sim.register_buffer(1, 1)
+    assert sim.slot_for_id[6] == 0 and sim.id_of_slot[6] == -1 and sim.stamp[6] == 0
+    assert [sim.slot_for_id[u] for u in (4, 5, 7)] == [4, 5, 7]
+    assert sim.clock == clock + E
+    sim.register_buffer(1, 1)                             # again: nothing new, the clock still advances
+    assert sim.clock == clock + 2 * E and len(sim.residents()) == 4
+    _check_maps(sim)
 
 
 def test_resize_keeps_most_recent_packed():
