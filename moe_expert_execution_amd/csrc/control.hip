@@ -300,6 +300,7 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
 constexpr int kFillThreads = 256;
 constexpr int64_t kFillChunk = 64 * 1024;
 constexpr int kFillBlocks = 512;
+typedef uint32_t fill_vec_t __attribute__((ext_vector_type(4)));   // 16 bytes
 
 __global__ void __launch_bounds__(kFillThreads)
     fill_kernel(const int32_t* wl_counts, const int32_t* wl_slot, const int32_t* wl_src,
@@ -311,19 +312,22 @@ __global__ void __launch_bounds__(kFillThreads)
         const int64_t i = c / cpr;
         const int64_t off = (c - i * cpr) * kFillChunk;
         const int64_t len = (S - off) < kFillChunk ? (S - off) : kFillChunk;
-        const uint4* src = reinterpret_cast<const uint4*>(bank + (int64_t)wl_src[i] * S + off);
-        uint4* dst = reinterpret_cast<uint4*>(pool + (int64_t)wl_slot[i] * S + off);
+        const fill_vec_t* src = reinterpret_cast<const fill_vec_t*>(bank + (int64_t)wl_src[i] * S + off);
+        fill_vec_t* dst = reinterpret_cast<fill_vec_t*>(pool + (int64_t)wl_slot[i] * S + off);
         const int64_t n16 = len / 16;
         int64_t b = threadIdx.x;
+        // streaming (nontemporal) stores: the records go to HBM without
+        // leaving dirty L2 lines whose write-back would delay the expert
+        // kernels that read them next
         for (; b + 3 * kFillThreads < n16; b += 4 * kFillThreads) {
-            uint4 v0 = src[b], v1 = src[b + kFillThreads], v2 = src[b + 2 * kFillThreads],
-                  v3 = src[b + 3 * kFillThreads];
-            dst[b] = v0;
-            dst[b + kFillThreads] = v1;
-            dst[b + 2 * kFillThreads] = v2;
-            dst[b + 3 * kFillThreads] = v3;
+            const fill_vec_t v0 = src[b], v1 = src[b + kFillThreads], v2 = src[b + 2 * kFillThreads],
+                             v3 = src[b + 3 * kFillThreads];
+            __builtin_nontemporal_store(v0, dst + b);
+            __builtin_nontemporal_store(v1, dst + b + kFillThreads);
+            __builtin_nontemporal_store(v2, dst + b + 2 * kFillThreads);
+            __builtin_nontemporal_store(v3, dst + b + 3 * kFillThreads);
         }
-        for (; b < n16; b += kFillThreads) dst[b] = src[b];
+        for (; b < n16; b += kFillThreads) __builtin_nontemporal_store(src[b], dst + b);
     }
 }
 
