@@ -213,6 +213,46 @@ def decode_bench(args):
             f"{args.steps / el:.1f} tok/s, fills {res['measured_profile']['fills_per_call']:.2f} and host experts "
             f"{res['measured_profile']['host_experts_per_call']:.2f} per layer call")
     sc.close()
+    if not args.no_graph:
+        # (4) the same steps from a cold cache, each one a replay of a HIP graph
+        # that holds one whole decode step (48 x route + classify + forward;
+        # the host experts run in captured host functions); the step's hidden
+        # states are copied into the graph's input buffer first
+        sc = new_cache()
+        h = sc.handle
+        xg = torch.empty((L, d), dtype=torch.int16, device="cuda")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gst = torch.cuda.current_stream().cuda_stream
+            for l in range(L):
+                M.ft_moe_route(sc.shape, xg[l].data_ptr(), wr[l].data_ptr(), 1, ids[l].data_ptr(), w[l].data_ptr(),
+                               gst)
+                M.ft_cache_classify(h, l, ids[l].data_ptr(), 1, None, gst)
+                M.ft_moe_forward(h, l, M.FT_MODE_CACHED, xg[l].data_ptr(), ids[l].data_ptr(), w[l].data_ptr(), 1,
+                                 y[l].data_ptr(), gst)
+        torch.cuda.synchronize()
+        for s_ in range(args.warmup):
+            xg.copy_(xs[:, s_])
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = M.ft_cache_stats(h).as_dict()
+        t0 = time.perf_counter()
+        for s_ in range(args.warmup, steps):
+            xg.copy_(xs[:, s_])
+            g.replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        g1 = M.ft_cache_stats(h).as_dict()
+        assert g1["error_flags"] == 0, g1
+        res["graph"] = {"tokens_per_s": args.steps / el, "ms_per_step": el / args.steps * 1e3,
+                        "miss_rate": (g1["misses"] - g0["misses"]) / max(g1["unique"] - g0["unique"], 1),
+                        "same_decisions_as_headline": all(g1[k_] - g0[k_] == s1[k_] - s0[k_]
+                                                          for k_ in ("hits", "misses", "fills", "cpu_experts"))}
+        log(f"decode replayed from a HIP graph of one step: {args.steps / el:.1f} tok/s ({el / args.steps * 1e3:.2f} "
+            f"ms/step), same decisions as the eager runs: {res['graph']['same_decisions_as_headline']}")
+        del g
+        sc.close()
     return res, bank, cfg
 
 
@@ -544,6 +584,7 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the decode run replayed from a HIP graph")
     ap.add_argument("--no-measured-profile", action="store_true",
                     help="skip the second decode run with the measured B_P / B_H")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (kernel work)")
@@ -613,6 +654,7 @@ def main():
         "kernel_timed_run_ms_per_step": dec["ms_per_step_kernel_timed_run"],
         "branches": dec["branches"],
         "measured_profile": dec.get("measured_profile"),
+        "graph": dec.get("graph"),
         "prefill": pre,
     }
     print(json.dumps(line), flush=True)

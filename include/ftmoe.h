@@ -249,7 +249,18 @@ ft_status ft_cache_classify(ft_cache* cache, int32_t layer, int32_t* ids, int32_
  *   is resident nowhere, at slot b*E + e with stamp clock + e; the clock
  *   then advances by E.  Reloading the buffer evicts them again.
  * x [T x d] bf16, routes [T x k] int32, w [T x k] fp32, y [T x d] bf16: device.
- * Errors: FT_ERR_ARG (also flags with CACHED mode), FT_ERR_STATE, FT_ERR_HIP.
+ * Graph capture: a decode layer step — ft_moe_route, ft_cache_classify and a
+ *   CACHED ft_moe_forward on one stream — may be captured into a HIP graph
+ *   and replayed, so that the step needs no host involvement beyond the
+ *   graph launch ("Making Large MoE Models Practical on a Single Machine",
+ *   section 10; the txtmix article's "CUDA-graph 兼容的 LRU 缓存" section:
+ *   fixed-size device buffers, routing-dependent control as data).  During
+ *   capture the host experts run in a captured host function (each captured
+ *   call keeps its context until ft_cache_destroy; a graph must not be
+ *   replayed after that).  Kernel timing must be off (FT_ERR_STATE);
+ *   STREAMED calls cannot be captured (FT_ERR_UNSUPPORTED).
+ * Errors: FT_ERR_ARG (also flags with CACHED mode), FT_ERR_STATE,
+ *   FT_ERR_UNSUPPORTED, FT_ERR_HIP.
  * ------------------------------------------------------------------------- */
 ft_status ft_moe_forward(ft_cache* cache, int32_t layer, int32_t mode, const uint16_t* x,
                          const int32_t* routes, const float* w, int32_t T, uint16_t* y, void* stream);

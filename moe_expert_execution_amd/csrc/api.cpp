@@ -405,19 +405,29 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
     const int k = c->sh.top_k;
     const int64_t d = c->sh.d_model;
     const bool gemv = T <= kGemvMaxTokens;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    FT_HIP(hipStreamIsCapturing(st, &cap));
+    const bool capturing = cap != hipStreamCaptureStatusNone;
+    if (capturing && c->timing) {
+        set_error("kernel timing must be off while a call is captured into a graph");
+        return FT_ERR_STATE;
+    }
     if (m == FT_MODE_CACHED) {
         // host branch: the planner copies the call's routes, weights and
         // activations into pinned staging and, with the mailbox, posts the
         // call's sequence number; the host workers run the host experts and
-        // leave their partial sums in pinned memory
+        // leave their partial sums in pinned memory.  A call being captured
+        // into a graph uses a host function instead (a graph node that every
+        // replay runs; the mailbox's sequence numbers are fixed per call).
         HostStaging hs = host_branch_staging(c->host);
-        HostSignal sig = host_branch_prepare(c->host, layer, T);
+        HostSignal sig = capturing ? HostSignal{} : host_branch_prepare(c->host, layer, T);
         FT_HIP(launch_plan(c, routes, T, -1, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, w, x, &hs, &sig,
                            st));
         if (!sig.mailbox) {
             FT_HIP(hipEventRecord(c->ev_fwd, st));
             FT_HIP(hipStreamWaitEvent(c->hstream, c->ev_fwd, 0));
-            FT_HIP(host_branch_enqueue(c->host, layer, T, c->hstream));
+            FT_HIP(capturing ? host_branch_enqueue_captured(c->host, layer, T, c->hstream)
+                             : host_branch_enqueue(c->host, layer, T, c->hstream));
             FT_HIP(hipEventRecord(c->ev_host, c->hstream));
         }
         // this layer's fills, then the GPU experts (hits and fills) from the slot pool
@@ -432,6 +442,10 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         }
         FT_HIP(launch_combine(c, routes, w, T, hs.P, y, st));
         return FT_OK;
+    }
+    if (capturing) {
+        set_error("STREAMED calls cannot be captured into a graph (their loads follow host-side buffer state)");
+        return FT_ERR_UNSUPPORTED;
     }
     // STREAMED: full-layer buffer layer % 2 (buffer 0 for every layer with
     // FT_SINGLE_BUFFER, whose loads then wait for the previous layer's compute)

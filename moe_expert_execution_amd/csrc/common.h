@@ -83,6 +83,9 @@ HostSignal host_branch_prepare(HostBranch* hb, int32_t layer, int32_t T);
 // Enqueue the host computation of layer `layer` for T tokens on `stream`
 // (staging must already hold routes, w and x for those tokens).
 hipError_t host_branch_enqueue(HostBranch* hb, int32_t layer, int32_t T, hipStream_t stream);
+// The same for a call being captured into a graph: a host function whose
+// context lives as long as the branch, so the graph can replay it.
+hipError_t host_branch_enqueue_captured(HostBranch* hb, int32_t layer, int32_t T, hipStream_t stream);
 int host_branch_threads(HostBranch* hb);
 // Run one host-branch call on the calling thread (staging must hold its routes,
 // weights and activations); no GPU work may be pending on the host branch.

@@ -23,6 +23,7 @@
 #include <chrono>
 #include <cmath>
 #include <condition_variable>
+#include <memory>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -67,6 +68,14 @@ struct HostBranch {
     // per-call scratch shared by the workers
     std::vector<float> xf;             // [max_tokens x d] fp32 activations of the tokens with host routes
     std::vector<float> hbuf;           // [max_tokens x f] SwiGLU output of the current expert
+    // host-function contexts of calls captured into graphs: each captured
+    // call owns one for the life of the branch (a graph may replay it any
+    // number of times)
+    struct GraphCall {
+        HostBranch* hb;
+        int layer, T;
+    };
+    std::vector<std::unique_ptr<GraphCall>> graph_calls;
     // ring of host-function contexts
     struct Call {
         HostBranch* hb;
@@ -369,6 +378,11 @@ void host_fn(void* p) {
     call->busy.store(0, std::memory_order_release);
 }
 
+void graph_host_fn(void* p) {
+    auto* call = static_cast<HostBranch::GraphCall*>(p);
+    run_call(call->hb, call->layer, call->T);
+}
+
 // Mailbox poller: waits for the GPU to post a sequence number, runs that call,
 // posts it as done.  Every posted number is answered, in order.
 void poller_main(HostBranch* hb, int cpu) {
@@ -523,6 +537,11 @@ hipError_t host_branch_enqueue(HostBranch* hb, int32_t layer, int32_t T, hipStre
     hipError_t e = hipLaunchHostFunc(stream, host_fn, &call);
     if (e != hipSuccess) call.busy.store(0);
     return e;
+}
+
+hipError_t host_branch_enqueue_captured(HostBranch* hb, int32_t layer, int32_t T, hipStream_t stream) {
+    hb->graph_calls.emplace_back(new HostBranch::GraphCall{hb, layer, T});
+    return hipLaunchHostFunc(stream, graph_host_fn, hb->graph_calls.back().get());
 }
 
 }  // namespace ftmoe
