@@ -218,187 +218,198 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
                 ks * kBK * 2, 0, 0);
     };
 
-    f32x16_t acc[4][2];
+    // The tile's MI = ceil(rows_valid / 32) row blocks are all that is
+    // computed: a short last tile of an expert (its few leftover rows) costs
+    // MI / 4 of a full tile's MFMAs.
+    auto body = [&](auto mi_count) {
+        constexpr int MI = decltype(mi_count)::value;
+        f32x16_t acc[MI][2];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
-
-    // Two sets of weight registers, for even and odd K-steps: step kt reads
-    // set kt % 2 and then refills it with K-step kt + 2, so every weight load
-    // has two K-steps to arrive and lands in the registers its consumer reads.
-    u32x4_t br[2][2][LBK];
-    typename FR::SRaw bs[2][2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int j = 0; j < LBK; ++j)
-                br[s2][i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(s2 * LBK + j) * 1024);
-            bs[s2][i] = scale_of(i, s2);
-        }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) load_a(s, s);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // A operand of MFMA step ks for the four row blocks, from buffer `stage`
-    const int m = lane & 31;
-    const int fm = (m & 7) ^ ((m >> 3) & 1);
-    auto read_a = [&](bf16x8_t (&af)[4], int stage, int ks) {
-        const int c = FR::a_koff(ks, g) >> 3;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-            af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[stage][(mi * 32 + m) * kBK + ((c ^ fm) << 3)]);
-    };
-    bf16x8_t af[2][4];
-    // A(0) has landed once only A(1) and A(2) may be outstanding
-    vm_wait<8>();
-    __builtin_amdgcn_s_barrier();
-    read_a(af[0], 0, 0);
-
-    // One K-step.  Vector-memory operations of a wave complete in issue order,
-    // so "A of step kt + 1 has landed" is a count of the loads issued after
-    // it.  A step issues RP weight refills, then (before its last MFMA
-    // group) A(kt + 3), then the last NB - RP refills (scale loads come after
-    // them and only make the count conservative); the prologue issued B(0),
-    // B(1), A(0), A(1), A(2).  After every wave has seen its own loads land,
-    // one barrier publishes buffer kt + 1; it also tells that every wave has
-    // finished step kt - 1, the last reader of the buffer A(kt + 3) refills.
-    // Putting it before the last MFMA group lets the next step's first LDS
-    // reads overlap this step's last MFMAs.  Instruction order is pinned with
-    // scheduling barriers: the compiler would otherwise sink every prefetch
-    // below the last MFMA.
-    constexpr int RP = 2 * (LBK - 1);             // refills issued before A(kt + 3)
-    auto kstep = [&](int kt, int stage, u32x4_t (&brs)[2][LBK], typename FR::SRaw (&bss)[2]) {
-        const int kw = kt + 2 < KT ? kt + 2 : KT - 1;     // weights refilled for two steps ahead
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (ks < 3) {
-                read_a(af[(ks + 1) & 1], stage, ks + 1);
-            } else {
-                if (kt >= 2) vm_wait<2 * NB + 4>();
-                else if (kt == 1) vm_wait<NB + 4 + RP>();
-                else vm_wait<4 + RP>();
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_sched_barrier(0);
-                load_a(kt + 3, (stage + 3) % kStages);
-                __builtin_amdgcn_sched_barrier(0);
-                read_a(af[0], (stage + 1) % kStages, 0);
-            }
-            const bf16x8_t b0 = b_frag<FMT>(brs[0], ks, bss[0]);
-            const bf16x8_t b1 = b_frag<FMT>(brs[1], ks, bss[1]);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, af[ks & 1][mi], acc[mi][0], 0, 0, 0);
-                acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, af[ks & 1][mi], acc[mi][1], 0, 0, 0);
-            }
-            constexpr int kDone = 4 / LBK;                // MFMA steps per lane block
-            if ((ks % kDone) == kDone - 1) {
-                const int j = ks / kDone;
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    brs[i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(kw * LBK + j) * 1024);
-            }
-            // order inside the group: the next group's LDS reads interleaved
-            // with the first MFMAs, then the rest, then the refill loads
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);       // global loads
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // the refilled set's scales, loaded straight into the registers that
-        // step kw reads (a copy would have to wait for the load)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) bss[i] = scale_of(i, kw);
-    };
-    static_assert(kStages == 4, "the step unrolling below pairs stages with weight register sets");
-    for (int kt = 0; kt < KT; kt += 4) {
-        kstep(kt, 0, br[0], bs[0]);
-        kstep(kt + 1, 1, br[1], bs[1]);
-        if (kt + 2 < KT) {
-            kstep(kt + 2, 2, br[0], bs[0]);
-            kstep(kt + 3, 3, br[1], bs[1]);
-        }
-    }
-    // the ring's last (unused) loads must land before the buffers are reused
-    vm_wait<0>();
-    __builtin_amdgcn_s_barrier();
-
-    // Epilogue.  The MFMAs compute C^T (weights as the A operand), so lane l
-    // holds row mi*32 + l%32 and, per group q, the four consecutive columns
-    // 8q + 4(l/32) .. +3 of each 32-column panel.  The tile goes through LDS
-    // (free once the ring has drained) so that every global store
-    // instruction writes whole contiguous row segments.
-    if (GU) {
-        // h = silu(g) * u, the whole 128 x 128 bf16 tile, rows padded by 16 bytes
-        constexpr int LDH = kBN / 2 + 8;
-        uint16_t* Hs = &As[0][0];
-        static_assert(kBM * LDH <= kStages * kBM * kBK, "h tile must fit the A buffers");
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float h[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) h[j] = silu(acc[mi][0][4 * q + j]) * acc[mi][1][4 * q + j];
-                uint2 o;
-                o.x = (uint32_t)f32_to_bf16_rne(h[0]) | ((uint32_t)f32_to_bf16_rne(h[1]) << 16);
-                o.y = (uint32_t)f32_to_bf16_rne(h[2]) | ((uint32_t)f32_to_bf16_rne(h[3]) << 16);
-                *reinterpret_cast<uint2*>(&Hs[(mi * 32 + m) * LDH + 32 * w + 8 * q + 4 * g]) = o;
-            }
-        __syncthreads();
-        // 16 lanes per 256-byte row, 16 rows per pass
-#pragma unroll
-        for (int it = 0; it < kBM / 16; ++it) {
-            const int r = it * 16 + (tid >> 4), c = (tid & 15) * 8;
-            if (r < rows_valid)
-                *reinterpret_cast<u32x4_t*>(a.Hout + (int64_t)(row0 + r) * a.f + nt * (kBN / 2) + c) =
-                    *reinterpret_cast<const u32x4_t*>(&Hs[r * LDH + c]);
-        }
-    } else {
-        // per wave: 32 rows x 64 bf16 columns at a time, rows padded by 16 bytes
-        constexpr int LDY = 64 + 8;
-        uint16_t* Ys = &As[0][0] + w * 32 * LDY;
-        static_assert(4 * 32 * LDY <= kStages * kBM * kBK, "y tiles must fit the A buffers");
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint2 o;
-                    o.x = (uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q]) |
-                          ((uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 1]) << 16);
-                    o.y = (uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 2]) |
-                          ((uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 3]) << 16);
-                    *reinterpret_cast<uint2*>(&Ys[m * LDY + 32 * ni + 8 * q + 4 * g]) = o;
-                }
-            // the wave reads back what it wrote (LDS operations of a wave stay in order)
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // 8 lanes per 128-byte row, 8 rows per pass
+                for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+
+        // Two sets of weight registers, for even and odd K-steps: step kt reads
+        // set kt % 2 and then refills it with K-step kt + 2, so every weight load
+        // has two K-steps to arrive and lands in the registers its consumer reads.
+        u32x4_t br[2][2][LBK];
+        typename FR::SRaw bs[2][2];
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int rr = it * 8 + (lane >> 3), c = (lane & 7) * 8;
-                const int r = mi * 32 + rr;
-                if (r < rows_valid)
-                    *reinterpret_cast<u32x4_t*>(a.Y + (int64_t)(row0 + r) * a.d + nt * kBN + 64 * w + c) =
-                        *reinterpret_cast<const u32x4_t*>(&Ys[rr * LDY + c]);
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int j = 0; j < LBK; ++j)
+                    br[s2][i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(s2 * LBK + j) * 1024);
+                bs[s2][i] = scale_of(i, s2);
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kStages - 1; ++s) load_a(s, s);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // A operand of MFMA step ks for the MI row blocks, from buffer `stage`
+        const int m = lane & 31;
+        const int fm = (m & 7) ^ ((m >> 3) & 1);
+        auto read_a = [&](bf16x8_t (&af)[MI], int stage, int ks) {
+            const int c = FR::a_koff(ks, g) >> 3;
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[stage][(mi * 32 + m) * kBK + ((c ^ fm) << 3)]);
+        };
+        bf16x8_t af[2][MI];
+        // A(0) has landed once only A(1) and A(2) may be outstanding
+        vm_wait<8>();
+        __builtin_amdgcn_s_barrier();
+        read_a(af[0], 0, 0);
+
+        // One K-step.  Vector-memory operations of a wave complete in issue order,
+        // so "A of step kt + 1 has landed" is a count of the loads issued after
+        // it.  A step issues RP weight refills, then (before its last MFMA
+        // group) A(kt + 3), then the last NB - RP refills (scale loads come after
+        // them and only make the count conservative); the prologue issued B(0),
+        // B(1), A(0), A(1), A(2).  After every wave has seen its own loads land,
+        // one barrier publishes buffer kt + 1; it also tells that every wave has
+        // finished step kt - 1, the last reader of the buffer A(kt + 3) refills.
+        // Putting it before the last MFMA group lets the next step's first LDS
+        // reads overlap this step's last MFMAs.  Instruction order is pinned with
+        // scheduling barriers: the compiler would otherwise sink every prefetch
+        // below the last MFMA.
+        constexpr int RP = 2 * (LBK - 1);             // refills issued before A(kt + 3)
+        auto kstep = [&](int kt, int stage, u32x4_t (&brs)[2][LBK], typename FR::SRaw (&bss)[2]) {
+            const int kw = kt + 2 < KT ? kt + 2 : KT - 1;     // weights refilled for two steps ahead
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks < 3) {
+                    read_a(af[(ks + 1) & 1], stage, ks + 1);
+                } else {
+                    if (kt >= 2) vm_wait<2 * NB + 4>();
+                    else if (kt == 1) vm_wait<NB + 4 + RP>();
+                    else vm_wait<4 + RP>();
+                    __builtin_amdgcn_s_barrier();
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_a(kt + 3, (stage + 3) % kStages);
+                    __builtin_amdgcn_sched_barrier(0);
+                    read_a(af[0], (stage + 1) % kStages, 0);
+                }
+                const bf16x8_t b0 = b_frag<FMT>(brs[0], ks, bss[0]);
+                const bf16x8_t b1 = b_frag<FMT>(brs[1], ks, bss[1]);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, af[ks & 1][mi], acc[mi][0], 0, 0, 0);
+                    acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, af[ks & 1][mi], acc[mi][1], 0, 0, 0);
+                }
+                constexpr int kDone = 4 / LBK;                // MFMA steps per lane block
+                if ((ks % kDone) == kDone - 1) {
+                    const int j = ks / kDone;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        brs[i][j] = *reinterpret_cast<const u32x4_t*>(bp[i] + (int64_t)(kw * LBK + j) * 1024);
+                }
+                // order inside the group: the next group's LDS reads interleaved
+                // with the first MFMAs, then the rest, then the refill loads
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, MI, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);       // global loads
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the refilled set's scales, loaded straight into the registers that
+            // step kw reads (a copy would have to wait for the load)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) bss[i] = scale_of(i, kw);
+        };
+        static_assert(kStages == 4, "the step unrolling below pairs stages with weight register sets");
+        for (int kt = 0; kt < KT; kt += 4) {
+            kstep(kt, 0, br[0], bs[0]);
+            kstep(kt + 1, 1, br[1], bs[1]);
+            if (kt + 2 < KT) {
+                kstep(kt + 2, 2, br[0], bs[0]);
+                kstep(kt + 3, 3, br[1], bs[1]);
+            }
         }
-    }
+        // the ring's last (unused) loads must land before the buffers are reused
+        vm_wait<0>();
+        __builtin_amdgcn_s_barrier();
+
+        // Epilogue.  The MFMAs compute C^T (weights as the A operand), so lane l
+        // holds row mi*32 + l%32 and, per group q, the four consecutive columns
+        // 8q + 4(l/32) .. +3 of each 32-column panel.  The tile goes through LDS
+        // (free once the ring has drained) so that every global store
+        // instruction writes whole contiguous row segments.
+        if (GU) {
+            // h = silu(g) * u, the whole 128 x 128 bf16 tile, rows padded by 16 bytes
+            constexpr int LDH = kBN / 2 + 8;
+            uint16_t* Hs = &As[0][0];
+            static_assert(kBM * LDH <= kStages * kBM * kBK, "h tile must fit the A buffers");
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float h[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) h[j] = silu(acc[mi][0][4 * q + j]) * acc[mi][1][4 * q + j];
+                    uint2 o;
+                    o.x = (uint32_t)f32_to_bf16_rne(h[0]) | ((uint32_t)f32_to_bf16_rne(h[1]) << 16);
+                    o.y = (uint32_t)f32_to_bf16_rne(h[2]) | ((uint32_t)f32_to_bf16_rne(h[3]) << 16);
+                    *reinterpret_cast<uint2*>(&Hs[(mi * 32 + m) * LDH + 32 * w + 8 * q + 4 * g]) = o;
+                }
+            __syncthreads();
+            // 16 lanes per 256-byte row, 16 rows per pass
+#pragma unroll
+            for (int it = 0; it < MI * 2; ++it) {
+                const int r = it * 16 + (tid >> 4), c = (tid & 15) * 8;
+                if (r < rows_valid)
+                    *reinterpret_cast<u32x4_t*>(a.Hout + (int64_t)(row0 + r) * a.f + nt * (kBN / 2) + c) =
+                        *reinterpret_cast<const u32x4_t*>(&Hs[r * LDH + c]);
+            }
+        } else {
+            // per wave: 32 rows x 64 bf16 columns at a time, rows padded by 16 bytes
+            constexpr int LDY = 64 + 8;
+            uint16_t* Ys = &As[0][0] + w * 32 * LDY;
+            static_assert(4 * 32 * LDY <= kStages * kBM * kBK, "y tiles must fit the A buffers");
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint2 o;
+                        o.x = (uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q]) |
+                              ((uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 1]) << 16);
+                        o.y = (uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 2]) |
+                              ((uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 3]) << 16);
+                        *reinterpret_cast<uint2*>(&Ys[m * LDY + 32 * ni + 8 * q + 4 * g]) = o;
+                    }
+                // the wave reads back what it wrote (LDS operations of a wave stay in order)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                // 8 lanes per 128-byte row, 8 rows per pass
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int rr = it * 8 + (lane >> 3), c = (lane & 7) * 8;
+                    const int r = mi * 32 + rr;
+                    if (r < rows_valid)
+                        *reinterpret_cast<u32x4_t*>(a.Y + (int64_t)(row0 + r) * a.d + nt * kBN + 64 * w + c) =
+                            *reinterpret_cast<const u32x4_t*>(&Ys[rr * LDY + c]);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
+    };
+    const int nmi = (rows_valid + 31) >> 5;
+    if (nmi >= 4) body(std::integral_constant<int, 4>{});
+    else if (nmi == 3) body(std::integral_constant<int, 3>{});
+    else if (nmi == 2) body(std::integral_constant<int, 2>{});
+    else body(std::integral_constant<int, 1>{});
 }
 
 template <int FMT>
