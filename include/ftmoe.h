@@ -124,7 +124,9 @@ typedef struct {
     uint64_t clock;          /* LRU clock (starts at 1)                          */
     int32_t error_flags;     /* sticky device flags: 1 = expert id out of range,
                                 2 = LRU clock past 2^40, 4 = repeated expert in a
-                                token's routes (the repeat is dropped)          */
+                                token's routes (the repeat is dropped), 8 = a
+                                graph-replayed call gave up waiting for the
+                                host experts (seconds; its output is invalid) */
     int32_t num_slots;
     uint64_t host_experts;   /* expert FFNs run by the host workers               */
     uint64_t host_bytes;     /* expert-record bytes the host workers read         */
@@ -254,11 +256,16 @@ ft_status ft_cache_classify(ft_cache* cache, int32_t layer, int32_t* ids, int32_
  *   and replayed, so that the step needs no host involvement beyond the
  *   graph launch ("Making Large MoE Models Practical on a Single Machine",
  *   section 10; the txtmix article's "CUDA-graph 兼容的 LRU 缓存" section:
- *   fixed-size device buffers, routing-dependent control as data).  During
- *   capture the host experts run in a captured host function (each captured
- *   call keeps its context until ft_cache_destroy; a graph must not be
- *   replayed after that).  Kernel timing must be off (FT_ERR_STATE);
- *   STREAMED calls cannot be captured (FT_ERR_UNSUPPORTED).
+ *   fixed-size device buffers, routing-dependent control as data).  A captured
+ *   call hands its host experts to the polling host thread through the
+ *   mailbox with a number drawn from a device counter (so every replay posts
+ *   a new one), and a one-wave kernel polls for the answer, bounded: after a
+ *   few seconds it sets error flag 8 and lets the stream go on.  With stream
+ *   host functions (FTMOE_HOST_SIGNAL=callback) the host experts become a
+ *   captured host function instead (its context lives until
+ *   ft_cache_destroy).  A graph must not be replayed after ft_cache_destroy.
+ *   Kernel timing must be off (FT_ERR_STATE); STREAMED calls cannot be
+ *   captured (FT_ERR_UNSUPPORTED).
  * Errors: FT_ERR_ARG (also flags with CACHED mode), FT_ERR_STATE,
  *   FT_ERR_UNSUPPORTED, FT_ERR_HIP.
  * ------------------------------------------------------------------------- */

@@ -150,7 +150,7 @@ void free_cache(ft_cache* c) {
     (void)hipDeviceSynchronize();
     if (c->host) host_branch_destroy(c->host);
     if (c->timing) timing_destroy(c->timing);
-    void* bufs[] = {c->pool, c->slot_for_id, c->id_of_slot, c->stamp, c->clock, c->counters, c->errflag,
+    void* bufs[] = {c->pool, c->slot_for_id, c->id_of_slot, c->stamp, c->clock, c->counters, c->errflag, c->gseq_dev,
                     c->wl_counts, c->wl_slot, c->wl_src, c->plan.meta, c->plan.active_slot, c->plan.seg,
                     c->plan.perm, c->plan.route_pos, c->plan.tile_active, c->plan.tile_row0, c->plan.tile_first,
                     c->plan.chunk_counts, c->H, c->Y, c->gv_part};
@@ -306,6 +306,7 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     CK(dalloc(&c->clock, 1));
     CK(dalloc(&c->counters, C_N));
     CK(dalloc(&c->errflag, 1));
+    CK(dalloc(&c->gseq_dev, 1));
     CK(dalloc(&c->wl_counts, 4));
     CK(dalloc(&c->wl_slot, cap));
     CK(dalloc(&c->wl_src, cap));
@@ -327,6 +328,7 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     CK(hipMemcpy(c->clock, &one, sizeof(one), hipMemcpyHostToDevice));
     CK(hipMemset(c->counters, 0, sizeof(unsigned long long) * C_N));
     CK(hipMemset(c->errflag, 0, sizeof(int32_t)));
+    CK(hipMemset(c->gseq_dev, 0, sizeof(uint64_t)));
     CK(hipMemset(c->plan.meta, 0, sizeof(int32_t) * 4));
     CK(hipStreamCreateWithFlags(&c->xfer, hipStreamNonBlocking));
     CK(hipStreamCreateWithFlags(&c->hstream, hipStreamNonBlocking));
@@ -417,13 +419,16 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         // activations into pinned staging and, with the mailbox, posts the
         // call's sequence number; the host workers run the host experts and
         // leave their partial sums in pinned memory.  A call being captured
-        // into a graph uses a host function instead (a graph node that every
-        // replay runs; the mailbox's sequence numbers are fixed per call).
+        // into a graph posts to the mailbox's graph words instead, numbered by
+        // a device counter so that every replay posts a new number, and a
+        // bounded polling kernel waits for the answer; without a poller, it
+        // uses a captured host function.
         HostStaging hs = host_branch_staging(c->host);
-        HostSignal sig = capturing ? HostSignal{} : host_branch_prepare(c->host, layer, T);
+        HostSignal sig = capturing ? host_branch_graph_signal(c->host, c->gseq_dev, layer, T)
+                                   : host_branch_prepare(c->host, layer, T);
         FT_HIP(launch_plan(c, routes, T, -1, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, w, x, &hs, &sig,
                            st));
-        if (!sig.mailbox) {
+        if (!sig.mailbox && !sig.gmbox) {
             FT_HIP(hipEventRecord(c->ev_fwd, st));
             FT_HIP(hipStreamWaitEvent(c->hstream, c->ev_fwd, 0));
             FT_HIP(capturing ? host_branch_enqueue_captured(c->host, layer, T, c->hstream)
@@ -437,6 +442,8 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
         if (sig.mailbox) {
             FT_HIP(hipStreamWaitValue64(st, sig.done_word, sig.seq, hipStreamWaitValueGte, ~0ull));
+        } else if (sig.gmbox) {
+            FT_HIP(launch_host_wait(c, sig, st));
         } else {
             FT_HIP(hipStreamWaitEvent(st, c->ev_host, 0));
         }

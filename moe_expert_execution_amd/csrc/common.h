@@ -73,13 +73,22 @@ HostStaging host_branch_staging(HostBranch* hb);
 // stores `seq` to *seq_word (pinned) after staging; a polling host thread runs
 // the call and stores `seq` to *done_word, which the stream waits for.
 // Otherwise a stream host function runs the call.
+// Graph mailbox (calls captured into a graph): the planner draws the call's
+// number from a device counter, stores layer and T, then the number, to the
+// mailbox's graph words; the poller answers in gdone, which a bounded polling
+// kernel waits for (numbers fixed at capture could not be replayed).
 struct HostSignal {
     bool mailbox;
     uint64_t seq;
     uint64_t* seq_word;
     uint64_t* done_word;
+    uint64_t* gmbox;            // graph words: [0] number, [8] done, [16] layer, [17] T (null = none)
+    uint64_t* gseq_dev;         // device counter of graph calls
+    int32_t layer, T;
 };
 HostSignal host_branch_prepare(HostBranch* hb, int32_t layer, int32_t T);
+// The graph mailbox for a captured call (gmbox null when no poller runs).
+HostSignal host_branch_graph_signal(HostBranch* hb, uint64_t* gseq_dev, int32_t layer, int32_t T);
 // Enqueue the host computation of layer `layer` for T tokens on `stream`
 // (staging must already hold routes, w and x for those tokens).
 hipError_t host_branch_enqueue(HostBranch* hb, int32_t layer, int32_t T, hipStream_t stream);
@@ -139,6 +148,7 @@ struct ft_cache {
     uint64_t* clock;           // [1]
     unsigned long long* counters;  // [C_N]
     int32_t* errflag;          // [1]
+    uint64_t* gseq_dev;        // [1] number of the last host-branch call made by a graph replay
     // internal copy of the last classify's fill worklist and counts
     int32_t* wl_counts;        // [4]
     int32_t* wl_slot;          // [cap]
@@ -175,6 +185,9 @@ hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, 
 hipError_t launch_fill(ft_cache* c, hipStream_t st, TimedLaunch tl = TimedLaunch());
 hipError_t launch_invalidate(ft_cache* c, int buf, hipStream_t st);
 hipError_t launch_register(ft_cache* c, int layer, int buf, hipStream_t st);
+// Wait on the stream until the host branch answered the last graph call
+// (bounded; on time-out error flag 8 is set and the wait ends).
+hipError_t launch_host_wait(ft_cache* c, const HostSignal& sig, hipStream_t st);
 hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t S, const int32_t* src_slots,
                                 int n, hipStream_t st);
 // plan: routes -> active slots, sorted rows, tiles.  slot_base >= 0 means routes

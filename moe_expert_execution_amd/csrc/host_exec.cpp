@@ -34,6 +34,7 @@ namespace ftmoe {
 namespace {
 
 constexpr int kRing = 256;
+constexpr size_t kMailboxBytes = 512;
 
 struct Job {
     int layer = 0, T = 0;
@@ -83,7 +84,8 @@ struct HostBranch {
         std::atomic<int> busy{0};
     } ring[kRing];
     uint64_t ring_next = 0;
-    // mailbox (pinned): [0] seq posted by the GPU, [8] done posted by the poller
+    // mailbox (pinned, u64 words): [0] seq posted by the GPU, [8] done posted
+    // by the poller; graph calls: [16] number, [24] done, [32] layer, [33] T
     bool use_mailbox = false;
     uint64_t* mbox = nullptr;
     uint64_t next_seq = 0;                   // last seq handed out (enqueuing thread)
@@ -394,9 +396,20 @@ void poller_main(HostBranch* hb, int cpu) {
     }
     volatile uint64_t* seq_word = hb->mbox;
     uint64_t* done_word = hb->mbox + 8;
-    uint64_t last = 0;
+    uint64_t* g = hb->mbox + 16;              // graph calls
+    uint64_t last = 0, glast = 0;
     int idle = 0;
     while (!hb->stop.load(std::memory_order_relaxed)) {
+        const uint64_t gs = __atomic_load_n(g, __ATOMIC_ACQUIRE);
+        if (gs != glast) {
+            idle = 0;
+            const int layer = (int)__atomic_load_n(g + 16, __ATOMIC_RELAXED);
+            const int T = (int)__atomic_load_n(g + 17, __ATOMIC_RELAXED);
+            run_call(hb, layer, T);
+            __atomic_store_n(g + 8, gs, __ATOMIC_RELEASE);
+            glast = gs;
+            continue;
+        }
         const uint64_t s = __atomic_load_n(seq_word, __ATOMIC_ACQUIRE);
         if (s == last) {
             if (++idle < 200000) {
@@ -437,9 +450,9 @@ HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const
     hb->stg.w = (float*)p;
     ok &= hipHostMalloc(&p, sizeof(float) * max_tokens * d, hipHostMallocDefault) == hipSuccess;
     hb->stg.P = (float*)p;
-    ok &= hipHostMalloc(&p, 128, hipHostMallocDefault) == hipSuccess;
+    ok &= hipHostMalloc(&p, kMailboxBytes, hipHostMallocDefault) == hipSuccess;
     hb->mbox = (uint64_t*)p;
-    if (hb->mbox) memset(hb->mbox, 0, 128);
+    if (hb->mbox) memset(hb->mbox, 0, kMailboxBytes);
     // the kernels write and read the staging through these same addresses
     for (void* hp : {(void*)hb->stg.x, (void*)hb->stg.routes, (void*)hb->stg.w, (void*)hb->stg.P, (void*)hb->mbox}) {
         void* dp = nullptr;
@@ -495,6 +508,16 @@ HostSignal host_branch_prepare(HostBranch* hb, int32_t layer, int32_t T) {
     s.seq = n;
     s.seq_word = hb->mbox;
     s.done_word = hb->mbox + 8;
+    return s;
+}
+
+HostSignal host_branch_graph_signal(HostBranch* hb, uint64_t* gseq_dev, int32_t layer, int32_t T) {
+    HostSignal s{};
+    if (!hb->use_mailbox) return s;
+    s.gmbox = hb->mbox + 16;
+    s.gseq_dev = gseq_dev;
+    s.layer = layer;
+    s.T = T;
     return s;
 }
 

@@ -53,6 +53,9 @@ struct PlanArgs {
     uint16_t* h_x;
     uint64_t* seq_word;      // mailbox: store seq here once staging is visible (null = none)
     uint64_t seq;
+    uint64_t* gmbox;         // graph mailbox words (null = none)
+    uint64_t* gseq_dev;      // device counter of graph calls
+    int32_t glayer;
 };
 
 // Post the call to the host branch's mailbox after the staging writes of the
@@ -61,6 +64,14 @@ __device__ __forceinline__ void post_mailbox(const PlanArgs& a) {
     if (a.seq_word && threadIdx.x == 0) {
         __threadfence_system();
         __hip_atomic_store(a.seq_word, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    if (a.gmbox && threadIdx.x == 0) {
+        const uint64_t n = *a.gseq_dev + 1;          // calls on one stream run in order
+        *a.gseq_dev = n;
+        __hip_atomic_store(a.gmbox + 16, (uint64_t)a.glayer, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(a.gmbox + 17, (uint64_t)a.T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __threadfence_system();
+        __hip_atomic_store(a.gmbox, n, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
@@ -350,6 +361,9 @@ hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base,
     PlanArgs a;
     a.seq_word = (sig && sig->mailbox) ? sig->seq_word : nullptr;
     a.seq = sig ? sig->seq : 0;
+    a.gmbox = sig ? sig->gmbox : nullptr;
+    a.gseq_dev = sig ? sig->gseq_dev : nullptr;
+    a.glayer = sig ? sig->layer : 0;
     a.w = w;
     a.x = x;
     a.d = c->sh.d_model;

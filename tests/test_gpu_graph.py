@@ -4,6 +4,7 @@ stamps and counters), with eager work and synchronisations between replays,
 and the layer outputs match the oracle.  A call that cannot be captured is
 refused with the documented status."""
 import numpy as np
+import pytest
 import torch
 
 import moe_expert_execution_amd as M
@@ -46,8 +47,14 @@ class Step:
 
 
 @gpu
-def test_graph_replay_equals_eager_step_for_step():
+@pytest.mark.parametrize("signal", ["mailbox", "callback"])
+def test_graph_replay_equals_eager_step_for_step(signal, monkeypatch):
+    """`mailbox`: the captured calls post to the polling host thread with
+    device-drawn numbers; `callback`: stream host functions, captured as host
+    nodes (FTMOE_HOST_SIGNAL is read when a cache is created)."""
     cuda()
+    if signal == "callback":
+        monkeypatch.setenv("FTMOE_HOST_SIGNAL", "callback")
     # a small cache under pressure: hits, fills and host-run misses every step
     cfg = synth.CONFIGS["decode"].with_(layers=4, d=256, E=16, k=4, f=128, slots=12, bp_mbps=20000,
                                         bh_mbps=60000)
