@@ -68,7 +68,7 @@ struct HostBranch {
     std::atomic<int> finished{0};
     // per-call scratch shared by the workers
     std::vector<float> xf;             // [max_tokens x d] fp32 activations of the tokens with host routes
-    std::vector<float> hbuf;           // [max_tokens x f] SwiGLU output of the current expert
+    std::vector<float> hbuf;           // SwiGLU outputs: [rows x f], rows = max(max_tokens, 2k)
     // host-function contexts of calls captured into graphs: each captured
     // call owns one for the life of the branch (a graph may replay it any
     // number of times)
@@ -233,49 +233,79 @@ struct WorkerScratch {
 };
 
 // All participants run this for the current job.  Work items are half
-// panels: 16 rows of the gate and up matrices (phase 1), then 16 output
-// columns of the down matrix (phase 2).
+// panels.  When the SwiGLU outputs of every (expert, token) entry fit the
+// scratch (decode: a few host experts of one token), the call runs in two
+// phases over all its experts at once: (1) 16 rows of one expert's gate and
+// up matrices per item, h of that expert's tokens; (2) 16 output columns per
+// item, every expert's down matrix in expert order, so each output element
+// still receives its experts' terms in the same order.  Otherwise the
+// experts run one after the other, two phases each.
 void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
     const Job& jb = hb->job;
     const int d = hb->sh.d_model, f = hb->sh.d_ff, E = hb->sh.experts;
     const int64_t S = hb->rl.S;
     float* P = hb->stg.P;
-    for (size_t xi = 0; xi < jb.experts.size(); ++xi) {
-        const int e = jb.experts[xi];
-        const int t0 = jb.tok_off[xi], t1 = jb.tok_off[xi + 1], nt = t1 - t0;
-        const uint8_t* rec = hb->bank + ((int64_t)jb.layer * E + e) * S;
-        ws.fit(nt);
-        // phase 1: h[i][n] = silu(x_i . WgT[n]) * (x_i . WuT[n])
-        for (int i = 0; i < nt; ++i) ws.vec[i] = hb->xf.data() + (int64_t)jb.tok[t0 + i] * d;
-        const int nblk1 = f / 16;
+    const int nx = (int)jb.experts.size();
+    const bool together = (int64_t)jb.tok.size() * f <= (int64_t)hb->hbuf.size();
+    // phase 1 of experts [x0, x1): items (expert, half panel); h rows are indexed by entry
+    auto phase1 = [&](int x0, int x1) {
+        const int per = f / 16;
+        const int nblk = (x1 - x0) * per;
         for (;;) {
-            const int b = hb->next_block.fetch_add(1, std::memory_order_relaxed);
-            if (b >= nblk1) break;
+            const int it = hb->next_block.fetch_add(1, std::memory_order_relaxed);
+            if (it >= nblk) break;
+            const int xi = x0 + it / per, b = it % per;
+            const int e = jb.experts[xi];
+            const int t0 = jb.tok_off[xi], nt = jb.tok_off[xi + 1] - t0;
+            const uint8_t* rec = hb->bank + ((int64_t)jb.layer * E + e) * S;
+            ws.fit(nt);
+            for (int i = 0; i < nt; ++i) ws.vec[i] = hb->xf.data() + (int64_t)jb.tok[t0 + i] * d;
             const int p = b >> 1, h = b & 1;
             half_panel_dots(hb, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.vec.data(), nt, ws.acc.data(),
                             ws.g.data());
             half_panel_dots(hb, rec, hb->rl.off_up, hb->rl.off_su, p, h, d, ws.vec.data(), nt, ws.acc.data(),
                             ws.u.data());
+            const int64_t hrow0 = together ? t0 : 0;
             for (int i = 0; i < nt; ++i)
                 for (int r = 0; r < 16; ++r)
-                    hb->hbuf[(int64_t)i * f + 16 * b + r] = silu(ws.g[i * 16 + r]) * ws.u[i * 16 + r];
+                    hb->hbuf[(hrow0 + i) * f + 16 * b + r] = silu(ws.g[i * 16 + r]) * ws.u[i * 16 + r];
         }
-        barrier(hb, participants);
-        // phase 2: P[t][c] += w * (h_i . WdT[c])
-        for (int i = 0; i < nt; ++i) ws.vec[i] = hb->hbuf.data() + (int64_t)i * f;
-        const int nblk2 = d / 16;
+    };
+    // phase 2 of experts [x0, x1): items are output half panels, each over the experts in order
+    auto phase2 = [&](int x0, int x1) {
+        const int nblk = d / 16;
         for (;;) {
             const int b = hb->next_block.fetch_add(1, std::memory_order_relaxed);
-            if (b >= nblk2) break;
-            half_panel_dots(hb, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f, ws.vec.data(), nt,
-                            ws.acc.data(), ws.y.data());
-            for (int i = 0; i < nt; ++i) {
-                float* pr = P + (int64_t)jb.tok[t0 + i] * d + 16 * b;
-                const float wt = jb.wt[t0 + i];
-                for (int r = 0; r < 16; ++r) pr[r] += wt * ws.y[i * 16 + r];
+            if (b >= nblk) break;
+            for (int xi = x0; xi < x1; ++xi) {
+                const int e = jb.experts[xi];
+                const int t0 = jb.tok_off[xi], nt = jb.tok_off[xi + 1] - t0;
+                const uint8_t* rec = hb->bank + ((int64_t)jb.layer * E + e) * S;
+                ws.fit(nt);
+                const int64_t hrow0 = together ? t0 : 0;
+                for (int i = 0; i < nt; ++i) ws.vec[i] = hb->hbuf.data() + (hrow0 + i) * f;
+                half_panel_dots(hb, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f, ws.vec.data(), nt,
+                                ws.acc.data(), ws.y.data());
+                for (int i = 0; i < nt; ++i) {
+                    float* pr = P + (int64_t)jb.tok[t0 + i] * d + 16 * b;
+                    const float wt = jb.wt[t0 + i];
+                    for (int r = 0; r < 16; ++r) pr[r] += wt * ws.y[i * 16 + r];
+                }
             }
         }
+    };
+    if (together) {
+        phase1(0, nx);
         barrier(hb, participants);
+        phase2(0, nx);
+        barrier(hb, participants);
+    } else {
+        for (int xi = 0; xi < nx; ++xi) {
+            phase1(xi, xi + 1);
+            barrier(hb, participants);
+            phase2(xi, xi + 1);
+            barrier(hb, participants);
+        }
     }
 }
 
@@ -463,7 +493,9 @@ HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const
         return nullptr;
     }
     hb->xf.resize((size_t)max_tokens * d);
-    hb->hbuf.resize((size_t)max_tokens * f);
+    // SwiGLU outputs: one row per token for experts run one at a time, or one
+    // row per (expert, token) entry when a call's entries fit (at least 2k rows)
+    hb->hbuf.resize((size_t)std::max<int64_t>(max_tokens, 2 * (int64_t)sh.top_k) * f);
     for (int i = 0; i < kRing; ++i) hb->ring[i].hb = hb;
     // worker count: cores in the affinity mask minus two (runtime threads, caller), at least one
     cpu_set_t set;
