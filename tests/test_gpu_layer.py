@@ -164,6 +164,35 @@ def test_fp8_cached(T, steps, nsample):
 
 
 @gpu
+def test_mxfp4_prefill_streamed_T4096():
+    """MXFP4 prefill at its full chunk (d=7168, E=256, top-8, f=2048, T=4096):
+    the layer in a full-layer buffer, the grouped MFMA GEMM as bench.py times
+    it, two sampled rows against the oracle."""
+    cuda()
+    cfg = synth.CONFIGS["mxfp4"].with_(layers=1)
+    T = 4096
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, "mxfp4", bank.ptr, 2 * cfg.E, T, cfg.bp_mbps, cfg.bh_mbps)
+    st = torch.cuda.current_stream().cuda_stream
+    try:
+        x = synth.tokens(cfg, T, 7, T)
+        ids, w, _ = OR.route(x, synth.router(cfg, 0), cfg.k)
+        xd, idd, wd = dev_u16(x), dev(ids.astype(np.int32)), dev(w)
+        y = torch.zeros((T, cfg.d), dtype=torch.int16, device="cuda")
+        M.ft_moe_forward(sc.handle, 0, M.FT_MODE_STREAMED, xd.data_ptr(), idd.data_ptr(), wd.data_ptr(), T,
+                         y.data_ptr(), st)
+        torch.cuda.synchronize()
+        rows = np.array([0, T - 1])
+        ref = oracle_rows(x, ids, w, expert_fn(recs, cfg, 0, maxsize=20), rows)
+        assert_close_rel(bf16_bits_to_f64(y)[rows], ref, TOL["mxfp4"], "mxfp4 T 4096")
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
 @pytest.mark.parametrize("T,steps,nsample", [(1, 4, 1), (16, 1, 2)])
 def test_mxfp4_cached(T, steps, nsample):
     """MXFP4 shape (d=7168, E=256, top-8, f=2048, e2m1 + e8m0 per 32), one
