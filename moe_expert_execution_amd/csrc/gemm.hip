@@ -15,10 +15,9 @@
 // by the four waves) is staged through LDS, loaded straight into a 4-deep
 // ring of buffers, one barrier per K-step.  Block-FP8 and MXFP4 weights are
 // converted to bf16 in registers right before their MFMA, so every format
-// issues the bf16 MFMA.  The expert
-// FFN with its gate/up and down projections read from one slot record follows
-// "The Expert Cache That Follows the Router", section "One logical expert,
-// two physical levels of memory".
+// issues the bf16 MFMA.  The expert FFN with its gate/up and down projections
+// read from one slot record follows "The Expert Cache That Follows the
+// Router", section "One logical expert, two physical levels of memory".
 #include <type_traits>
 
 #include "wfmt.h"
@@ -120,10 +119,12 @@ __device__ __forceinline__ void vm_wait() {
 // M-tile: all blocks of an expert run together in one XCD, where its A rows
 // and weight panels are read from HBM about once and then hit that XCD's L2.
 //
-// The activation tile goes from memory straight into LDS
-// (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's base +
-// 16 x lane) through a ring of kStages K-step buffers, kStages - 1 steps ahead
-// of its use.  A buffer is 128 rows x 128 bytes; 16-byte chunk c of row r sits
+// The activation tile goes from memory straight into LDS (buffer_load_dwordx4
+// with the lds modifier: each lane's 16 bytes land at the wave's base + 16 x
+// lane) through a ring of kStages K-step buffers, kStages - 1 steps ahead of
+// its use.  The buffer form, not global_load_lds: the compiler treats the
+// latter as a FLAT access to both memory kinds and then turns every register
+// wait into vmcnt(0), draining the weight prefetch.  A buffer is 128 rows x 128 bytes; 16-byte chunk c of row r sits
 // at position c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), so that the 16 (or 8)
 // rows one ds_read_b128 serves per cycle fall in distinct banks.  Waits are
 // explicit (vmcnt + s_barrier): a __syncthreads would also drain the weight
