@@ -220,8 +220,13 @@ __global__ void __launch_bounds__(64) route_select_kernel(int T, int E, int k, i
         const int ee = lane + 64 * j;
         double z = -INFINITY;
         if (ee < E) {
+            // all partials in flight at once, then added in their fixed order
+            double p[kRouteDS];
+#pragma unroll
+            for (int ds = 0; ds < kRouteDS; ++ds) p[ds] = g_route_part[((int64_t)ds * kRouteSmallT + t) * kRouteMaxE + ee];
             z = 0.0;
-            for (int ds = 0; ds < kRouteDS; ++ds) z += g_route_part[((int64_t)ds * kRouteSmallT + t) * kRouteMaxE + ee];
+#pragma unroll
+            for (int ds = 0; ds < kRouteDS; ++ds) z += p[ds];
         }
         zl[j] = z;
         taken[j] = ee >= E;
