@@ -187,7 +187,7 @@ def decode_bench(args):
         try:
             from moe_expert_execution_amd import bwprofile
             bwprofile.save("bf16", bwprofile.gpu_key(), prof.bp_mbps, prof.bh_mbps,
-                           directory=os.path.join(ROOT, "gpurun_out", "bwprofile"))
+                           directory=os.environ.get("FTMOE_PROFILE_DIR", bwprofile.DEFAULT_DIR))
         except Exception as exc:          # the store is a convenience; the measurement stands
             log(f"profile not stored: {exc}")
         M.ft_cache_set_profile(h, prof)
