@@ -137,7 +137,9 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint16_t As[kStages][kBM * kBK];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int NT = GU ? a.f / (kBN / 2) : a.d / kBN;
+    // d (a multiple of 128) may end in a half N-tile of the down product: its
+    // waves 2 and 3 have no columns, re-read the last panel and store nothing
+    const int NT = GU ? a.f / (kBN / 2) : (a.d + kBN - 1) / kBN;
     const int V = a.meta[1] * NT;                 // valid workgroups
     const int b = blockIdx.x;
     if (b >= V) return;
@@ -171,8 +173,9 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
         soff[0] = a.off_sg;
         soff[1] = a.off_su;
     } else {
-        pn[0] = nt * 8 + 2 * w;
-        pn[1] = pn[0] + 1;
+        const int last = a.d / 32 - 1;
+        pn[0] = min(nt * 8 + 2 * w, last);
+        pn[1] = min(nt * 8 + 2 * w + 1, last);
         bp[0] = rec + a.off_down + pn[0] * panel_bytes + lane * 16;
         bp[1] = rec + a.off_down + pn[1] * panel_bytes + lane * 16;
         soff[0] = soff[1] = a.off_sd;
@@ -373,6 +376,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
             // per wave: 32 rows x 64 bf16 columns at a time, rows padded by 16 bytes
             constexpr int LDY = 64 + 8;
             uint16_t* Ys = &As[0][0] + w * 32 * LDY;
+            const bool col_ok = nt * kBN + 64 * w < a.d;
             static_assert(4 * 32 * LDY <= kStages * kBM * kBK, "y tiles must fit the A buffers");
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
@@ -396,7 +400,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
                 for (int it = 0; it < 4; ++it) {
                     const int rr = it * 8 + (lane >> 3), c = (lane & 7) * 8;
                     const int r = mi * 32 + rr;
-                    if (r < rows_valid)
+                    if (r < rows_valid && col_ok)
                         *reinterpret_cast<u32x4_t*>(a.Y + (int64_t)(row0 + r) * a.d + nt * kBN + 64 * w + c) =
                             *reinterpret_cast<const u32x4_t*>(&Ys[rr * LDY + c]);
                 }
@@ -415,7 +419,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
 
 template <int FMT>
 hipError_t launch_fmt(const GemmArgs& a, int64_t max_tiles, Timing* tm, hipStream_t st) {
-    const int64_t g1 = max_tiles * (a.f / (kBN / 2)), g2 = max_tiles * (a.d / kBN);
+    const int64_t g1 = max_tiles * (a.f / (kBN / 2)), g2 = max_tiles * ((a.d + kBN - 1) / kBN);
     TimedLaunch t1 = timing_launch(tm, FT_K_GEMM_GU);
     hipExtLaunchKernelGGL((gemm_kernel<FMT, true>), dim3((unsigned)g1), dim3(kGemmThreads), 0, st, t1.start, t1.stop,
                           0, a);

@@ -216,3 +216,31 @@ def test_mxfp4_cached(T, steps, nsample):
     finally:
         sc.close()
         bank.close()
+
+
+@gpu
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("d,f", [(32768, 128), (128, 8192)])
+def test_layer_at_the_size_limits(fmt, d, f):
+    """The largest d (32768) and f (8192) the library accepts, every format:
+    T = 1 and 4 (GEMV: eight K-parts at d = 32768, 64 KiB of h in LDS at
+    f = 8192) and T = 37 (MFMA GEMM with a ragged last tile); all rows
+    against the oracle, every expert resident after its fill."""
+    cuda()
+    cfg = synth.CONFIGS["tiny"].with_(d=d, f=f, E=4, k=2, fmt=fmt, slots=4, bp_mbps=60000, bh_mbps=60000,
+                                      cfg_id=95)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, fmt, bank.ptr, cfg.slots, 37, cfg.bp_mbps, cfg.bh_mbps)
+    try:
+        ex = expert_fn(recs, cfg, 0, maxsize=4)
+        wr = synth.router(cfg, 0)
+        for T in (1, 4, 37):
+            x = synth.tokens(cfg, T, 500 + T)
+            ids, w, _ = OR.route(x, wr, cfg.k)
+            y, _ = run_cached(sc, 0, x, ids, w)
+            assert_close_rel(y, oracle_rows(x, ids, w, ex, np.arange(T)), TOL[fmt], f"{fmt} d {d} f {f} T {T}")
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
