@@ -426,8 +426,14 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         HostStaging hs = host_branch_staging(c->host);
         HostSignal sig = capturing ? host_branch_graph_signal(c->host, c->gseq_dev, layer, T)
                                    : host_branch_prepare(c->host, layer, T);
+        // with a mailbox, this call's pending fill rides in the planner's
+        // launch (a host function, in contrast, must follow the staging at once)
+        const bool plan_fill =
+            c->fill_pending && (sig.mailbox || sig.gmbox) && (int64_t)T * k <= kSmallPlanRoutes;
+        const TimedLaunch ftl = plan_fill ? timing_launch(c->timing, FT_K_FILL) : TimedLaunch();
         FT_HIP(launch_plan(c, routes, T, -1, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, w, x, &hs, &sig,
-                           st));
+                           st, plan_fill ? &ftl : nullptr));
+        if (plan_fill) c->fill_pending = false;
         if (!sig.mailbox && !sig.gmbox) {
             FT_HIP(hipEventRecord(c->ev_fwd, st));
             FT_HIP(hipStreamWaitEvent(c->hstream, c->ev_fwd, 0));

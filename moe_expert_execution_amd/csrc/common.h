@@ -195,10 +195,11 @@ hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int6
 // `work_counter` (C_GEMV_EXPERTS or C_GEMM_EXPERTS) receives the active-slot
 // count and the next counter the row count.
 // With `stage`, routes, w and x of the call are also copied into the host
-// branch's pinned staging.
+// branch's pinned staging.  With `fill` (R <= kSmallPlanRoutes only), the
+// pending fill runs in the same launch, timed by those events.
 hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, int work_counter,
                        const float* w, const uint16_t* x, const HostStaging* stage, const HostSignal* sig,
-                       hipStream_t st);
+                       hipStream_t st, const TimedLaunch* fill = nullptr);
 hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 int gemv_kparts(const ft_shape& s);
 hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st);

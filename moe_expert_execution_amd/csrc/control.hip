@@ -10,6 +10,7 @@
 // invalidation of a full-layer buffer before it is overwritten, and the record
 // gather used by resize.
 #include "common.h"
+#include "fill.h"
 
 namespace ftmoe {
 namespace {
@@ -86,7 +87,10 @@ __device__ __forceinline__ int fill_count(int m, int h, int N, uint32_t bp, uint
     return q < 0 ? 0 : (int)q;
 }
 
+// KPT: victim keys per thread, ceil(N / kCtrlThreads) rounded up to a power of two
+template <int KPT>
 __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
+    static_assert(KPT * kCtrlThreads <= kMaxSlots, "keys per thread beyond the slot limit");
     __shared__ uint32_t ebits[kMaxExperts / 32];
     __shared__ int wordbase[kMaxExperts / 32];
     __shared__ int16_t pos_of_e[kMaxExperts];     // expert -> unique index
@@ -96,6 +100,7 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
     __shared__ int16_t miss_list[kMaxExperts];    // miss rank -> unique index
     __shared__ uint32_t hitbits[kMaxSlots / 32];
     __shared__ int16_t victims[kMaxExperts];     // slots fit 15 bits (N <= 32768)
+    __shared__ int32_t victim_old[kMaxExperts];  // each victim's owner (flat id) or -1
     __shared__ int wsum[kWaves];
     __shared__ uint64_t wmin[2][kWaves];
     __shared__ int sh_nuniq, sh_evict;
@@ -104,6 +109,28 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
     const int E = a.E, N = a.N, R = a.R;
     const int ewords = (E + 31) >> 5, nwords = (N + 31) >> 5;
     const uint64_t clk = *a.clock;
+
+    // Every map read of the call is issued here, together: the layer's
+    // slot_for_id entries (expert tid + j * kCtrlThreads), and the stamp and
+    // owner of each slot this thread keys in the victim scan (slot
+    // tid + j * kCtrlThreads).  The rest of the kernel then works on chip
+    // and only stores.  (Stamps of slots hit in this call change below, but
+    // those slots never compete as victims.)
+    constexpr int kEPerThread = kMaxExperts / kCtrlThreads;
+    int sfi[kEPerThread];
+#pragma unroll
+    for (int j = 0; j < kEPerThread; ++j) {
+        const int e = tid + j * kCtrlThreads;
+        sfi[j] = e < E ? a.slot_for_id[(int64_t)a.layer * E + e] : -1;
+    }
+    uint64_t pst[KPT];
+    int pown[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int s = tid + j * kCtrlThreads;
+        pst[j] = s < N ? a.stamp[s] : 0;
+        pown[j] = s < N ? a.id_of_slot[s] : -1;
+    }
 
     for (int i = tid; i < ewords; i += kCtrlThreads) ebits[i] = 0;
     for (int i = tid; i < nwords; i += kCtrlThreads) hitbits[i] = 0;
@@ -135,13 +162,16 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
     const int nu = sh_nuniq;
 
     // 3. unique index of every routed expert, and its residency
-    for (int e = tid; e < E; e += kCtrlThreads) {
+#pragma unroll
+    for (int j = 0; j < kEPerThread; ++j) {
+        const int e = tid + j * kCtrlThreads;
+        if (e >= E) break;
         uint32_t wv = ebits[e >> 5];
         if (wv & (1u << (e & 31))) {
             int idx = wordbase[e >> 5] + __popc(wv & ((1u << (e & 31)) - 1u));
             pos_of_e[e] = (int16_t)idx;
             e_of_u[idx] = (int16_t)e;
-            int s = a.slot_for_id[(int64_t)a.layer * E + e];
+            const int s = sfi[j];
             uslot[idx] = (s >= 0 && s < N) ? s : -1;
         }
     }
@@ -178,14 +208,14 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
     // 5. one scan of the slots: each thread keeps its (stamp, slot) keys; the
     //    q smallest keys among slots not hit in this call are the victims
     if (q > 0) {
-        uint64_t keys[kKeysPerThread];
+        uint64_t keys[KPT];
         uint64_t lmin = ~0ull;
 #pragma unroll
-        for (int j = 0; j < kKeysPerThread; ++j) {
+        for (int j = 0; j < KPT; ++j) {
             int s = tid + j * kCtrlThreads;
             uint64_t k = ~0ull;
             if (s < N && !(hitbits[s >> 5] & (1u << (s & 31)))) {
-                uint64_t st = a.stamp[s];
+                uint64_t st = pst[j];
                 if (st >= kStampLimit) st = kStampLimit - 1;
                 k = (st << 24) | (uint64_t)s;
             }
@@ -211,8 +241,9 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
             if (lmin == g) {
                 uint64_t nm = ~0ull;
 #pragma unroll
-                for (int j = 0; j < kKeysPerThread; ++j) {
+                for (int j = 0; j < KPT; ++j) {
                     uint64_t k = keys[j];
+                    if (k == g && g != ~0ull) victim_old[i] = pown[j];   // keys are unique (slot in the low bits)
                     if (k > g && k < nm) nm = k;
                 }
                 lmin = nm;
@@ -228,7 +259,7 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
         int32_t u = a.layer * E + e;
         if (r < q) {
             int v = victims[r];
-            int old = a.id_of_slot[v];
+            int old = victim_old[r];
             if (old >= 0) {
                 a.slot_for_id[old] = -1;
                 atomicAdd(&sh_evict, 1);
@@ -294,41 +325,15 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
     }
 }
 
-// Device-initiated pull of whole records: record wl_src[i] of the pinned host
-// bank -> slot wl_slot[i], for i < q.  The grid is fixed (q is device data);
-// each workgroup walks 64 KiB chunks.
+// The decode fill as a kernel of its own (the planner's launch carries it
+// when the call posts to the host branch through a mailbox).
 constexpr int kFillThreads = 256;
-constexpr int64_t kFillChunk = 64 * 1024;
 constexpr int kFillBlocks = 512;
-typedef uint32_t fill_vec_t __attribute__((ext_vector_type(4)));   // 16 bytes
 
 __global__ void __launch_bounds__(kFillThreads)
     fill_kernel(const int32_t* wl_counts, const int32_t* wl_slot, const int32_t* wl_src,
                 const uint8_t* __restrict__ bank, uint8_t* __restrict__ pool, int64_t S) {
-    const int q = wl_counts[3];
-    const int64_t cpr = (S + kFillChunk - 1) / kFillChunk;
-    const int64_t total = (int64_t)q * cpr;
-    for (int64_t c = blockIdx.x; c < total; c += gridDim.x) {
-        const int64_t i = c / cpr;
-        const int64_t off = (c - i * cpr) * kFillChunk;
-        const int64_t len = (S - off) < kFillChunk ? (S - off) : kFillChunk;
-        const fill_vec_t* src = reinterpret_cast<const fill_vec_t*>(bank + (int64_t)wl_src[i] * S + off);
-        fill_vec_t* dst = reinterpret_cast<fill_vec_t*>(pool + (int64_t)wl_slot[i] * S + off);
-        const int64_t n16 = len / 16;
-        int64_t b = threadIdx.x;
-        // streaming (nontemporal) stores: the records go to HBM without
-        // leaving dirty L2 lines whose write-back would delay the expert
-        // kernels that read them next
-        for (; b + 3 * kFillThreads < n16; b += 4 * kFillThreads) {
-            const fill_vec_t v0 = src[b], v1 = src[b + kFillThreads], v2 = src[b + 2 * kFillThreads],
-                             v3 = src[b + 3 * kFillThreads];
-            __builtin_nontemporal_store(v0, dst + b);
-            __builtin_nontemporal_store(v1, dst + b + kFillThreads);
-            __builtin_nontemporal_store(v2, dst + b + 2 * kFillThreads);
-            __builtin_nontemporal_store(v3, dst + b + 3 * kFillThreads);
-        }
-        for (; b < n16; b += kFillThreads) __builtin_nontemporal_store(src[b], dst + b);
-    }
+    fill_records<kFillThreads>(wl_counts, wl_slot, wl_src, bank, pool, S, blockIdx.x, gridDim.x);
 }
 
 // Clear the owners of full-layer buffer slots [s0, s0 + E) before a layer is
@@ -419,7 +424,13 @@ hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, 
     a.wl_counts = c->wl_counts;
     a.wl_slot = c->wl_slot;
     a.wl_src = c->wl_src;
-    hipLaunchKernelGGL(classify_kernel, dim3(1), dim3(kCtrlThreads), 0, st, a);
+    const int kpt = (a.N + kCtrlThreads - 1) / kCtrlThreads;
+    if (kpt <= 1) hipLaunchKernelGGL(classify_kernel<1>, dim3(1), dim3(kCtrlThreads), 0, st, a);
+    else if (kpt <= 2) hipLaunchKernelGGL(classify_kernel<2>, dim3(1), dim3(kCtrlThreads), 0, st, a);
+    else if (kpt <= 4) hipLaunchKernelGGL(classify_kernel<4>, dim3(1), dim3(kCtrlThreads), 0, st, a);
+    else if (kpt <= 8) hipLaunchKernelGGL(classify_kernel<8>, dim3(1), dim3(kCtrlThreads), 0, st, a);
+    else if (kpt <= 16) hipLaunchKernelGGL(classify_kernel<16>, dim3(1), dim3(kCtrlThreads), 0, st, a);
+    else hipLaunchKernelGGL(classify_kernel<kKeysPerThread>, dim3(1), dim3(kCtrlThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,46 @@
+// Device-initiated pull of whole expert records from the pinned host bank
+// into slots: the decode fill of "The Expert Cache That Follows the Router",
+// section "One logical expert, two physical levels of memory" (a miss admitted
+// to the cache brings its whole record to the device).
+#pragma once
+
+#include "common.h"
+
+namespace ftmoe {
+
+constexpr int64_t kFillChunk = 64 * 1024;
+typedef uint32_t fill_vec_t __attribute__((ext_vector_type(4)));   // 16 bytes
+
+// Record wl_src[i] of the bank -> slot wl_slot[i], for i < q = wl_counts[3]
+// (device data, so the grid is fixed).  Workgroup `blk` of `nblk`, NT
+// threads, walks 64 KiB chunks of the q records.
+template <int NT>
+__device__ __forceinline__ void fill_records(const int32_t* wl_counts, const int32_t* wl_slot,
+                                             const int32_t* wl_src, const uint8_t* __restrict__ bank,
+                                             uint8_t* __restrict__ pool, int64_t S, int blk, int nblk) {
+    const int q = wl_counts[3];
+    const int64_t cpr = (S + kFillChunk - 1) / kFillChunk;
+    const int64_t total = (int64_t)q * cpr;
+    for (int64_t c = blk; c < total; c += nblk) {
+        const int64_t i = c / cpr;
+        const int64_t off = (c - i * cpr) * kFillChunk;
+        const int64_t len = (S - off) < kFillChunk ? (S - off) : kFillChunk;
+        const fill_vec_t* src = reinterpret_cast<const fill_vec_t*>(bank + (int64_t)wl_src[i] * S + off);
+        fill_vec_t* dst = reinterpret_cast<fill_vec_t*>(pool + (int64_t)wl_slot[i] * S + off);
+        const int64_t n16 = len / 16;
+        int64_t b = threadIdx.x;
+        // streaming (nontemporal) stores: the records go to HBM without
+        // leaving dirty L2 lines whose write-back would delay the expert
+        // kernels that read them next
+        for (; b + 3 * NT < n16; b += 4 * NT) {
+            const fill_vec_t v0 = src[b], v1 = src[b + NT], v2 = src[b + 2 * NT], v3 = src[b + 3 * NT];
+            __builtin_nontemporal_store(v0, dst + b);
+            __builtin_nontemporal_store(v1, dst + b + NT);
+            __builtin_nontemporal_store(v2, dst + b + 2 * NT);
+            __builtin_nontemporal_store(v3, dst + b + 3 * NT);
+        }
+        for (; b < n16; b += NT) __builtin_nontemporal_store(src[b], dst + b);
+    }
+}
+
+}  // namespace ftmoe

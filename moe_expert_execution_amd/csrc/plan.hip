@@ -17,6 +17,7 @@
 // More: three kernels over 64-token chunks — per-chunk slot masks and counts,
 // one scan, then rank = chunk offset + popcount(mask below the token).
 #include "common.h"
+#include "fill.h"
 
 namespace ftmoe {
 namespace {
@@ -160,7 +161,7 @@ __device__ void emit_tiles(const PlanArgs& a, int n_active, int* wsum) {
 }
 
 // ---- one-workgroup planner (R <= 1024) ------------------------------------------
-__global__ void __launch_bounds__(kPlanThreads) plan_small_kernel(PlanArgs a) {
+__device__ __forceinline__ void plan_small(const PlanArgs& a) {
     __shared__ uint32_t keys[kSmallPlanRoutes];
     __shared__ int wsum[kPlanThreads / 64];
     const int tid = threadIdx.x;
@@ -226,6 +227,33 @@ __global__ void __launch_bounds__(kPlanThreads) plan_small_kernel(PlanArgs a) {
     }
     __syncthreads();
     emit_tiles(a, n_active, wsum);
+}
+
+__global__ void __launch_bounds__(kPlanThreads) plan_small_kernel(PlanArgs a) { plan_small(a); }
+
+struct FillArgs {
+    const int32_t* wl_counts;
+    const int32_t* wl_slot;
+    const int32_t* wl_src;
+    const uint8_t* bank;
+    uint8_t* pool;
+    int64_t S;
+};
+constexpr int kPlanFillBlocks = 512;   // fill workgroups of kPlanThreads beside the planner: one 64 KiB chunk each for q <= 3 at decode sizes
+
+// The planner and the call's fill in one launch: workgroup 0 plans, the rest
+// pull the filled records.  Neither reads what the other writes (the plan
+// reads the routes, the fill the worklist; classify wrote both), and the
+// planner's few microseconds disappear under the PCIe pull.
+__global__ void __launch_bounds__(kPlanThreads) plan_fill_kernel(PlanArgs a, FillArgs f) {
+    if (blockIdx.x == 0) {
+        plan_small(a);
+        return;
+    }
+    // 256 threads per workgroup pull, 16 KiB of host reads in flight per
+    // chunk step: more per workgroup lowers the PCIe rate
+    if (threadIdx.x < 256)
+        fill_records<256>(f.wl_counts, f.wl_slot, f.wl_src, f.bank, f.pool, f.S, blockIdx.x - 1, gridDim.x - 1);
 }
 
 // ---- chunked planner (any R; key space <= 8192) --------------------------------
@@ -357,7 +385,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_scatter_kernel(PlanArgs a) 
 
 hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, int work_counter,
                        const float* w, const uint16_t* x, const HostStaging* stage, const HostSignal* sig,
-                       hipStream_t st) {
+                       hipStream_t st, const TimedLaunch* fill) {
     PlanArgs a;
     a.seq_word = (sig && sig->mailbox) ? sig->seq_word : nullptr;
     a.seq = sig ? sig->seq : 0;
@@ -390,7 +418,12 @@ hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base,
     a.tile_first = c->plan.tile_first;
     a.chunk_counts = c->plan.chunk_counts;
     a.work = c->counters + work_counter;
-    if (a.R <= kSmallPlanRoutes) {
+    if (fill) {
+        if (a.R > kSmallPlanRoutes) return hipErrorInvalidValue;
+        FillArgs f{c->wl_counts, c->wl_slot, c->wl_src, c->bank_dev, c->pool, c->rl.S};
+        hipExtLaunchKernelGGL(plan_fill_kernel, dim3(1 + kPlanFillBlocks), dim3(kPlanThreads), 0, st, fill->start,
+                              fill->stop, 0, a, f);
+    } else if (a.R <= kSmallPlanRoutes) {
         hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
     } else {
         if (a.key_space > kLargeKeySpace) return hipErrorInvalidValue;
