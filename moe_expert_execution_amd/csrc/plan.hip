@@ -250,8 +250,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_fill_kernel(PlanArgs a, Fil
         plan_small(a);
         return;
     }
-    // 256 threads per workgroup pull, 16 KiB of host reads in flight per
-    // chunk step: more per workgroup lowers the PCIe rate
+    // 256 threads per workgroup pull, as in the fill kernel: a workgroup's
+    // host reads in flight set the PCIe rate
     if (threadIdx.x < 256)
         fill_records<256>(f.wl_counts, f.wl_slot, f.wl_src, f.bank, f.pool, f.S, blockIdx.x - 1, gridDim.x - 1);
 }
