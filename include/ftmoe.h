@@ -125,8 +125,8 @@ typedef struct {
     int32_t error_flags;     /* sticky device flags: 1 = expert id out of range,
                                 2 = LRU clock past 2^40, 4 = repeated expert in a
                                 token's routes (the repeat is dropped), 8 = a
-                                graph-replayed call gave up waiting for the
-                                host experts (seconds; its output is invalid) */
+                                call gave up waiting for the host experts
+                                (seconds; its output is invalid) */
     int32_t num_slots;
     uint64_t host_experts;   /* expert FFNs run by the host workers               */
     uint64_t host_bytes;     /* expert-record bytes the host workers read         */

@@ -9,11 +9,31 @@ namespace ftmoe {
 namespace {
 
 constexpr int kCombThreads = 256;
+constexpr uint32_t kHostWaitPolls = 1u << 22;   // seconds of polls (each a PCIe read): far beyond any host call
 
+// With `done`, each workgroup first waits until the host branch has answered
+// the call: *done (pinned memory) reaches the call's number — `seq`, or
+// *seq_dev when the number is drawn on the device (graph calls).  The wait is
+// bounded: past kHostWaitPolls polls it raises error flag 8 and goes on, so
+// every wave ends.
 __global__ void __launch_bounds__(kCombThreads)
     combine_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ route_pos,
                    const float* __restrict__ w, const uint16_t* __restrict__ Y, const float* P, int T, int k, int d,
-                   uint16_t* __restrict__ y) {
+                   uint16_t* __restrict__ y, const uint64_t* done, const uint64_t* seq_dev, uint64_t seq,
+                   int32_t* errflag) {
+    if (done) {
+        if (threadIdx.x == 0) {
+            const uint64_t n = seq_dev ? *seq_dev : seq;
+            for (uint32_t it = 0; __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < n; ++it) {
+                if (it >= kHostWaitPolls) {
+                    atomicOr(errflag, 8);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+        }
+        __syncthreads();
+    }
     const int t = blockIdx.y;
     const int c = (blockIdx.x * kCombThreads + threadIdx.x) * 4;
     if (t >= T || c >= d) return;
@@ -51,12 +71,22 @@ __global__ void __launch_bounds__(kCombThreads)
 }  // namespace
 
 hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, const float* P, uint16_t* y,
-                          hipStream_t st) {
+                          hipStream_t st, const HostSignal* wait) {
     if (T <= 0) return hipSuccess;
     const int d = c->sh.d_model;
     dim3 grid((d / 4 + kCombThreads - 1) / kCombThreads, T);
+    const uint64_t* done = nullptr;
+    const uint64_t* seq_dev = nullptr;
+    uint64_t seq = 0;
+    if (wait && wait->gmbox) {
+        done = wait->gmbox + 8;
+        seq_dev = wait->gseq_dev;
+    } else if (wait && wait->mailbox) {
+        done = wait->done_word;
+        seq = wait->seq;
+    }
     hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, st, routes, c->plan.route_pos, w, c->Y, P, T,
-                       c->sh.top_k, d, y);
+                       c->sh.top_k, d, y, done, seq_dev, seq, c->errflag);
     return hipGetLastError();
 }
 

@@ -185,9 +185,6 @@ hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, 
 hipError_t launch_fill(ft_cache* c, hipStream_t st, TimedLaunch tl = TimedLaunch());
 hipError_t launch_invalidate(ft_cache* c, int buf, hipStream_t st);
 hipError_t launch_register(ft_cache* c, int layer, int buf, hipStream_t st);
-// Wait on the stream until the host branch answered the last graph call
-// (bounded; on time-out error flag 8 is set and the wait ends).
-hipError_t launch_host_wait(ft_cache* c, const HostSignal& sig, hipStream_t st);
 hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t S, const int32_t* src_slots,
                                 int n, hipStream_t st);
 // plan: routes -> active slots, sorted rows, tiles.  slot_base >= 0 means routes
@@ -204,8 +201,10 @@ hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 int gemv_kparts(const ft_shape& s);
 hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 // P: the host branch's partial sums [T x d] in pinned host memory (null when
-// the call has no host branch).
+// the call has no host branch).  With a mailbox or graph-mailbox `wait`, the
+// kernel itself first waits (bounded, error flag 8) for the host branch's
+// answer to the call.
 hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, const float* P,
-                          uint16_t* y, hipStream_t st);
+                          uint16_t* y, hipStream_t st, const HostSignal* wait = nullptr);
 int gemm_tile_m();
 }  // namespace ftmoe

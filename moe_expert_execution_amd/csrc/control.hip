@@ -453,30 +453,6 @@ hipError_t launch_register(ft_cache* c, int layer, int buf, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Bounded wait for the host branch's answer to the last graph call: one lane
-// polls the done word in pinned memory (system-scope loads) until it reaches
-// the call's number; after `limit` polls it raises error flag 8 and returns,
-// so the wave always ends.
-__global__ void host_wait_kernel(const uint64_t* gseq_dev, const uint64_t* gdone, int32_t* errflag,
-                                 uint32_t limit) {
-    if (threadIdx.x != 0) return;
-    const uint64_t n = *gseq_dev;
-    for (uint32_t it = 0; __hip_atomic_load(gdone, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < n; ++it) {
-        if (it >= limit) {
-            atomicOr(errflag, 8);
-            return;
-        }
-        __builtin_amdgcn_s_sleep(32);
-    }
-}
-
-hipError_t launch_host_wait(ft_cache* c, const HostSignal& sig, hipStream_t st) {
-    // ~2^22 polls of ~1 us each: seconds, far beyond any host call
-    hipLaunchKernelGGL(host_wait_kernel, dim3(1), dim3(64), 0, st, (const uint64_t*)sig.gseq_dev,
-                       (const uint64_t*)(sig.gmbox + 8), c->errflag, 1u << 22);
-    return hipGetLastError();
-}
-
 hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t S, const int32_t* src_slots,
                                 int n, hipStream_t st) {
     if (n <= 0) return hipSuccess;
