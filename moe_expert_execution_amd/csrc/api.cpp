@@ -2,6 +2,7 @@
 // validation, resource ownership, stream/event ordering, and the calls that
 // enqueue the kernels.  No C++ exception crosses the boundary.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -321,6 +322,10 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     c->cap_gemv = std::min<int32_t>(max_tokens, kGemvMaxTokens) * shape->top_k;
     c->gv_kq = gemv_kparts(*shape);
     CK(dalloc(&c->gv_part, 2ll * c->gv_kq * c->cap_gemv * f));
+    // seconds of polls, each a PCIe read: far beyond any host call (a test
+    // lowers it to force the time-out path)
+    c->host_wait_polls = 1u << 22;
+    if (const char* e = getenv("FTMOE_HOST_WAIT_POLLS")) c->host_wait_polls = (uint32_t)strtoul(e, nullptr, 10);
     CK(hipMemset(c->slot_for_id, 0xFF, sizeof(int32_t) * L * E));
     CK(hipMemset(c->id_of_slot, 0xFF, sizeof(int32_t) * c->N));
     CK(hipMemset(c->stamp, 0, sizeof(uint64_t) * c->N));

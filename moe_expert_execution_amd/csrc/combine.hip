@@ -9,23 +9,22 @@ namespace ftmoe {
 namespace {
 
 constexpr int kCombThreads = 256;
-constexpr uint32_t kHostWaitPolls = 1u << 22;   // seconds of polls (each a PCIe read): far beyond any host call
 
 // With `done`, each workgroup first waits until the host branch has answered
 // the call: *done (pinned memory) reaches the call's number — `seq`, or
 // *seq_dev when the number is drawn on the device (graph calls).  The wait is
-// bounded: past kHostWaitPolls polls it raises error flag 8 and goes on, so
-// every wave ends.
+// bounded: past `limit` polls it raises error flag 8 and goes on, so every
+// wave ends.
 __global__ void __launch_bounds__(kCombThreads)
     combine_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ route_pos,
                    const float* __restrict__ w, const uint16_t* __restrict__ Y, const float* P, int T, int k, int d,
                    uint16_t* __restrict__ y, const uint64_t* done, const uint64_t* seq_dev, uint64_t seq,
-                   int32_t* errflag) {
+                   uint32_t limit, int32_t* errflag) {
     if (done) {
         if (threadIdx.x == 0) {
             const uint64_t n = seq_dev ? *seq_dev : seq;
             for (uint32_t it = 0; __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < n; ++it) {
-                if (it >= kHostWaitPolls) {
+                if (it >= limit) {
                     atomicOr(errflag, 8);
                     break;
                 }
@@ -86,7 +85,7 @@ hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, in
         seq = wait->seq;
     }
     hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, st, routes, c->plan.route_pos, w, c->Y, P, T,
-                       c->sh.top_k, d, y, done, seq_dev, seq, c->errflag);
+                       c->sh.top_k, d, y, done, seq_dev, seq, c->host_wait_polls, c->errflag);
     return hipGetLastError();
 }
 

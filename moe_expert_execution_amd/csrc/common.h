@@ -71,12 +71,14 @@ struct HostStaging {
 HostStaging host_branch_staging(HostBranch* hb);
 // How a forward call hands work to the host branch.  Mailbox: the planner
 // stores `seq` to *seq_word (pinned) after staging; a polling host thread runs
-// the call and stores `seq` to *done_word, which the stream waits for.
-// Otherwise a stream host function runs the call.
+// the call and stores `seq` to *done_word, which the combine kernel polls
+// (bounded) before it reads the host partials.  Otherwise a stream host
+// function runs the call.
 // Graph mailbox (calls captured into a graph): the planner draws the call's
 // number from a device counter, stores layer and T, then the number, to the
-// mailbox's graph words; the poller answers in gdone, which a bounded polling
-// kernel waits for (numbers fixed at capture could not be replayed).
+// mailbox's graph words; the poller answers in gdone, which the combine
+// kernel polls against the device counter (numbers fixed at capture could not
+// be replayed).
 struct HostSignal {
     bool mailbox;
     uint64_t seq;
@@ -148,6 +150,7 @@ struct ft_cache {
     uint64_t* clock;           // [1]
     unsigned long long* counters;  // [C_N]
     int32_t* errflag;          // [1]
+    uint32_t host_wait_polls;  // bound of the combine's wait for the host branch (FTMOE_HOST_WAIT_POLLS)
     uint64_t* gseq_dev;        // [1] number of the last host-branch call made by a graph replay
     // internal copy of the last classify's fill worklist and counts
     int32_t* wl_counts;        // [4]

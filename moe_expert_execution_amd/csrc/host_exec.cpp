@@ -59,7 +59,8 @@ struct HostBranch {
     std::mutex mu;
     std::condition_variable cv;
     std::atomic<uint64_t> gen{0};
-    std::atomic<bool> stop{false};
+    std::atomic<bool> stop{false};          // workers
+    std::atomic<bool> stop_poller{false};   // the mailbox poller (stopped first)
     Job job;
     int cur_expert = 0;
     std::atomic<int> next_block{0};
@@ -429,7 +430,7 @@ void poller_main(HostBranch* hb, int cpu) {
     uint64_t* g = hb->mbox + 16;              // graph calls
     uint64_t last = 0, glast = 0;
     int idle = 0;
-    while (!hb->stop.load(std::memory_order_relaxed)) {
+    while (!hb->stop_poller.load(std::memory_order_relaxed)) {
         const uint64_t gs = __atomic_load_n(g, __ATOMIC_ACQUIRE);
         if (gs != glast) {
             idle = 0;
@@ -450,7 +451,7 @@ void poller_main(HostBranch* hb, int cpu) {
             continue;
         }
         idle = 0;
-        for (uint64_t n = last + 1; n <= s; ++n) {
+        for (uint64_t n = last + 1; n <= s && !hb->stop_poller.load(std::memory_order_relaxed); ++n) {
             const HostBranch::Params p = hb->params[n % kRing];
             run_call(hb, p.layer, p.T);
             __atomic_store_n(done_word, n, __ATOMIC_RELEASE);
@@ -515,14 +516,11 @@ HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const
         int cpu = cpus.empty() ? -1 : cpus[(i + 2) % cpus.size()];
         hb->workers.emplace_back(worker_main, hb, i, cpu);
     }
-    // signalling: a polled mailbox when the device can wait on a memory value
-    // (FTMOE_HOST_SIGNAL=callback forces stream host functions)
-    int dev = 0, can_wait = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&can_wait, hipDeviceAttributeCanUseStreamWaitValue, dev) != hipSuccess)
-        can_wait = 0;
+    // signalling: a polled mailbox in pinned memory, whose done word the
+    // combine kernel polls (FTMOE_HOST_SIGNAL=callback forces stream host
+    // functions)
     const char* sig = getenv("FTMOE_HOST_SIGNAL");
-    hb->use_mailbox = can_wait && !(sig && strcmp(sig, "callback") == 0);
+    hb->use_mailbox = !(sig && strcmp(sig, "callback") == 0);
     if (hb->use_mailbox) hb->poller = std::thread(poller_main, hb, cpus.empty() ? -1 : cpus[1 % cpus.size()]);
     return hb;
 }
@@ -558,12 +556,16 @@ HostSignal host_branch_graph_signal(HostBranch* hb, uint64_t* gseq_dev, int32_t 
 
 void host_branch_destroy(HostBranch* hb) {
     if (!hb) return;
+    // the poller first: a call it is running needs every worker, so the
+    // workers stop only once it has returned (the host can still be behind
+    // the device here, when a combine gave up waiting for it)
+    hb->stop_poller.store(true);
+    if (hb->poller.joinable()) hb->poller.join();
     {
         std::lock_guard<std::mutex> lk(hb->mu);
         hb->stop.store(true);
     }
     hb->cv.notify_all();
-    if (hb->poller.joinable()) hb->poller.join();
     for (auto& t : hb->workers) t.join();
     if (hb->stg.x) (void)hipHostFree(hb->stg.x);
     if (hb->stg.routes) (void)hipHostFree(hb->stg.routes);
