@@ -143,7 +143,9 @@ typedef struct {
  *   pool is authoritative: "The Expert Cache That Follows the Router", section
  *   "One logical expert, two physical levels of memory").  It must stay valid
  *   and unchanged until ft_cache_destroy.
- * num_slots: N complete records allocated in HBM (1..32768).
+ * num_slots: N complete records allocated in HBM (1..32768), one slot every
+ *   ft_record_bytes() rounded up to 256 bytes (so each slot's record starts
+ *   aligned; a bank record is copied into a slot whole).
  * max_tokens: largest T any later call will pass (sizes internal buffers),
  *   1..65535, with max_tokens * top_k * d_ff * 2 below 4 GiB (the expert
  *   GEMMs reach activation rows through 32-bit byte offsets).

@@ -25,7 +25,7 @@ void set_error(const char* fmt, ...) {
 
 void clear_error() { g_err[0] = 0; }
 
-bool record_layout(const ft_shape& s, RecordLayout* o) {
+static bool record_layout_packed(const ft_shape& s, RecordLayout* o) {
     const int64_t d = s.d_model, f = s.d_ff, fd = d * f;
     if (d <= 0 || f <= 0 || d % 128 || f % 128 || d > 32768 || f > 8192) return false;
     switch (s.fmt) {
@@ -60,6 +60,12 @@ bool record_layout(const ft_shape& s, RecordLayout* o) {
         }
     }
     return false;
+}
+
+bool record_layout(const ft_shape& s, RecordLayout* o) {
+    if (!record_layout_packed(s, o)) return false;
+    o->P = (o->S + 255) & ~(int64_t)255;
+    return true;
 }
 
 // ---- expert-kernel timing: a ring of event pairs, folded into totals when a
@@ -210,9 +216,14 @@ ft_status enqueue_load(ft_cache* c, int layer, int buf, hipStream_t st) {
     }
     if (c->release_recorded[buf]) FT_HIP(hipStreamWaitEvent(c->xfer, c->release[buf], 0));
     FT_HIP(launch_invalidate(c, buf, c->xfer));
-    const int64_t E = c->sh.experts, S = c->rl.S;
-    FT_HIP(hipMemcpyAsync(c->pool + (int64_t)buf * E * S, c->bank_host + (int64_t)layer * E * S, E * S,
-                          hipMemcpyHostToDevice, c->xfer));
+    const int64_t E = c->sh.experts, S = c->rl.S, P = c->rl.P;
+    if (P == S) {
+        FT_HIP(hipMemcpyAsync(c->pool + (int64_t)buf * E * P, c->bank_host + (int64_t)layer * E * S, E * S,
+                              hipMemcpyHostToDevice, c->xfer));
+    } else {   // records of S bytes into slots P bytes apart
+        FT_HIP(hipMemcpy2DAsync(c->pool + (int64_t)buf * E * P, (size_t)P, c->bank_host + (int64_t)layer * E * S,
+                                (size_t)S, (size_t)S, (size_t)E, hipMemcpyHostToDevice, c->xfer));
+    }
     FT_HIP(hipEventRecord(c->ready[buf], c->xfer));
     FT_HIP(hipEventRecord(c->ev_xlast, c->xfer));
     c->xfer_pending = true;
@@ -300,7 +311,7 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     c->bank_dev = static_cast<const uint8_t*>(dptr);
     const int64_t L = shape->layers, E = shape->experts, S = c->rl.S, d = shape->d_model, f = shape->d_ff;
     const int64_t cap = c->cap;
-    CK(hipMalloc(reinterpret_cast<void**>(&c->pool), (size_t)(c->N * S)));
+    CK(hipMalloc(reinterpret_cast<void**>(&c->pool), (size_t)(c->N * c->rl.P)));
     CK(dalloc(&c->slot_for_id, L * E));
     CK(dalloc(&c->id_of_slot, c->N));
     CK(dalloc(&c->stamp, c->N));
@@ -530,7 +541,7 @@ ft_status ft_cache_resize(ft_cache* c, int64_t new_num_slots) {
         return e == hipErrorOutOfMemory ? FT_ERR_NOMEM : FT_ERR_HIP;
     };
     hipError_t e;
-    if ((e = hipMalloc(reinterpret_cast<void**>(&npool), (size_t)(Nn * S)))) return fail(e);
+    if ((e = hipMalloc(reinterpret_cast<void**>(&npool), (size_t)(Nn * c->rl.P)))) return fail(e);
     if ((e = dalloc(&nios, Nn))) return fail(e);
     if ((e = dalloc(&nstamp, Nn))) return fail(e);
     if ((e = dalloc(&src, std::max<size_t>(res.size(), 1)))) return fail(e);
@@ -543,7 +554,7 @@ ft_status ft_cache_resize(ft_cache* c, int64_t new_num_slots) {
     }
     if (!res.empty()) {
         if ((e = hipMemcpy(src, res.data(), sizeof(int32_t) * res.size(), hipMemcpyHostToDevice))) return fail(e);
-        if ((e = launch_resize_gather(c->pool, npool, S, src, (int)res.size(), 0))) return fail(e);
+        if ((e = launch_resize_gather(c->pool, npool, c->rl.P, src, (int)res.size(), 0))) return fail(e);
         if ((e = hipDeviceSynchronize())) return fail(e);
     }
     FT_HIP(hipMemcpy(nios, h_ios.data(), sizeof(int32_t) * Nn, hipMemcpyHostToDevice));
@@ -761,7 +772,7 @@ ft_status ft_cache_read_slot(const ft_cache* c, int64_t slot, void* dst) {
     FT_REQUIRE(slot >= 0 && slot < c->N, "slot out of range");
     ft_status fs = flush_fill_sync(const_cast<ft_cache*>(c));
     if (fs != FT_OK) return fs;
-    FT_HIP(hipMemcpy(dst, c->pool + slot * c->rl.S, (size_t)c->rl.S, hipMemcpyDeviceToHost));
+    FT_HIP(hipMemcpy(dst, c->pool + slot * c->rl.P, (size_t)c->rl.S, hipMemcpyDeviceToHost));
     return FT_OK;
 }
 

@@ -50,7 +50,10 @@ void clear_error();
 
 // ---- record geometry ------------------------------------------------------------
 struct RecordLayout {
-    int64_t S;             // bytes per record
+    int64_t S;             // bytes per record (the host bank's record stride)
+    int64_t P;             // slot stride of the device pool: S rounded up to 256 bytes, so every slot's
+                           // record starts aligned for 16-byte loads (block-FP8 records of small d, f
+                           // are not multiples of 16 bytes)
     int64_t off_gate, off_up, off_down;         // code / value offsets
     int64_t off_sg, off_su, off_sd;             // scale offsets (fp8, mxfp4)
 };
@@ -188,7 +191,7 @@ hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, 
 hipError_t launch_fill(ft_cache* c, hipStream_t st, TimedLaunch tl = TimedLaunch());
 hipError_t launch_invalidate(ft_cache* c, int buf, hipStream_t st);
 hipError_t launch_register(ft_cache* c, int layer, int buf, hipStream_t st);
-hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t S, const int32_t* src_slots,
+hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t P, const int32_t* src_slots,
                                 int n, hipStream_t st);
 // plan: routes -> active slots, sorted rows, tiles.  slot_base >= 0 means routes
 // are raw expert ids mapped to slot slot_base + e (full-layer buffer).

@@ -332,8 +332,8 @@ constexpr int kFillBlocks = 512;
 
 __global__ void __launch_bounds__(kFillThreads)
     fill_kernel(const int32_t* wl_counts, const int32_t* wl_slot, const int32_t* wl_src,
-                const uint8_t* __restrict__ bank, uint8_t* __restrict__ pool, int64_t S) {
-    fill_records<kFillThreads>(wl_counts, wl_slot, wl_src, bank, pool, S, blockIdx.x, gridDim.x);
+                const uint8_t* __restrict__ bank, uint8_t* __restrict__ pool, int64_t S, int64_t P) {
+    fill_records<kFillThreads>(wl_counts, wl_slot, wl_src, bank, pool, S, P, blockIdx.x, gridDim.x);
 }
 
 // Clear the owners of full-layer buffer slots [s0, s0 + E) before a layer is
@@ -377,18 +377,19 @@ __global__ void register_kernel(int32_t layer, int32_t s0, int32_t E, int32_t* s
     }
 }
 
-// new_pool[i] = old_pool[src_slots[i]] for i < n (whole records).
+// new_pool[i] = old_pool[src_slots[i]] for i < n (whole slots of P bytes, P a
+// multiple of 256).
 __global__ void __launch_bounds__(kFillThreads)
-    gather_kernel(const uint8_t* __restrict__ old_pool, uint8_t* __restrict__ new_pool, int64_t S,
+    gather_kernel(const uint8_t* __restrict__ old_pool, uint8_t* __restrict__ new_pool, int64_t P,
                   const int32_t* src_slots, int n) {
-    const int64_t cpr = (S + kFillChunk - 1) / kFillChunk;
+    const int64_t cpr = (P + kFillChunk - 1) / kFillChunk;
     const int64_t total = (int64_t)n * cpr;
     for (int64_t c = blockIdx.x; c < total; c += gridDim.x) {
         const int64_t i = c / cpr;
         const int64_t off = (c - i * cpr) * kFillChunk;
-        const int64_t len = (S - off) < kFillChunk ? (S - off) : kFillChunk;
-        const uint4* src = reinterpret_cast<const uint4*>(old_pool + (int64_t)src_slots[i] * S + off);
-        uint4* dst = reinterpret_cast<uint4*>(new_pool + i * S + off);
+        const int64_t len = (P - off) < kFillChunk ? (P - off) : kFillChunk;
+        const uint4* src = reinterpret_cast<const uint4*>(old_pool + (int64_t)src_slots[i] * P + off);
+        uint4* dst = reinterpret_cast<uint4*>(new_pool + i * P + off);
         for (int64_t b = threadIdx.x; b < len / 16; b += kFillThreads) dst[b] = src[b];
     }
 }
@@ -437,7 +438,7 @@ hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, 
 hipError_t launch_fill(ft_cache* c, hipStream_t st, TimedLaunch tl) {
     hipExtLaunchKernelGGL(fill_kernel, dim3(kFillBlocks), dim3(kFillThreads), 0, st, tl.start, tl.stop, 0,
                           (const int32_t*)c->wl_counts, (const int32_t*)c->wl_slot, (const int32_t*)c->wl_src,
-                          c->bank_dev, c->pool, c->rl.S);
+                          c->bank_dev, c->pool, c->rl.S, c->rl.P);
     return hipGetLastError();
 }
 
@@ -453,10 +454,10 @@ hipError_t launch_register(ft_cache* c, int layer, int buf, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t S, const int32_t* src_slots,
+hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int64_t P, const int32_t* src_slots,
                                 int n, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gather_kernel, dim3(kFillBlocks), dim3(kFillThreads), 0, st, old_pool, new_pool, S,
+    hipLaunchKernelGGL(gather_kernel, dim3(kFillBlocks), dim3(kFillThreads), 0, st, old_pool, new_pool, P,
                        src_slots, n);
     return hipGetLastError();
 }

@@ -44,7 +44,7 @@ struct GemmArgs {
     const int32_t* tile_row0;
     const int32_t* tile_first;
     const uint8_t* pool;
-    int64_t S;
+    int64_t S;          // slot stride of the pool (bytes)
     int64_t off_gate, off_up, off_down, off_sg, off_su, off_sd;
 };
 
@@ -451,7 +451,7 @@ hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     a.tile_row0 = c->plan.tile_row0;
     a.tile_first = c->plan.tile_first;
     a.pool = c->pool;
-    a.S = c->rl.S;
+    a.S = c->rl.P;   // slot stride of the pool
     a.off_gate = c->rl.off_gate;
     a.off_up = c->rl.off_up;
     a.off_down = c->rl.off_down;

@@ -39,7 +39,7 @@ struct GemvArgs {
     const int32_t* seg;
     const int32_t* perm;
     const uint8_t* pool;
-    int64_t S;
+    int64_t S;          // slot stride of the pool (bytes)
     int64_t off_gate, off_up, off_down, off_sg, off_su, off_sd;
     float* part;        // [2][kq][cap_g][f]: K-part sums of g (0) and u (1)
     uint16_t* hb;       // [cap_g][f] bf16 h, when formed once by the finalize kernel
@@ -498,7 +498,7 @@ hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st) {
     a.seg = c->plan.seg;
     a.perm = c->plan.perm;
     a.pool = c->pool;
-    a.S = c->rl.S;
+    a.S = c->rl.P;   // slot stride of the pool
     a.off_gate = c->rl.off_gate;
     a.off_up = c->rl.off_up;
     a.off_down = c->rl.off_down;

@@ -237,7 +237,7 @@ struct FillArgs {
     const int32_t* wl_src;
     const uint8_t* bank;
     uint8_t* pool;
-    int64_t S;
+    int64_t S, P;   // bank record stride, pool slot stride
 };
 constexpr int kPlanFillBlocks = 512;   // fill workgroups of kPlanThreads beside the planner: one 64 KiB chunk each for q <= 3 at decode sizes
 
@@ -253,7 +253,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_fill_kernel(PlanArgs a, Fil
     // 256 threads per workgroup pull, as in the fill kernel: a workgroup's
     // host reads in flight set the PCIe rate
     if (threadIdx.x < 256)
-        fill_records<256>(f.wl_counts, f.wl_slot, f.wl_src, f.bank, f.pool, f.S, blockIdx.x - 1, gridDim.x - 1);
+        fill_records<256>(f.wl_counts, f.wl_slot, f.wl_src, f.bank, f.pool, f.S, f.P, blockIdx.x - 1,
+                          gridDim.x - 1);
 }
 
 // ---- chunked planner (any R; key space <= 8192) --------------------------------
@@ -420,7 +421,7 @@ hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base,
     a.work = c->counters + work_counter;
     if (fill) {
         if (a.R > kSmallPlanRoutes) return hipErrorInvalidValue;
-        FillArgs f{c->wl_counts, c->wl_slot, c->wl_src, c->bank_dev, c->pool, c->rl.S};
+        FillArgs f{c->wl_counts, c->wl_slot, c->wl_src, c->bank_dev, c->pool, c->rl.S, c->rl.P};
         hipExtLaunchKernelGGL(plan_fill_kernel, dim3(1 + kPlanFillBlocks), dim3(kPlanThreads), 0, st, fill->start,
                               fill->stop, 0, a, f);
     } else if (a.R <= kSmallPlanRoutes) {

@@ -47,22 +47,24 @@ class Step:
 
 
 @gpu
-@pytest.mark.parametrize("signal", ["mailbox", "callback"])
-def test_graph_replay_equals_eager_step_for_step(signal, monkeypatch):
+@pytest.mark.parametrize("signal,fmt", [("mailbox", "bf16"), ("callback", "bf16"), ("mailbox", "fp8"),
+                                        ("mailbox", "mxfp4")])
+def test_graph_replay_equals_eager_step_for_step(signal, fmt, monkeypatch):
     """`mailbox`: the captured calls post to the polling host thread with
     device-drawn numbers; `callback`: stream host functions, captured as host
-    nodes (FTMOE_HOST_SIGNAL is read when a cache is created)."""
+    nodes (FTMOE_HOST_SIGNAL is read when a cache is created).  Every weight
+    format with the mailbox."""
     cuda()
     if signal == "callback":
         monkeypatch.setenv("FTMOE_HOST_SIGNAL", "callback")
     # a small cache under pressure: hits, fills and host-run misses every step
     cfg = synth.CONFIGS["decode"].with_(layers=4, d=256, E=16, k=4, f=128, slots=12, bp_mbps=20000,
-                                        bh_mbps=60000)
+                                        bh_mbps=60000, fmt=fmt)
     steps = 12
     bank = make_bank(cfg)
     recs = bank.records(cfg.S)
     xs, wr = _setup(cfg, steps)
-    mk = lambda: SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, 1, cfg.bp_mbps,
+    mk = lambda: SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, fmt, bank.ptr, cfg.slots, 1, cfg.bp_mbps,
                            cfg.bh_mbps)
     a, b = mk(), mk()
     try:
@@ -92,7 +94,8 @@ def test_graph_replay_equals_eager_step_for_step(signal, monkeypatch):
                 w = ea.w.cpu().numpy()
                 for l in range(cfg.layers):
                     ref = OM.moe_layer(x[l:l + 1], ids[l:l + 1], w[l:l + 1], expert_fn(recs, cfg, l))
-                    assert_close_rel(bf16_bits_to_f64(gb.y[l:l + 1]), ref, 2e-2, f"graph step {s} layer {l}")
+                    assert_close_rel(bf16_bits_to_f64(gb.y[l:l + 1]), ref, 2e-2 if fmt == "bf16" else 5e-2,
+                                     f"graph step {s} layer {l}")
         ca, cb = M.ft_cache_stats(a.handle), M.ft_cache_stats(b.handle)
         for key in ("calls", "unique", "hits", "misses", "fills", "cpu_experts", "evictions", "host_experts"):
             assert getattr(ca, key) == getattr(cb, key), key
