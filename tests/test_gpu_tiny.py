@@ -37,17 +37,28 @@ def test_route_tiny_bit_exact():
 
 
 @gpu
-@pytest.mark.parametrize("cfgname,T,E", [("decode", 1, None), ("decode", 300, None), ("mxfp4", 37, None),
-                                         ("tiny", 5, None), ("decode", 1531, None), ("fp8", 1000, None),
-                                         ("decode", 77, 64), ("decode", 40, 96)])
-def test_route_shapes_bit_exact(cfgname, T, E):
+@pytest.mark.parametrize("cfgname,T,E,k,d", [
+    ("decode", 1, None, None, None), ("decode", 300, None, None, None), ("mxfp4", 37, None, None, None),
+    ("tiny", 5, None, None, None), ("decode", 1531, None, None, None), ("fp8", 1000, None, None, None),
+    ("decode", 77, 64, None, None), ("decode", 40, 96, None, None),
+    # one token with E % 8 != 0; 2..16 tokens with odd E; one and 16 tokens at E = 256; the
+    # general kernel at E = 200; d off a multiple of 128; a single expert
+    ("tiny", 1, 5, 2, None), ("tiny", 7, 12, 3, None), ("fp8", 1, None, None, None),
+    ("mxfp4", 16, None, None, None), ("decode", 17, 200, 6, None), ("tiny", 3, 24, 4, 200),
+    ("tiny", 33, 60, 5, 72), ("tiny", 4, 1, 1, None)])
+def test_route_shapes_bit_exact(cfgname, T, E, k, d):
     """Routing ids bit-exact and weights to fp32 rounding against the oracle, for
-    the small-T path, the matrix-core path (E in {64, 128, 256}; ragged last
-    workgroup) and the general path (E = 96)."""
+    the small-T paths (one token, 16-byte router rows when E % 8 == 0; up to 16
+    tokens), the matrix-core path (E in {64, 128, 256}, d % 128 == 0; ragged
+    last workgroup) and the general path."""
     cuda()
     cfg = synth.CONFIGS[cfgname]
     if E is not None:
         cfg = cfg.with_(E=E)
+    if k is not None:
+        cfg = cfg.with_(k=k)
+    if d is not None:
+        cfg = cfg.with_(d=d)
     x = synth.tokens(cfg, T, 11)
     wr = synth.router(cfg, 3)
     ids, w = _route_gpu(cfg, x, wr, T)
