@@ -244,3 +244,30 @@ def test_layer_at_the_size_limits(fmt, d, f):
     finally:
         sc.close()
         bank.close()
+
+
+@gpu
+@pytest.mark.parametrize("T,k", [(128, 8), (129, 8), (6, 1), (300, 1)])
+def test_planner_boundary_and_top1(T, k):
+    """T * k = 1,024 routes is the largest call of the one-workgroup planner
+    (which rides in the fill's launch); 1,032 takes the chunked planner and
+    a separate fill.  Top-1 routing on both sides of the GEMV/GEMM switch.
+    Decode shape, 64 slots, every class mixed; all rows against the oracle."""
+    cuda()
+    cfg = synth.CONFIGS["decode"].with_(layers=1, slots=64, k=k)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, T, cfg.bp_mbps, cfg.bh_mbps)
+    try:
+        ex = expert_fn(recs, cfg, 0, maxsize=cfg.E)
+        wr = synth.router(cfg, 0)
+        for s in range(2):
+            x = synth.tokens(cfg, T, 800 + s)
+            ids, w, _ = OR.route(x, wr, cfg.k)
+            y, routes = run_cached(sc, 0, x, ids, w)
+            assert (routes < 0).any() or s > 0
+            assert_close_rel(y, oracle_rows(x, ids, w, ex, np.arange(T)), TOL["bf16"], f"T {T} k {k} call {s}")
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
