@@ -149,7 +149,9 @@ typedef struct {
  * max_tokens: largest T any later call will pass (sizes internal buffers),
  *   1..65535, with max_tokens * top_k * d_ff * 2 below 4 GiB (the expert
  *   GEMMs reach activation rows through 32-bit byte offsets).
- * Errors: FT_ERR_ARG (shape, null, N, max_tokens), FT_ERR_NOMEM, FT_ERR_HIP.
+ * Errors: FT_ERR_ARG (shape, null, N, max_tokens; a host_bank that is not
+ *   pinned, or whose allocation is known to end before layers * experts
+ *   records), FT_ERR_NOMEM, FT_ERR_HIP.
  * Synchronises the current device.
  *
  * Record layout (S bytes), matrices [rows x K] in this order:

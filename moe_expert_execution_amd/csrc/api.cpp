@@ -309,6 +309,26 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
         return FT_ERR_ARG;
     }
     c->bank_dev = static_cast<const uint8_t*>(dptr);
+    {
+        // Where the runtime knows the bank's allocation (hipHostMalloc memory),
+        // it must reach layers * experts records past host_bank: fills and
+        // layer loads read the bank from the device, where a short bank faults.
+        const int64_t need = (int64_t)shape->layers * shape->experts * c->rl.S;
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        if (hipMemGetAddressRange(&base, &size, const_cast<void*>(host_bank)) == hipSuccess && base && size) {
+            const int64_t avail =
+                (int64_t)(static_cast<const uint8_t*>(base) + size - static_cast<const uint8_t*>(host_bank));
+            if (avail < need) {
+                free_cache(c);
+                set_error("host bank allocation holds %lld bytes from host_bank; layers * experts records need %lld",
+                          (long long)avail, (long long)need);
+                return FT_ERR_ARG;
+            }
+        } else {
+            (void)hipGetLastError();   // an untracked pointer: no check, and no stale error left behind
+        }
+    }
     const int64_t L = shape->layers, E = shape->experts, S = c->rl.S, d = shape->d_model, f = shape->d_ff;
     const int64_t cap = c->cap;
     CK(hipMalloc(reinterpret_cast<void**>(&c->pool), (size_t)(c->N * c->rl.P)));

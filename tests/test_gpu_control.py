@@ -29,7 +29,7 @@ class TraceRunner:
         self.small = cfg.with_(d=128, f=128, fmt="bf16") if small else cfg
         self.bank = make_bank(self.small)
         maxT = max(calls_T)
-        self.sc = SlotCache(cfg.layers, cfg.E, cfg.k, self.small.d, self.small.f, "bf16", self.bank.ptr,
+        self.sc = SlotCache(cfg.layers, cfg.E, cfg.k, self.small.d, self.small.f, self.small.fmt, self.bank.ptr,
                             cfg.slots, maxT, cfg.bp_mbps, cfg.bh_mbps, cfg.max_fetch)
         self.sim = OC.SlotCacheSim(cfg.layers, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps, cfg.max_fetch)
         n = len(calls_T)
@@ -339,3 +339,29 @@ def test_warm_decode_variant_gpu():
     finally:
         sc.close()
         bank.close()
+
+
+@gpu
+@pytest.mark.parametrize("slots", [12000, 32768])
+def test_control_at_the_maxima(slots):
+    """E = 4,096 experts (the largest accepted), 512-token calls (4,096 routes)
+    and up to N = 32,768 slots (the largest accepted; 12,000 and 32,768 take
+    the victim scan's 16- and 32-keys-per-thread kernels), with more
+    layer-experts (40,960) than slots, so the pool fills and then evicts;
+    every output and the maps bit-exact against the simulator.  Records are
+    the smallest the library accepts (MXFP4, d = f = 128)."""
+    cuda()
+    cfg = synth.CONFIGS["tiny"].with_(layers=10, E=4096, k=8, d=128, f=128, fmt="mxfp4", slots=slots,
+                                      bp_mbps=60000, bh_mbps=60000)
+    rng = np.random.default_rng(slots)
+    calls = 40
+    tr = TraceRunner(cfg, [512] * calls, small=False)
+    try:
+        for i in range(calls):
+            ids = np.stack([rng.choice(cfg.E, size=cfg.k, replace=False) for _ in range(512)])
+            tr.call(int(rng.integers(0, cfg.layers)), ids)
+        hits, fills, cpu = tr.check()
+        s = M.ft_cache_stats(tr.sc.handle)
+        assert fills > slots and s.evictions > 0 and hits > 0
+    finally:
+        tr.close()

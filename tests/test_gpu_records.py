@@ -108,3 +108,31 @@ def test_streamed_layer_load_copies_whole_records(fmt, d, f):
     finally:
         sc.close()
         bank.close()
+
+
+@gpu
+def test_short_host_bank_is_refused():
+    """A pinned bank whose allocation ends before layers * experts records is
+    refused when the cache is created (nothing is launched); a bank of the
+    full size is accepted, also when it starts inside a larger allocation."""
+    from moe_expert_execution_amd.tensors import PinnedBank
+    cuda()
+    cfg = synth.CONFIGS["tiny"].with_(layers=2)
+    need = cfg.layers * cfg.E * cfg.S
+    mk = lambda ptr: SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, cfg.fmt, ptr, cfg.slots, 4, cfg.bp_mbps,
+                               cfg.bh_mbps)
+    short = PinnedBank(need - 4096)
+    try:
+        with pytest.raises(M.FtError) as ei:
+            mk(short.ptr)
+        assert ei.value.status == M.FT_ERR_ARG, str(ei.value)
+    finally:
+        short.close()
+    big = PinnedBank(need + 8192)
+    try:
+        mk(big.ptr + 4096).close()
+        with pytest.raises(M.FtError) as ei:
+            mk(big.ptr + 8192 + 256)
+        assert ei.value.status == M.FT_ERR_ARG, str(ei.value)
+    finally:
+        big.close()
