@@ -37,7 +37,8 @@ def _slots_hold_their_records(sc, recs, n_ids, n_slots, what):
 def test_fills_and_resize_copy_whole_records(fmt, d, f):
     """Cold cache, every miss filled (B_P = B_H): decode calls (GEMV) and
     T = 5 calls (GEMM) against the oracle, slot bytes against the bank; then
-    a resize to fewer slots against the simulator, and calls after it."""
+    resizes to fewer and to more slots against the simulator, with calls
+    after each."""
     cuda()
     cfg = synth.CONFIGS["decode"].with_(layers=2, d=d, f=f, E=16, k=4, slots=16, fmt=fmt, bp_mbps=60000,
                                         bh_mbps=60000)
@@ -69,6 +70,16 @@ def test_fills_and_resize_copy_whole_records(fmt, d, f):
         assert _slots_hold_their_records(sc, recs, n_ids, 10, "after resize") == sum(1 for u in s_ios if u >= 0)
         for i, T in enumerate((1, 5)):
             call(i % 2, T, 400 + i)
+        # and back up: the residents keep their slots' order, the new slots start empty
+        M.ft_cache_resize(sc.handle, 24)
+        sim.resize(24)
+        sfi, ios, st, clk = M.ft_cache_snapshot(sc.handle, n_ids, 24)
+        s_sfi, s_ios, s_st, s_clk = sim.arrays()
+        assert np.array_equal(sfi, s_sfi) and np.array_equal(ios, s_ios) and np.array_equal(st, s_st)
+        assert clk == s_clk
+        assert _slots_hold_their_records(sc, recs, n_ids, 24, "after growth") == sum(1 for u in s_ios if u >= 0)
+        for i, T in enumerate((5, 1, 5)):
+            call(i % 2, T, 450 + i)
         assert M.ft_cache_stats(sc.handle).error_flags == 0
     finally:
         sc.close()
