@@ -15,60 +15,68 @@ from oracle import moe as OM
 from gpu_util import assert_close_rel, bf16_bits_to_f64, cuda, expert_fn, gpu, make_bank
 
 
-def _setup(cfg, steps):
-    L, E, k, d = cfg.layers, cfg.E, cfg.k, cfg.d
-    xs = torch.stack([torch.from_numpy(synth.ar1_tokens(cfg, l, steps).view(np.int16)) for l in range(L)]).cuda()
+def _setup(cfg, steps, T=1):
+    """Per layer: `steps` calls of T tokens (T = 1: the AR(1) decode stream)."""
+    L = cfg.layers
+    if T == 1:
+        xs = torch.stack([torch.from_numpy(synth.ar1_tokens(cfg, l, steps).view(np.int16)) for l in range(L)])
+        xs = xs[:, :, None, :]
+    else:
+        xs = torch.stack([torch.stack([torch.from_numpy(synth.tokens(cfg, T, 60 + s, l).view(np.int16))
+                                       for s in range(steps)]) for l in range(L)])
     wr = torch.stack([torch.from_numpy(synth.router(cfg, l).view(np.int16)) for l in range(L)]).cuda()
-    return xs, wr
+    return xs.cuda(), wr
 
 
 class Step:
-    """Fixed buffers of one decode step (one token through every layer)."""
+    """Fixed buffers of one step: T tokens through every layer."""
 
-    def __init__(self, cfg, sc, wr):
+    def __init__(self, cfg, sc, wr, T=1):
         L, k, d = cfg.layers, cfg.k, cfg.d
-        self.cfg, self.sc, self.wr = cfg, sc, wr
-        self.x = torch.zeros((L, d), dtype=torch.int16, device="cuda")
-        self.ids = torch.zeros((L, k), dtype=torch.int32, device="cuda")
-        self.routes = torch.zeros((L, k), dtype=torch.int32, device="cuda")
-        self.w = torch.zeros((L, k), dtype=torch.float32, device="cuda")
-        self.y = torch.zeros((L, d), dtype=torch.int16, device="cuda")
+        self.cfg, self.sc, self.wr, self.T = cfg, sc, wr, T
+        self.x = torch.zeros((L, T, d), dtype=torch.int16, device="cuda")
+        self.ids = torch.zeros((L, T, k), dtype=torch.int32, device="cuda")
+        self.routes = torch.zeros((L, T, k), dtype=torch.int32, device="cuda")
+        self.w = torch.zeros((L, T, k), dtype=torch.float32, device="cuda")
+        self.y = torch.zeros((L, T, d), dtype=torch.int16, device="cuda")
 
     def enqueue(self):
-        h, shp = self.sc.handle, self.sc.shape
+        h, shp, T = self.sc.handle, self.sc.shape, self.T
         st = torch.cuda.current_stream().cuda_stream
         for l in range(self.cfg.layers):
-            M.ft_moe_route(shp, self.x[l].data_ptr(), self.wr[l].data_ptr(), 1, self.ids[l].data_ptr(),
+            M.ft_moe_route(shp, self.x[l].data_ptr(), self.wr[l].data_ptr(), T, self.ids[l].data_ptr(),
                            self.w[l].data_ptr(), st)
             self.routes[l].copy_(self.ids[l])
-            M.ft_cache_classify(h, l, self.routes[l].data_ptr(), 1, None, st)
+            M.ft_cache_classify(h, l, self.routes[l].data_ptr(), T, None, st)
             M.ft_moe_forward(h, l, M.FT_MODE_CACHED, self.x[l].data_ptr(), self.routes[l].data_ptr(),
-                             self.w[l].data_ptr(), 1, self.y[l].data_ptr(), st)
+                             self.w[l].data_ptr(), T, self.y[l].data_ptr(), st)
 
 
 @gpu
-@pytest.mark.parametrize("signal,fmt", [("mailbox", "bf16"), ("callback", "bf16"), ("mailbox", "fp8"),
-                                        ("mailbox", "mxfp4")])
-def test_graph_replay_equals_eager_step_for_step(signal, fmt, monkeypatch):
+@pytest.mark.parametrize("signal,fmt,T", [("mailbox", "bf16", 1), ("callback", "bf16", 1), ("mailbox", "fp8", 1),
+                                          ("mailbox", "mxfp4", 1), ("mailbox", "bf16", 3), ("mailbox", "bf16", 8)])
+def test_graph_replay_equals_eager_step_for_step(signal, fmt, T, monkeypatch):
     """`mailbox`: the captured calls post to the polling host thread with
     device-drawn numbers; `callback`: stream host functions, captured as host
     nodes (FTMOE_HOST_SIGNAL is read when a cache is created).  Every weight
-    format with the mailbox."""
+    format with the mailbox; calls of 3 tokens (the 4-row GEMV) and of 8
+    (the grouped GEMM)."""
     cuda()
     if signal == "callback":
         monkeypatch.setenv("FTMOE_HOST_SIGNAL", "callback")
     # a small cache under pressure: hits, fills and host-run misses every step
-    cfg = synth.CONFIGS["decode"].with_(layers=4, d=256, E=16, k=4, f=128, slots=12, bp_mbps=20000,
-                                        bh_mbps=60000, fmt=fmt)
+    # (calls of several tokens touch most of a layer's experts: more slots)
+    cfg = synth.CONFIGS["decode"].with_(layers=4, d=256, E=16, k=4, f=128, slots=12 if T == 1 else 40,
+                                        bp_mbps=20000, bh_mbps=60000, fmt=fmt)
     steps = 12
     bank = make_bank(cfg)
     recs = bank.records(cfg.S)
-    xs, wr = _setup(cfg, steps)
-    mk = lambda: SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, fmt, bank.ptr, cfg.slots, 1, cfg.bp_mbps,
+    xs, wr = _setup(cfg, steps, T)
+    mk = lambda: SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, fmt, bank.ptr, cfg.slots, T, cfg.bp_mbps,
                            cfg.bh_mbps)
     a, b = mk(), mk()
     try:
-        ea, gb = Step(cfg, a, wr), Step(cfg, b, wr)
+        ea, gb = Step(cfg, a, wr, T), Step(cfg, b, wr, T)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -93,8 +101,8 @@ def test_graph_replay_equals_eager_step_for_step(signal, fmt, monkeypatch):
                 ids = ea.ids.cpu().numpy()
                 w = ea.w.cpu().numpy()
                 for l in range(cfg.layers):
-                    ref = OM.moe_layer(x[l:l + 1], ids[l:l + 1], w[l:l + 1], expert_fn(recs, cfg, l))
-                    assert_close_rel(bf16_bits_to_f64(gb.y[l:l + 1]), ref, 2e-2 if fmt == "bf16" else 5e-2,
+                    ref = OM.moe_layer(x[l], ids[l], w[l], expert_fn(recs, cfg, l))
+                    assert_close_rel(bf16_bits_to_f64(gb.y[l]), ref, 2e-2 if fmt == "bf16" else 5e-2,
                                      f"graph step {s} layer {l}")
         ca, cb = M.ft_cache_stats(a.handle), M.ft_cache_stats(b.handle)
         for key in ("calls", "unique", "hits", "misses", "fills", "cpu_experts", "evictions", "host_experts"):
