@@ -189,8 +189,13 @@ int64_t ft_record_bytes(const ft_shape* shape);
  * ids [T x k]  int32, device, out: experts by logit descending, ties to the
  *              lower expert index
  * w  [T x k]   fp32, device, out: softmax over the k chosen logits
- * Logits are accumulated in fp64 from exact bf16 products.  Stateless; T >= 0
- * (T = 0 enqueues nothing).  Errors: FT_ERR_ARG, FT_ERR_HIP.
+ * Logits are accumulated in fp64 from exact bf16 products.  T >= 0 (T = 0
+ * enqueues nothing).  Keeps no state between calls, with one restriction: a
+ * call of T <= 16 tokens passes its partial logits from its first kernel to
+ * its second through one device-wide scratch area of the library, so two such
+ * calls must not run at the same time (e.g. on two streams); calls on one
+ * stream, and calls of more tokens, are unrestricted.  Errors: FT_ERR_ARG,
+ * FT_ERR_HIP.
  * ------------------------------------------------------------------------- */
 ft_status ft_moe_route(const ft_shape* shape, const uint16_t* x, const uint16_t* wr, int32_t T,
                        int32_t* ids, float* w, void* stream);

@@ -129,6 +129,8 @@ __global__ void __launch_bounds__(kRouteThreads)
 // ---- small T (decode): the d-range is split over kRouteDS workgroups so the
 // router matrix streams through many CUs; partial logits go to a file-scope
 // device array and a second kernel adds them in a fixed order, then selects.
+// The array is shared by every call on the device, so two small-T calls must
+// not run concurrently (on one stream they are ordered).
 constexpr int kRouteSmallT = 16;
 constexpr int kRouteDS = 32;
 __device__ double g_route_part[kRouteDS * kRouteSmallT * kRouteMaxE];
