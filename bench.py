@@ -12,7 +12,8 @@ the control kernel, fills, GPU experts, host experts and the combine.
 
 Also reported: the live roofline of the dominant kernel (the decode gate/up
 GEMV, HIP events on the stream it runs on), the oracle timed on the host
-cores on a bounded sample, and a prefill section (8,192-token chunk: MFMA
+cores on a bounded sample, p50/p99 latency of each call of the decode path
+(route, classify, forward), and a prefill section (8,192-token chunk: MFMA
 utilisation of the grouped GEMMs with all experts resident, and 24 layers
 streamed through the double buffer over PCIe).
 
@@ -252,6 +253,40 @@ def decode_bench(args):
         log(f"decode replayed from a HIP graph of one step: {args.steps / el:.1f} tok/s ({el / args.steps * 1e3:.2f} "
             f"ms/step), same decisions as the eager runs: {res['graph']['same_decisions_as_headline']}")
         del g
+        sc.close()
+    if not args.no_latency:
+        # (5) latency of each call on the path: HIP events on the calls' stream
+        # around every route, classify and forward of 2 steps x 48 layers
+        # (after the warm-up, cold start); forward holds the planner + the
+        # PCIe pull of the call's fills, the GPU experts and the combine
+        sc = new_cache()
+        h, shp = sc.handle, sc.shape
+        for s_ in range(args.warmup):
+            step(h, shp, s_)
+        torch.cuda.synchronize()
+        evs = []
+        for s_ in range(args.warmup, args.warmup + min(2, args.steps)):
+            for l in range(L):
+                xp = xs[l, s_].data_ptr()
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                e[0].record()
+                M.ft_moe_route(shp, xp, wr[l].data_ptr(), 1, ids[l].data_ptr(), w[l].data_ptr(), stream)
+                e[1].record()
+                M.ft_cache_classify(h, l, ids[l].data_ptr(), 1, None, stream)
+                e[2].record()
+                M.ft_moe_forward(h, l, M.FT_MODE_CACHED, xp, ids[l].data_ptr(), w[l].data_ptr(), 1,
+                                 y[l].data_ptr(), stream)
+                e[3].record()
+                evs.append(e)
+        torch.cuda.synchronize()
+        lat = {}
+        for name, a_, b_ in (("route", 0, 1), ("classify", 1, 2), ("forward", 2, 3)):
+            v = sorted(e[a_].elapsed_time(e[b_]) * 1e3 for e in evs)
+            lat[name] = {"p50": v[len(v) // 2], "p99": v[min(len(v) - 1, int(0.99 * len(v)))], "calls": len(v)}
+        res["latency_us"] = lat
+        log("per-call latency (us, p50/p99): " +
+            ", ".join(f"{n} {v['p50']:.1f}/{v['p99']:.1f}" for n, v in lat.items()))
+        assert M.ft_cache_stats(h).error_flags == 0
         sc.close()
     return res, bank, cfg
 
@@ -585,6 +620,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the decode run replayed from a HIP graph")
+    ap.add_argument("--no-latency", action="store_true", help="skip the per-call latency run of the decode path")
     ap.add_argument("--no-measured-profile", action="store_true",
                     help="skip the second decode run with the measured B_P / B_H")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (kernel work)")
@@ -655,6 +691,7 @@ def main():
         "branches": dec["branches"],
         "measured_profile": dec.get("measured_profile"),
         "graph": dec.get("graph"),
+        "latency_us": dec.get("latency_us"),
         "prefill": pre,
     }
     print(json.dumps(line), flush=True)
