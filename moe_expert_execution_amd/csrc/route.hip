@@ -21,6 +21,53 @@ __device__ __forceinline__ double bf16_to_f64(uint16_t u) {
     return (double)__uint_as_float((uint32_t)u << 16);
 }
 
+// One wave selects the k largest of the logits zl (lane l holds experts
+// l + 64 j; taken marks slots to skip), ties to the lower expert, and writes
+// the ids and the softmax of the chosen logits (fp64, stored fp32).
+__device__ __forceinline__ void topk_softmax_wave(double (&zl)[kRouteMaxE / 64], bool (&taken)[kRouteMaxE / 64], int lane, int k,
+                                  int32_t* __restrict__ ids, float* __restrict__ w) {
+    double zsel[kMaxTopK];
+    int esel[kMaxTopK];
+    for (int r = 0; r < k; ++r) {
+        // best of this lane: largest z, ties to lower expert index; then across the wave
+        double bz = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxE / 64; ++j) {
+            const int ee = lane + 64 * j;
+            if (!taken[j] && (zl[j] > bz || (zl[j] == bz && ee < be))) {
+                bz = zl[j];
+                be = ee;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const double oz = __shfl_xor(bz, off, 64);
+            const int oe = __shfl_xor(be, off, 64);
+            if (oz > bz || (oz == bz && oe < be)) {
+                bz = oz;
+                be = oe;
+            }
+        }
+        zsel[r] = bz;
+        esel[r] = be;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxE / 64; ++j)
+            if (lane + 64 * j == be) taken[j] = true;
+    }
+    if (lane == 0) {
+        double s = 0.0, ex[kMaxTopK];
+        for (int r = 0; r < k; ++r) {
+            ex[r] = exp(zsel[r] - zsel[0]);
+            s += ex[r];
+        }
+        for (int r = 0; r < k; ++r) {
+            ids[r] = esel[r];
+            w[r] = (float)(ex[r] / s);
+        }
+    }
+}
+
 // Logits of kRouteTokens tokens: thread (g, e) sums the k-slice i = g, g + G,
 // ... of column e; the G partial sums are added in a fixed order.
 __global__ void __launch_bounds__(kRouteThreads)
@@ -82,47 +129,7 @@ __global__ void __launch_bounds__(kRouteThreads)
             zl[j] = ee < E ? zs[t][ee] : -INFINITY;
             taken[j] = ee >= E;
         }
-        double zsel[kMaxTopK];
-        int esel[kMaxTopK];
-        for (int r = 0; r < k; ++r) {
-            // best of this lane: largest z, ties to lower expert index
-            double bz = -INFINITY;
-            int be = 0x7fffffff;
-#pragma unroll
-            for (int j = 0; j < kRouteMaxE / 64; ++j) {
-                int ee = lane + 64 * j;
-                if (!taken[j] && (zl[j] > bz || (zl[j] == bz && ee < be))) {
-                    bz = zl[j];
-                    be = ee;
-                }
-            }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                double oz = __shfl_xor(bz, off, 64);
-                int oe = __shfl_xor(be, off, 64);
-                if (oz > bz || (oz == bz && oe < be)) {
-                    bz = oz;
-                    be = oe;
-                }
-            }
-            zsel[r] = bz;
-            esel[r] = be;
-#pragma unroll
-            for (int j = 0; j < kRouteMaxE / 64; ++j)
-                if (lane + 64 * j == be) taken[j] = true;
-        }
-        if (lane == 0) {
-            double s = 0.0;
-            double ex[kMaxTopK];
-            for (int r = 0; r < k; ++r) {
-                ex[r] = exp(zsel[r] - zsel[0]);
-                s += ex[r];
-            }
-            for (int r = 0; r < k; ++r) {
-                ids[(int64_t)(t0 + t) * k + r] = esel[r];
-                w[(int64_t)(t0 + t) * k + r] = (float)(ex[r] / s);
-            }
-        }
+        topk_softmax_wave(zl, taken, lane, k, ids + (int64_t)(t0 + t) * k, w + (int64_t)(t0 + t) * k);
     }
 }
 
@@ -233,92 +240,7 @@ __global__ void __launch_bounds__(64) route_select_kernel(int T, int E, int k, i
         zl[j] = z;
         taken[j] = ee >= E;
     }
-    double zsel[kMaxTopK];
-    int esel[kMaxTopK];
-    for (int r = 0; r < k; ++r) {
-        double bz = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < kRouteMaxE / 64; ++j) {
-            const int ee = lane + 64 * j;
-            if (!taken[j] && (zl[j] > bz || (zl[j] == bz && ee < be))) {
-                bz = zl[j];
-                be = ee;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const double oz = __shfl_xor(bz, off, 64);
-            const int oe = __shfl_xor(be, off, 64);
-            if (oz > bz || (oz == bz && oe < be)) {
-                bz = oz;
-                be = oe;
-            }
-        }
-        zsel[r] = bz;
-        esel[r] = be;
-#pragma unroll
-        for (int j = 0; j < kRouteMaxE / 64; ++j)
-            if (lane + 64 * j == be) taken[j] = true;
-    }
-    if (lane == 0) {
-        double s = 0.0, ex[kMaxTopK];
-        for (int r = 0; r < k; ++r) {
-            ex[r] = exp(zsel[r] - zsel[0]);
-            s += ex[r];
-        }
-        for (int r = 0; r < k; ++r) {
-            ids[(int64_t)t * k + r] = esel[r];
-            w[(int64_t)t * k + r] = (float)(ex[r] / s);
-        }
-    }
-}
-
-
-// One wave selects the k largest of the logits zl (lane l holds experts
-// l + 64 j; taken marks slots to skip), ties to the lower expert, and writes
-// the ids and the softmax of the chosen logits (fp64, stored fp32).
-__device__ void topk_softmax_wave(double (&zl)[kRouteMaxE / 64], bool (&taken)[kRouteMaxE / 64], int lane, int k,
-                                  int32_t* __restrict__ ids, float* __restrict__ w) {
-    double zsel[kMaxTopK];
-    int esel[kMaxTopK];
-    for (int r = 0; r < k; ++r) {
-        double bz = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < kRouteMaxE / 64; ++j) {
-            const int ee = lane + 64 * j;
-            if (!taken[j] && (zl[j] > bz || (zl[j] == bz && ee < be))) {
-                bz = zl[j];
-                be = ee;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const double oz = __shfl_xor(bz, off, 64);
-            const int oe = __shfl_xor(be, off, 64);
-            if (oz > bz || (oz == bz && oe < be)) {
-                bz = oz;
-                be = oe;
-            }
-        }
-        zsel[r] = bz;
-        esel[r] = be;
-#pragma unroll
-        for (int j = 0; j < kRouteMaxE / 64; ++j)
-            if (lane + 64 * j == be) taken[j] = true;
-    }
-    if (lane == 0) {
-        double s = 0.0, ex[kMaxTopK];
-        for (int r = 0; r < k; ++r) {
-            ex[r] = exp(zsel[r] - zsel[0]);
-            s += ex[r];
-        }
-        for (int r = 0; r < k; ++r) {
-            ids[r] = esel[r];
-            w[r] = (float)(ex[r] / s);
-        }
-    }
+    topk_softmax_wave(zl, taken, lane, k, ids + (int64_t)t * k, w + (int64_t)t * k);
 }
 
 // Many tokens, E in {64, 128, 256}: the logits are a [T x d] x [d x E] product
