@@ -181,6 +181,35 @@ def decode_bench(args):
         f"({gu_gbs / HBM_PEAK_GBS:.1%}), pair {both_gbs:.0f} GB/s, miss rate {res['cache']['miss_rate']:.2f}, "
         f"fill {res['branches']['fill_gbs']:.1f} GB/s, host {res['branches']['host_gbs']:.1f} GB/s "
         f"({delta['host_seconds']:.2f}s busy of {el2:.2f}s in the kernel-timed run)")
+    # (3) hits only: the last step replayed on the warm cache with fills off
+    # (max_fetch 0), so every GPU-executed expert is a resident record and each
+    # is read again only after the other 47 layers (~2.7 GB of reads), far more
+    # than the 256 MB Infinity Cache; a record that a fill has just written is
+    # never among them.  Same experts per launch as the run above.
+    M.ft_cache_set_timing(h, False)
+    M.ft_cache_set_profile(h, M.profile(cfg.bp_mbps, cfg.bh_mbps, 0))
+    step(h, sc.shape, steps - 1)
+    torch.cuda.synchronize()
+    q0 = M.ft_cache_stats(h).as_dict()
+    M.ft_cache_set_timing(h, True)
+    for _ in range(args.hits_only_reps):
+        step(h, sc.shape, steps - 1)
+    torch.cuda.synchronize()
+    th = M.ft_cache_timing(h)
+    q1 = M.ft_cache_stats(h).as_dict()
+    assert q1["error_flags"] == 0 and q1["fills"] == q0["fills"], q1
+    hx = th.gemv_experts
+    res["decode_kernels"]["hits_only"] = {
+        "gateup_gbs": hx * gu_bytes / (th.ms[M.FT_K_GEMV_GU] / 1e3) / 1e9,
+        "gateup_frac": hx * gu_bytes / (th.ms[M.FT_K_GEMV_GU] / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "down_gbs": hx * dn_bytes / (th.ms[M.FT_K_GEMV_DOWN] / 1e3) / 1e9,
+        "avg_gateup_launch_us": th.ms[M.FT_K_GEMV_GU] / max(th.launches[M.FT_K_GEMV_GU], 1) * 1e3,
+        "gpu_experts_per_layer_step": hx / max(th.launches[M.FT_K_GEMV_GU], 1),
+        "launches": th.launches[M.FT_K_GEMV_GU], "fills": q1["fills"] - q0["fills"],
+        "workload": f"decode step {steps - 1} replayed {args.hits_only_reps} times on the warm cache, max_fetch 0",
+    }
+    log(f"decode hits only: gate/up GEMV {res['decode_kernels']['hits_only']['gateup_gbs']:.0f} GB/s, "
+        f"{res['decode_kernels']['hits_only']['gpu_experts_per_layer_step']:.2f} experts per launch")
     if not args.no_measured_profile:
         # the same decode run again from a cold cache, with q* fed by this machine's measured B_P / B_H
         M.ft_cache_set_timing(h, False)
@@ -621,6 +650,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the decode run replayed from a HIP graph")
     ap.add_argument("--no-latency", action="store_true", help="skip the per-call latency run of the decode path")
+    ap.add_argument("--hits-only-reps", type=int, default=32,
+                    help="replays of the last decode step with fills off (hit-only GEMV bandwidth)")
     ap.add_argument("--no-measured-profile", action="store_true",
                     help="skip the second decode run with the measured B_P / B_H")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (kernel work)")
