@@ -221,7 +221,7 @@ ft_status ft_moe_route(const ft_shape* shape, const uint16_t* x, const uint16_t*
  * clock+hits+i, clock += hits+q; victims are the q smallest (stamp, slot)
  * among slots not hit by this call (empty slots have stamp 0); the i-th fill
  * takes the i-th victim; host-run misses leave residency and recency unchanged.
- * Errors: FT_ERR_ARG (layer, T > max_tokens, null ids), FT_ERR_HIP.
+ * Errors: FT_ERR_ARG (layer, T outside 1..max_tokens, null ids), FT_ERR_HIP.
  * ------------------------------------------------------------------------- */
 ft_status ft_cache_classify(ft_cache* cache, int32_t layer, int32_t* ids, int32_t T,
                             const ft_classify_out* out, void* stream);
@@ -275,8 +275,9 @@ ft_status ft_cache_classify(ft_cache* cache, int32_t layer, int32_t* ids, int32_
  *   ft_cache_destroy).  A graph must not be replayed after ft_cache_destroy.
  *   Kernel timing must be off (FT_ERR_STATE); STREAMED calls cannot be
  *   captured (FT_ERR_UNSUPPORTED).
- * Errors: FT_ERR_ARG (also flags with CACHED mode), FT_ERR_STATE,
- *   FT_ERR_UNSUPPORTED, FT_ERR_HIP.
+ * Errors: FT_ERR_ARG (layer, T outside 1..max_tokens, null pointers, flags
+ *   with CACHED mode), FT_ERR_STATE, FT_ERR_UNSUPPORTED, FT_ERR_HIP.  A
+ *   refused call enqueues nothing and changes no state.
  * ------------------------------------------------------------------------- */
 ft_status ft_moe_forward(ft_cache* cache, int32_t layer, int32_t mode, const uint16_t* x,
                          const int32_t* routes, const float* w, int32_t T, uint16_t* y, void* stream);

@@ -203,6 +203,48 @@ def test_out_of_range_ids_flagged():
 
 
 @gpu
+def test_empty_calls():
+    """T = 0: routing enqueues nothing and writes nothing; classify and forward
+    refuse it with FT_ERR_ARG and leave the cache as it was, so the next call
+    behaves as if the refused ones had not been made."""
+    cuda()
+    cfg = synth.CONFIGS["tiny"]
+    bank = make_bank(cfg)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, 4, cfg.bp_mbps, cfg.bh_mbps)
+    try:
+        st = torch.cuda.current_stream().cuda_stream
+        x = torch.zeros((1, cfg.d), dtype=torch.int16, device="cuda")
+        wr = torch.zeros((cfg.d, cfg.E), dtype=torch.int16, device="cuda")
+        ids = torch.full((1, cfg.k), -7, dtype=torch.int32, device="cuda")
+        w = torch.full((1, cfg.k), -7.0, dtype=torch.float32, device="cuda")
+        M.ft_moe_route(sc.shape, x.data_ptr(), wr.data_ptr(), 0, ids.data_ptr(), w.data_ptr(), st)
+        torch.cuda.synchronize()
+        assert (ids.cpu() == -7).all() and (w.cpu() == -7.0).all()
+        before = M.ft_cache_stats(sc.handle).as_dict()
+        with pytest.raises(M.FtError) as ei:
+            M.ft_cache_classify(sc.handle, 0, ids.data_ptr(), 0, None, st)
+        assert ei.value.status == M.FT_ERR_ARG
+        with pytest.raises(M.FtError) as ei:
+            M.ft_moe_forward(sc.handle, 0, M.FT_MODE_CACHED, x.data_ptr(), ids.data_ptr(), w.data_ptr(), 0,
+                             x.data_ptr(), st)
+        assert ei.value.status == M.FT_ERR_ARG
+        torch.cuda.synchronize()
+        assert M.ft_cache_stats(sc.handle).as_dict() == before
+        # the next call is the first one the cache sees: every expert misses
+        ids = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
+        buf = ClassifyBuffers(8)
+        M.ft_cache_classify(sc.handle, 0, ids.data_ptr(), 1, buf.struct, st)
+        got = buf.host()
+        r = OC.SlotCacheSim(1, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps).classify(0, np.array([[0, 1]], np.int32))
+        assert got["uniq"] == list(r.uniq) and got["cls"] == list(r.cls) and got["q"] == r.q and got["hits"] == 0
+        assert got["slot"] == list(r.slot)
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
 def test_streamed_needs_two_buffers():
     cuda()
     cfg = synth.CONFIGS["tiny"]
