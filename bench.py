@@ -198,6 +198,8 @@ def decode_bench(args):
     th = M.ft_cache_timing(h)
     q1 = M.ft_cache_stats(h).as_dict()
     assert q1["error_flags"] == 0 and q1["fills"] == q0["fills"], q1
+    # back to the configured profile (ft_cache_profile keeps the cache's max_fetch)
+    M.ft_cache_set_profile(h, M.profile(cfg.bp_mbps, cfg.bh_mbps, cfg.max_fetch))
     hx = th.gemv_experts
     res["decode_kernels"]["hits_only"] = {
         "gateup_gbs": hx * gu_bytes / (th.ms[M.FT_K_GEMV_GU] / 1e3) / 1e9,
@@ -214,6 +216,7 @@ def decode_bench(args):
         # the same decode run again from a cold cache, with q* fed by this machine's measured B_P / B_H
         M.ft_cache_set_timing(h, False)
         prof = M.ft_cache_profile(h, 16)          # leaves the cache empty (cold)
+        assert prof.max_fetch == cfg.max_fetch, prof.max_fetch
         try:
             from moe_expert_execution_amd import bwprofile
             bwprofile.save("bf16", bwprofile.gpu_key(), prof.bp_mbps, prof.bh_mbps,
