@@ -336,18 +336,31 @@ def cpu_baseline(bank, cfg, sample_steps):
     xs = [synth.ar1_tokens(cfg, l, sample_steps) for l in range(L)]
     wrs = [synth.router(cfg, l) for l in range(L)]
     sim = OC.SlotCacheSim(L, E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
-    t0 = time.perf_counter()
+    part = {"route": 0.0, "simulator": 0.0, "layer": 0.0}
+    clk = time.perf_counter
+    t0 = clk()
     for s in range(sample_steps):
         for l in range(L):
             x = xs[l][s:s + 1]
+            ta = clk()
             ids, w, _ = OR.route(x, wrs[l], k)
+            tb = clk()
             sim.classify(l, ids)
+            tc = clk()
             OM.moe_layer(x, ids, w, lambda e: OF.decode_record(recs[l * E + e], cfg.fmt, cfg.d, cfg.f))
-    el = time.perf_counter() - t0
-    blas = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+            td = clk()
+            part["route"] += tb - ta
+            part["simulator"] += tc - tb
+            part["layer"] += td - tc
+    el = clk() - t0
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
     cores = len(os.sched_getaffinity(0))
-    return {"value": sample_steps / el, "unit": "tokens/s", "cores": cores, "blas_threads": blas[0] if blas else 1,
+    calls = sample_steps * L
+    return {"value": sample_steps / el, "unit": "tokens/s", "cores": cores,
+            "blas_threads": blas[0].get("num_threads") if blas else 1,
+            "blas_library": blas[0].get("internal_api") if blas else None,
             "kind": "oracle", "seconds": el,
+            "us_per_layer_call": {key: v / calls * 1e6 for key, v in part.items()},
             "sample": f"decode steps 0..{sample_steps - 1} x {L} layers (route + LRU simulator + fp64 layer)"}
 
 
