@@ -15,8 +15,10 @@
  *  - All functions return ft_status.  On error nothing has been enqueued and
  *    ft_last_error() (thread-local) describes the problem.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
- *    GPU step is enqueued on it; only create, resize, stats, snapshot,
- *    read_slot and destroy synchronise with the device.
+ *    GPU step of a call is enqueued on it, except the full-layer loads of
+ *    STREAMED mode (the library's transfer stream, ordered by events); only
+ *    create, resize, profile, set_profile, stats, timing, snapshot, read_slot
+ *    and destroy synchronise with the device.
  *  - Device pointers must be allocated on the device that created the cache.
  *  - A handle is used from one host thread at a time.
  *  - bf16 values are passed as uint16_t bit patterns.
@@ -122,11 +124,13 @@ typedef struct {
     uint64_t bytes_filled;   /* record bytes copied host -> slot by fills        */
     uint64_t layers_streamed;/* full-layer loads into the two buffers            */
     uint64_t clock;          /* LRU clock (starts at 1)                          */
-    int32_t error_flags;     /* sticky device flags: 1 = expert id out of range,
-                                2 = LRU clock past 2^40, 4 = repeated expert in a
-                                token's routes (the repeat is dropped), 8 = a
-                                call gave up waiting for the host experts
-                                (seconds; its output is invalid) */
+    int32_t error_flags;     /* sticky device flags: 1 = expert id or route out of
+                                range (ignored), 2 = LRU clock past 2^40, 4 =
+                                repeated expert in a token's routes (the repeat
+                                is dropped), 8 = a call gave up waiting for the
+                                host experts (seconds; its output is invalid),
+                                16 = a graph captured before ft_cache_resize
+                                was replayed (it did nothing; output zero) */
     int32_t num_slots;
     uint64_t host_experts;   /* expert FFNs run by the host workers               */
     uint64_t host_bytes;     /* expert-record bytes the host workers read         */
@@ -174,6 +178,22 @@ typedef struct {
 ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, const void* host_bank,
                           int64_t num_slots, int32_t max_tokens, ft_cache** out);
 
+/* ---------------------------------------------------------------------------
+ * ft_cache_create_layers — ft_cache_create over one bank per layer.
+ * layer_banks[l] (l < layers): PINNED host memory holding layer l's `experts`
+ *   records back to back (record e at offset e * ft_record_bytes()); the
+ *   table itself is copied, the banks are caller-owned and must stay valid
+ *   and unchanged until ft_cache_destroy.  Entries may point to the same
+ *   memory (layers that share weights); flat ids, and so residency and LRU
+ *   decisions, stay per layer.  ft_cache_create(host_bank) is this call with
+ *   layer_banks[l] = host_bank + l * experts * ft_record_bytes().
+ * Everything else, errors included, is as ft_cache_create (FT_ERR_ARG names
+ * a layer whose bank is null, not pinned, or whose allocation is known to
+ * end before its E records).
+ * ------------------------------------------------------------------------- */
+ft_status ft_cache_create_layers(const ft_shape* shape, const ft_profile* profile, const void* const* layer_banks,
+                                 int64_t num_slots, int32_t max_tokens, ft_cache** out);
+
 /* Release every resource of the cache (synchronises).  NULL is accepted. */
 ft_status ft_cache_destroy(ft_cache* cache);
 
@@ -214,9 +234,13 @@ ft_status ft_moe_route(const ft_shape* shape, const uint16_t* x, const uint16_t*
  *              becomes INT32_MIN, which ft_moe_forward ignores.
  * out          caller-owned device arrays (see ft_classify_out); may be NULL
  *              when the caller does not need them.
- * Enqueues the control kernel on `stream` and the fills (device-initiated
- * copies of whole records from the pinned host bank into the victim slots) on
- * the library's transfer stream; never synchronises with the host.
+ * Enqueues the control kernel on `stream`; never synchronises with the host.
+ * The fills it chooses (device-initiated copies of whole records from the
+ * pinned host bank into the victim slots) are enqueued by the next call on the
+ * cache, on that call's stream: normally the CACHED ft_moe_forward of the same
+ * layer, which first stages the host branch's inputs so that the PCIe pull
+ * and the host experts run at the same time; any other call (or a sync point)
+ * enqueues them first on the classify's stream.
  * Policy: unique ids ascend by flat id; hits are stamped clock+r, fills
  * clock+hits+i, clock += hits+q; victims are the q smallest (stamp, slot)
  * among slots not hit by this call (empty slots have stamp 0); the i-th fill
@@ -235,10 +259,14 @@ ft_status ft_cache_classify(ft_cache* cache, int32_t layer, int32_t* ids, int32_
  * and host partial sums: METAL MEDIA summary, Figure 2 caption).
  * mode FT_MODE_CACHED: routes are the in-place output of the preceding
  *   ft_cache_classify for this layer.  Slot routes run on the GPU from the
- *   slot pool (after that call's fills complete); -(1+e) routes run on the
- *   library's host workers from the host bank (never from a slot, residency
- *   unchanged: same page, paragraph on the host source as fallback); the
- *   partial sums merge before the bf16 rounding.
+ *   slot pool, after that call's fills, which this call enqueues on `stream`
+ *   once the host branch's inputs are staged; -(1+e) routes (0 <= e < E) run
+ *   on the library's host workers from the host bank (never from a slot,
+ *   residency unchanged: same page, paragraph on the host source as
+ *   fallback); the partial sums merge before the bf16 rounding.  INT32_MIN
+ *   routes are skipped; any other value raises error flag 1 and is skipped.
+ *   A call of more than 1,024 routes (T * top_k) needs num_slots <= 8,192
+ *   (the key space of the many-route planner): FT_ERR_UNSUPPORTED otherwise.
  * mode FT_MODE_STREAMED (needs num_slots >= 2E, else FT_ERR_STATE): routes are
  *   raw expert ids 0..E-1; the layer is computed from full-layer buffer
  *   layer % 2 (slots [b*E, (b+1)*E)), loading it first on the transfer stream
@@ -272,9 +300,13 @@ ft_status ft_cache_classify(ft_cache* cache, int32_t layer, int32_t* ids, int32_
  *   few seconds it sets error flag 8 and lets the stream go on.  With stream
  *   host functions (FTMOE_HOST_SIGNAL=callback) the host experts become a
  *   captured host function instead (its context lives until
- *   ft_cache_destroy).  A graph must not be replayed after ft_cache_destroy.
- *   Kernel timing must be off (FT_ERR_STATE); STREAMED calls cannot be
- *   captured (FT_ERR_UNSUPPORTED).
+ *   ft_cache_destroy).  A replay reads the cache's current profile (set by
+ *   ft_cache_set_profile or ft_cache_profile after the capture).  A graph
+ *   captured before ft_cache_resize must be captured again: replayed, each of
+ *   its calls does nothing except set its routes to INT32_MIN and its output
+ *   y to zero, and raises error flag 16.  A graph must not be replayed after
+ *   ft_cache_destroy.  Kernel timing must be off (FT_ERR_STATE); STREAMED
+ *   calls cannot be captured (FT_ERR_UNSUPPORTED).
  * Errors: FT_ERR_ARG (layer, T outside 1..max_tokens, null pointers, flags
  *   with CACHED mode), FT_ERR_STATE, FT_ERR_UNSUPPORTED, FT_ERR_HIP.  A
  *   refused call enqueues nothing and changes no state.
@@ -289,8 +321,11 @@ ft_status ft_moe_forward(ft_cache* cache, int32_t layer, int32_t mode, const uin
  * The caller guarantees no work is pending on this cache.  Keeps the
  * min(new_num_slots, residents) entries with the largest stamps, packed into
  * slots 0.. in ascending old-slot order, stamps and clock unchanged; every
- * other new slot is empty.  Synchronises.  Errors: FT_ERR_ARG, FT_ERR_NOMEM
- * (the old cache is then unchanged), FT_ERR_HIP.
+ * other new slot is empty.  Graphs captured before the resize are void (see
+ * ft_moe_forward).  Synchronises.  Errors: FT_ERR_ARG; FT_ERR_NOMEM and
+ * FT_ERR_HIP while the new pool is built (the cache is then unchanged);
+ * FT_ERR_HIP from the final map writes (the device failed part-way: destroy
+ * the cache).
  * ------------------------------------------------------------------------- */
 ft_status ft_cache_resize(ft_cache* cache, int64_t new_num_slots);
 
@@ -316,16 +351,18 @@ ft_status ft_cache_resize(ft_cache* cache, int64_t new_num_slots);
 ft_status ft_cache_profile(ft_cache* cache, int32_t records, ft_profile* out);
 
 /* Replace the cache's B_P / B_H / max_fetch (for example with a measured
- * profile).  Later classify calls compute q* from it; calls already enqueued
- * keep the profile they were launched with.  Errors: FT_ERR_ARG. */
+ * profile).  Later classify calls, and replays of graphs captured earlier,
+ * compute q* from it; calls already enqueued keep the profile they were
+ * enqueued under (this call synchronises first).  Errors: FT_ERR_ARG,
+ * FT_ERR_HIP. */
 ft_status ft_cache_set_profile(ft_cache* cache, const ft_profile* profile);
 
 /* Counters and sticky error flags (synchronises). */
 ft_status ft_cache_stats(const ft_cache* cache, ft_stats* out);
 
 /* Expert-kernel timing (measurement support).  When enabled, every
- * ft_moe_forward brackets its expert kernels with HIP events on the caller's
- * stream and every ft_cache_classify its fill kernel on the transfer stream;
+ * ft_moe_forward brackets its expert kernels, and every fill launch its
+ * kernel, with HIP events on the stream the kernel runs on;
  * ft_cache_timing synchronises and returns, per kernel class (0 GEMV gate/up,
  * 1 GEMV down, 2 GEMM gate/up, 3 GEMM down, 4 fill), the number of launches
  * and their summed event durations, plus device-side counts of the work those

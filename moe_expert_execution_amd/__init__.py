@@ -67,6 +67,8 @@ _lib = None
 # name -> (restype, argtypes)
 _SIGS = {
     "ft_cache_create": (i32, [ctypes.POINTER(FtShape), ctypes.POINTER(FtProfile), vp, i64, i32, ctypes.POINTER(vp)]),
+    "ft_cache_create_layers": (i32, [ctypes.POINTER(FtShape), ctypes.POINTER(FtProfile), ctypes.POINTER(vp), i64, i32,
+                                     ctypes.POINTER(vp)]),
     "ft_cache_destroy": (i32, [vp]),
     "ft_record_bytes": (i64, [ctypes.POINTER(FtShape)]),
     "ft_moe_route": (i32, [ctypes.POINTER(FtShape), vp, vp, i32, vp, vp, vp]),
@@ -141,6 +143,15 @@ def ft_cache_create(shp: FtShape, prof: FtProfile, host_bank: int, num_slots: in
     h = vp()
     _check(lib().ft_cache_create(ctypes.byref(shp), ctypes.byref(prof), host_bank, num_slots, max_tokens,
                                  ctypes.byref(h)))
+    return h.value
+
+
+def ft_cache_create_layers(shp: FtShape, prof: FtProfile, layer_banks, num_slots: int, max_tokens: int) -> int:
+    """`layer_banks`: one pinned host address per layer (entries may repeat)."""
+    table = (vp * len(layer_banks))(*layer_banks)
+    h = vp()
+    _check(lib().ft_cache_create_layers(ctypes.byref(shp), ctypes.byref(prof), table, num_slots, max_tokens,
+                                        ctypes.byref(h)))
     return h.value
 
 

@@ -158,9 +158,10 @@ void free_cache(ft_cache* c) {
     if (c->host) host_branch_destroy(c->host);
     if (c->timing) timing_destroy(c->timing);
     void* bufs[] = {c->pool, c->slot_for_id, c->id_of_slot, c->stamp, c->clock, c->counters, c->errflag, c->gseq_dev,
+                    c->dstate,
                     c->wl_counts, c->wl_slot, c->wl_src, c->plan.meta, c->plan.active_slot, c->plan.seg,
                     c->plan.perm, c->plan.route_pos, c->plan.tile_active, c->plan.tile_row0, c->plan.tile_first,
-                    c->plan.chunk_counts, c->H, c->Y, c->gv_part};
+                    c->plan.chunk_counts, c->H, c->Y, c->gv_part, c->bank_dev};
     for (void* b : bufs)
         if (b) (void)hipFree(b);
     hipEvent_t evs[] = {c->ev_ctrl, c->ev_fwd, c->ev_host, c->ev_xlast, c->ev_fence,
@@ -169,22 +170,29 @@ void free_cache(ft_cache* c) {
         if (e) (void)hipEventDestroy(e);
     if (c->xfer) (void)hipStreamDestroy(c->xfer);
     if (c->hstream) (void)hipStreamDestroy(c->hstream);
+    delete[] c->bank_host;
     delete c;
 }
 
-// Buffers whose size depends on the slot count.
+// The planner's tile lists and chunk counts, sized for any slot count (a call
+// has at most one active slot per route), so that resize never reallocates
+// buffers a captured call may hold.
 hipError_t alloc_plan(ft_cache* c) {
     const int64_t cap = c->cap;
-    const int64_t act = std::min<int64_t>(cap, std::max<int64_t>(c->N, c->sh.experts));
-    c->plan.max_tiles = (cap + gemm_tile_m() - 1) / gemm_tile_m() + act + 1;
-    const int64_t keyspace = std::max<int64_t>(c->N, c->sh.experts);
+    c->plan.max_tiles = (cap + gemm_tile_m() - 1) / gemm_tile_m() + cap + 1;
     const int64_t chunks = (c->max_tokens + kChunkTokens - 1) / kChunkTokens;
     hipError_t e;
     if ((e = dalloc(&c->plan.tile_active, c->plan.max_tiles))) return e;
     if ((e = dalloc(&c->plan.tile_row0, c->plan.max_tiles))) return e;
     if ((e = dalloc(&c->plan.tile_first, cap + 1))) return e;
-    if ((e = dalloc(&c->plan.chunk_counts, chunks * std::min<int64_t>(keyspace, 8192)))) return e;
+    if ((e = dalloc(&c->plan.chunk_counts, chunks * kLargeKeySpace))) return e;
     return hipSuccess;
+}
+
+// Write the profile and pool generation the kernels read at run time.
+hipError_t write_dstate(ft_cache* c) {
+    DevState ds{c->gen, c->prof.bp_mbps, c->prof.bh_mbps, c->prof.max_fetch};
+    return hipMemcpy(c->dstate, &ds, sizeof(ds), hipMemcpyHostToDevice);
 }
 
 // Enqueue the fills chosen by the last classify (if not yet enqueued) on `st`.
@@ -218,10 +226,10 @@ ft_status enqueue_load(ft_cache* c, int layer, int buf, hipStream_t st) {
     FT_HIP(launch_invalidate(c, buf, c->xfer));
     const int64_t E = c->sh.experts, S = c->rl.S, P = c->rl.P;
     if (P == S) {
-        FT_HIP(hipMemcpyAsync(c->pool + (int64_t)buf * E * P, c->bank_host + (int64_t)layer * E * S, E * S,
+        FT_HIP(hipMemcpyAsync(c->pool + (int64_t)buf * E * P, c->bank_host[layer], E * S,
                               hipMemcpyHostToDevice, c->xfer));
     } else {   // records of S bytes into slots P bytes apart
-        FT_HIP(hipMemcpy2DAsync(c->pool + (int64_t)buf * E * P, (size_t)P, c->bank_host + (int64_t)layer * E * S,
+        FT_HIP(hipMemcpy2DAsync(c->pool + (int64_t)buf * E * P, (size_t)P, c->bank_host[layer],
                                 (size_t)S, (size_t)S, (size_t)E, hipMemcpyHostToDevice, c->xfer));
     }
     FT_HIP(hipEventRecord(c->ready[buf], c->xfer));
@@ -264,8 +272,8 @@ ft_status ft_host_free(void* ptr) {
     return FT_OK;
 }
 
-ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, const void* host_bank,
-                          int64_t num_slots, int32_t max_tokens, ft_cache** out) {
+ft_status ft_cache_create_layers(const ft_shape* shape, const ft_profile* profile, const void* const* layer_banks,
+                                 int64_t num_slots, int32_t max_tokens, ft_cache** out) {
     clear_error();
     FT_REQUIRE(out, "out is null");
     *out = nullptr;
@@ -273,7 +281,8 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     if (st != FT_OK) return st;
     FT_REQUIRE(profile && profile->bp_mbps > 0 && profile->bh_mbps > 0, "profile bandwidths must be > 0");
     FT_REQUIRE(profile->max_fetch >= -1, "max_fetch must be >= -1");
-    FT_REQUIRE(host_bank, "host bank is null");
+    FT_REQUIRE(layer_banks, "layer bank table is null");
+    for (int32_t l = 0; l < shape->layers; ++l) FT_REQUIRE(layer_banks[l], "bank of layer %d is null", l);
     FT_REQUIRE(num_slots >= 1 && num_slots <= kMaxSlots, "num_slots must be in 1..%d", kMaxSlots);
     FT_REQUIRE(max_tokens >= 1 && max_tokens <= 65535, "max_tokens must be in 1..65535");
     FT_REQUIRE((int64_t)max_tokens * shape->top_k <= (1 << 24), "max_tokens * top_k too large");
@@ -290,7 +299,6 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     c->max_tokens = max_tokens;
     c->cap = max_tokens * shape->top_k;
     c->buf_layer[0] = c->buf_layer[1] = -1;
-    c->bank_host = static_cast<const uint8_t*>(host_bank);
 #define CK(call)                                                                             \
     do {                                                                                     \
         hipError_t e_ = (call);                                                              \
@@ -301,40 +309,50 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
         }                                                                                    \
     } while (0)
     CK(hipGetDevice(&c->device));
-    void* dptr = nullptr;
-    if (hipHostGetDevicePointer(&dptr, const_cast<void*>(host_bank), 0) != hipSuccess || !dptr) {
-        (void)hipGetLastError();
+    const int64_t L = shape->layers, E = shape->experts, S = c->rl.S, d = shape->d_model, f = shape->d_ff;
+    c->bank_host = new (std::nothrow) const uint8_t*[L];
+    if (!c->bank_host) {
         free_cache(c);
-        set_error("host bank must be pinned host memory (ft_host_alloc / hipHostMalloc)");
-        return FT_ERR_ARG;
+        return FT_ERR_NOMEM;
     }
-    c->bank_dev = static_cast<const uint8_t*>(dptr);
-    {
+    std::vector<const uint8_t*> dev_banks(L);
+    for (int64_t l = 0; l < L; ++l) {
+        void* hp = const_cast<void*>(layer_banks[l]);
+        void* dptr = nullptr;
+        if (hipHostGetDevicePointer(&dptr, hp, 0) != hipSuccess || !dptr) {
+            (void)hipGetLastError();
+            free_cache(c);
+            set_error("bank of layer %lld must be pinned host memory (ft_host_alloc / hipHostMalloc)", (long long)l);
+            return FT_ERR_ARG;
+        }
         // Where the runtime knows the bank's allocation (hipHostMalloc memory),
-        // it must reach layers * experts records past host_bank: fills and
-        // layer loads read the bank from the device, where a short bank faults.
-        const int64_t need = (int64_t)shape->layers * shape->experts * c->rl.S;
+        // it must hold the layer's E records: fills and layer loads read the
+        // bank from the device, where a short bank faults.
         hipDeviceptr_t base = nullptr;
         size_t size = 0;
-        if (hipMemGetAddressRange(&base, &size, const_cast<void*>(host_bank)) == hipSuccess && base && size) {
+        if (hipMemGetAddressRange(&base, &size, hp) == hipSuccess && base && size) {
             const int64_t avail =
-                (int64_t)(static_cast<const uint8_t*>(base) + size - static_cast<const uint8_t*>(host_bank));
-            if (avail < need) {
+                (int64_t)(static_cast<const uint8_t*>(base) + size - static_cast<const uint8_t*>(hp));
+            if (avail < E * S) {
                 free_cache(c);
-                set_error("host bank allocation holds %lld bytes from host_bank; layers * experts records need %lld",
-                          (long long)avail, (long long)need);
+                set_error("bank of layer %lld: its allocation holds %lld bytes from the pointer; %lld records need "
+                          "%lld", (long long)l, (long long)avail, (long long)E, (long long)(E * S));
                 return FT_ERR_ARG;
             }
         } else {
             (void)hipGetLastError();   // an untracked pointer: no check, and no stale error left behind
         }
+        c->bank_host[l] = static_cast<const uint8_t*>(hp);
+        dev_banks[l] = static_cast<const uint8_t*>(dptr);
     }
-    const int64_t L = shape->layers, E = shape->experts, S = c->rl.S, d = shape->d_model, f = shape->d_ff;
+    CK(dalloc(&c->bank_dev, L));
+    CK(hipMemcpy(c->bank_dev, dev_banks.data(), sizeof(const uint8_t*) * L, hipMemcpyHostToDevice));
     const int64_t cap = c->cap;
     CK(hipMalloc(reinterpret_cast<void**>(&c->pool), (size_t)(c->N * c->rl.P)));
     CK(dalloc(&c->slot_for_id, L * E));
-    CK(dalloc(&c->id_of_slot, c->N));
-    CK(dalloc(&c->stamp, c->N));
+    CK(dalloc(&c->id_of_slot, kMaxSlots));
+    CK(dalloc(&c->stamp, kMaxSlots));
+    CK(dalloc(&c->dstate, 1));
     CK(dalloc(&c->clock, 1));
     CK(dalloc(&c->counters, C_N));
     CK(dalloc(&c->errflag, 1));
@@ -358,8 +376,9 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     c->host_wait_polls = 1u << 22;
     if (const char* e = getenv("FTMOE_HOST_WAIT_POLLS")) c->host_wait_polls = (uint32_t)strtoul(e, nullptr, 10);
     CK(hipMemset(c->slot_for_id, 0xFF, sizeof(int32_t) * L * E));
-    CK(hipMemset(c->id_of_slot, 0xFF, sizeof(int32_t) * c->N));
-    CK(hipMemset(c->stamp, 0, sizeof(uint64_t) * c->N));
+    CK(hipMemset(c->id_of_slot, 0xFF, sizeof(int32_t) * kMaxSlots));
+    CK(hipMemset(c->stamp, 0, sizeof(uint64_t) * kMaxSlots));
+    CK(write_dstate(c));
     const uint64_t one = 1;
     CK(hipMemcpy(c->clock, &one, sizeof(one), hipMemcpyHostToDevice));
     CK(hipMemset(c->counters, 0, sizeof(unsigned long long) * C_N));
@@ -381,6 +400,20 @@ ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, cons
     }
     *out = c;
     return FT_OK;
+}
+
+ft_status ft_cache_create(const ft_shape* shape, const ft_profile* profile, const void* host_bank,
+                          int64_t num_slots, int32_t max_tokens, ft_cache** out) {
+    clear_error();
+    FT_REQUIRE(out, "out is null");
+    *out = nullptr;
+    ft_status st = check_shape(shape);
+    if (st != FT_OK) return st;
+    FT_REQUIRE(host_bank, "host bank is null");
+    const int64_t stride = (int64_t)shape->experts * ft_record_bytes(shape);
+    std::vector<const void*> layers(shape->layers);
+    for (int32_t l = 0; l < shape->layers; ++l) layers[l] = static_cast<const uint8_t*>(host_bank) + l * stride;
+    return ft_cache_create_layers(shape, profile, layers.data(), num_slots, max_tokens, out);
 }
 
 ft_status ft_cache_destroy(ft_cache* cache) {
@@ -451,6 +484,11 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         return FT_ERR_STATE;
     }
     if (m == FT_MODE_CACHED) {
+        if ((int64_t)T * k > kSmallPlanRoutes && c->N > kLargeKeySpace) {
+            set_error("a CACHED call of more than %d routes needs num_slots <= %d (the chunked planner's key space)",
+                      kSmallPlanRoutes, kLargeKeySpace);
+            return FT_ERR_UNSUPPORTED;
+        }
         // host branch: the planner copies the call's routes, weights and
         // activations into pinned staging and, with the mailbox, posts the
         // call's sequence number; the host workers run the host experts and
@@ -504,10 +542,6 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         set_error("STREAMED mode needs num_slots >= %lld (%lld slots)", (long long)need, (long long)c->N);
         return FT_ERR_STATE;
     }
-    if (!gemv && (int64_t)T * k > kSmallPlanRoutes && E > 8192) {
-        set_error("too many experts for the chunked planner");
-        return FT_ERR_UNSUPPORTED;
-    }
     const int b = single ? 0 : layer % 2;
     if (c->buf_layer[b] != layer) {
         ft_status s = enqueue_load(c, layer, b, st);
@@ -537,34 +571,18 @@ ft_status ft_cache_resize(ft_cache* c, int64_t new_num_slots) {
     FT_REQUIRE(new_num_slots >= 1 && new_num_slots <= kMaxSlots, "num_slots must be in 1..%d", kMaxSlots);
     ft_status fs = flush_fill_sync(c);
     if (fs != FT_OK) return fs;
-    const int64_t L = c->sh.layers, E = c->sh.experts, S = c->rl.S, N = c->N, Nn = new_num_slots;
+    const int64_t L = c->sh.layers, E = c->sh.experts, N = c->N, Nn = new_num_slots;
     std::vector<int32_t> ios(N);
     std::vector<uint64_t> stamp(N);
     FT_HIP(hipMemcpy(ios.data(), c->id_of_slot, sizeof(int32_t) * N, hipMemcpyDeviceToHost));
     FT_HIP(hipMemcpy(stamp.data(), c->stamp, sizeof(uint64_t) * N, hipMemcpyDeviceToHost));
+    // the min(Nn, residents) most recent residents, in ascending old-slot order
     std::vector<int32_t> res;
     for (int64_t s = 0; s < N; ++s)
         if (ios[s] >= 0) res.push_back((int32_t)s);
     std::stable_sort(res.begin(), res.end(), [&](int32_t a, int32_t b) { return stamp[a] > stamp[b]; });
     if ((int64_t)res.size() > Nn) res.resize(Nn);
     std::sort(res.begin(), res.end());
-    // new arrays first: on failure the old cache is untouched
-    uint8_t* npool = nullptr;
-    int32_t *nios = nullptr, *src = nullptr, *ntile_a = nullptr, *ntile_r = nullptr, *ncc = nullptr;
-    uint64_t* nstamp = nullptr;
-    auto fail = [&](hipError_t e) {
-        (void)hipFree(npool);
-        (void)hipFree(nios);
-        (void)hipFree(src);
-        (void)hipFree(nstamp);
-        set_error("resize allocation failed: %s", hipGetErrorString(e));
-        return e == hipErrorOutOfMemory ? FT_ERR_NOMEM : FT_ERR_HIP;
-    };
-    hipError_t e;
-    if ((e = hipMalloc(reinterpret_cast<void**>(&npool), (size_t)(Nn * c->rl.P)))) return fail(e);
-    if ((e = dalloc(&nios, Nn))) return fail(e);
-    if ((e = dalloc(&nstamp, Nn))) return fail(e);
-    if ((e = dalloc(&src, std::max<size_t>(res.size(), 1)))) return fail(e);
     std::vector<int32_t> h_ios(Nn, -1), h_sfi(L * E, -1);
     std::vector<uint64_t> h_st(Nn, 0);
     for (size_t i = 0; i < res.size(); ++i) {
@@ -572,34 +590,48 @@ ft_status ft_cache_resize(ft_cache* c, int64_t new_num_slots) {
         h_st[i] = stamp[res[i]];
         h_sfi[ios[res[i]]] = (int32_t)i;
     }
+    // The new pool is built first; a failure up to the commit leaves the cache
+    // as it was.
+    uint8_t* npool = nullptr;
+    int32_t* src = nullptr;
+    auto fail = [&](hipError_t e, const char* what) {
+        (void)hipFree(npool);
+        (void)hipFree(src);
+        set_error("resize: %s failed: %s", what, hipGetErrorString(e));
+        return e == hipErrorOutOfMemory ? FT_ERR_NOMEM : FT_ERR_HIP;
+    };
+    hipError_t e;
+    if ((e = hipMalloc(reinterpret_cast<void**>(&npool), (size_t)(Nn * c->rl.P)))) return fail(e, "pool allocation");
+    if ((e = dalloc(&src, std::max<size_t>(res.size(), 1)))) return fail(e, "gather list allocation");
     if (!res.empty()) {
-        if ((e = hipMemcpy(src, res.data(), sizeof(int32_t) * res.size(), hipMemcpyHostToDevice))) return fail(e);
-        if ((e = launch_resize_gather(c->pool, npool, c->rl.P, src, (int)res.size(), 0))) return fail(e);
-        if ((e = hipDeviceSynchronize())) return fail(e);
+        if ((e = hipMemcpy(src, res.data(), sizeof(int32_t) * res.size(), hipMemcpyHostToDevice)))
+            return fail(e, "gather list copy");
+        if ((e = launch_resize_gather(c->pool, npool, c->rl.P, src, (int)res.size(), 0))) return fail(e, "gather");
+        if ((e = hipDeviceSynchronize())) return fail(e, "gather");
     }
-    FT_HIP(hipMemcpy(nios, h_ios.data(), sizeof(int32_t) * Nn, hipMemcpyHostToDevice));
-    FT_HIP(hipMemcpy(nstamp, h_st.data(), sizeof(uint64_t) * Nn, hipMemcpyHostToDevice));
-    FT_HIP(hipMemcpy(c->slot_for_id, h_sfi.data(), sizeof(int32_t) * L * E, hipMemcpyHostToDevice));
     (void)hipFree(src);
+    src = nullptr;
+    // Commit.  The maps are rewritten in place (they are sized for any slot
+    // count) and the pool generation advances, so that a call replayed from a
+    // graph captured before this resize does nothing (error flag 16).  A HIP
+    // failure from here on means the device failed part-way: the cache must
+    // then be destroyed.
+    if ((e = hipMemcpy(c->id_of_slot, h_ios.data(), sizeof(int32_t) * Nn, hipMemcpyHostToDevice)) ||
+        (e = hipMemcpy(c->stamp, h_st.data(), sizeof(uint64_t) * Nn, hipMemcpyHostToDevice)) ||
+        (e = hipMemcpy(c->slot_for_id, h_sfi.data(), sizeof(int32_t) * L * E, hipMemcpyHostToDevice))) {
+        (void)hipFree(npool);
+        set_error("resize: writing the maps failed: %s (destroy the cache)", hipGetErrorString(e));
+        return FT_ERR_HIP;
+    }
     (void)hipFree(c->pool);
-    (void)hipFree(c->id_of_slot);
-    (void)hipFree(c->stamp);
     c->pool = npool;
-    c->id_of_slot = nios;
-    c->stamp = nstamp;
     c->N = Nn;
-    (void)hipFree(c->plan.tile_active);
-    (void)hipFree(c->plan.tile_row0);
-    (void)hipFree(c->plan.chunk_counts);
-    c->plan.tile_active = c->plan.tile_row0 = c->plan.chunk_counts = nullptr;
-    (void)ntile_a;
-    (void)ntile_r;
-    (void)ncc;
-    FT_HIP(alloc_plan(c));
+    c->gen += 1;
     c->buf_layer[0] = c->buf_layer[1] = -1;
     c->release_recorded[0] = c->release_recorded[1] = false;
     c->xfer_pending = false;
     c->streaming = false;
+    FT_HIP(write_dstate(c));
     FT_HIP(hipDeviceSynchronize());
     return FT_OK;
 }
@@ -609,7 +641,11 @@ ft_status ft_cache_set_profile(ft_cache* c, const ft_profile* p) {
     FT_REQUIRE(c && p, "null pointer");
     FT_REQUIRE(p->bp_mbps > 0 && p->bh_mbps > 0, "bandwidths must be positive");
     FT_REQUIRE(p->max_fetch >= -1, "max_fetch must be -1 or >= 0");
+    // calls already enqueued run with the profile they were enqueued under
+    ft_status fs = flush_fill_sync(c);
+    if (fs != FT_OK) return fs;
     c->prof = *p;
+    FT_HIP(write_dstate(c));
     return FT_OK;
 }
 

@@ -1,7 +1,8 @@
 // Weighted top-k combine: y[t] = sum over the token's GPU routes, j ascending,
-// of w[t,j] * Y[row(t,j)] (bf16 expert outputs), plus the host branch's partial sum P[t] when the
-// token has routes executed on the host; accumulated in fp32 and rounded once
-// to bf16.  The GPU and host partial outputs merge into the layer output
+// of w[t,j] * Y[row(t,j)] (bf16 expert outputs), plus the host branch's partial
+// sum P[t] when the token has a host route -(1+e), 0 <= e < E (the routes the
+// host branch runs and whose P rows it writes); accumulated in fp32 and
+// rounded once to bf16.  The GPU and host partial outputs merge into the layer output
 // (METAL MEDIA summary, Figure 2 caption; hyper.ai summary, section 方法).
 #include "wfmt.h"
 
@@ -17,7 +18,7 @@ constexpr int kCombThreads = 256;
 // wave ends.
 __global__ void __launch_bounds__(kCombThreads)
     combine_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ route_pos,
-                   const float* __restrict__ w, const uint16_t* __restrict__ Y, const float* P, int T, int k, int d,
+                   const float* __restrict__ w, const uint16_t* __restrict__ Y, const float* P, int T, int k, int d, int E,
                    uint16_t* __restrict__ y, const uint64_t* done, const uint64_t* seq_dev, uint64_t seq,
                    uint32_t limit, int32_t* errflag) {
     if (done) {
@@ -50,7 +51,7 @@ __global__ void __launch_bounds__(kCombThreads)
             acc.w = fmaf(wj, bf16hi(v.y), acc.w);
         } else {
             const int rv = routes[r];
-            host |= (rv < 0 && rv != INT32_MIN);
+            host |= (rv < 0 && rv >= -E);
         }
     }
     if (P && host) {
@@ -85,7 +86,7 @@ hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, in
         seq = wait->seq;
     }
     hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, st, routes, c->plan.route_pos, w, c->Y, P, T,
-                       c->sh.top_k, d, y, done, seq_dev, seq, c->host_wait_polls, c->errflag);
+                       c->sh.top_k, d, c->sh.experts, y, done, seq_dev, seq, c->host_wait_polls, c->errflag);
     return hipGetLastError();
 }
 

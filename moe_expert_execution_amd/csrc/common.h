@@ -20,6 +20,7 @@ constexpr int kKeysPerThread = kMaxSlots / kCtrlThreads;   // victim keys held p
 constexpr uint64_t kStampLimit = 1ull << 40;               // stamps fit 40 bits; slot 24 bits
 constexpr int kChunkTokens = 64;       // tokens per stable-sort chunk (one 64-bit mask)
 constexpr int kSmallPlanRoutes = 1024; // routes handled by the one-workgroup planner
+constexpr int kLargeKeySpace = 8192;   // slots (or experts) addressable by the chunked planner
 constexpr int kGemvMaxTokens = 4;      // tokens per call served by the GEMV path
 
 // device counters (ft_stats order)
@@ -61,7 +62,7 @@ bool record_layout(const ft_shape& s, RecordLayout* out);
 
 // ---- the host branch ------------------------------------------------------------
 struct HostBranch;
-HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const uint8_t* bank_host,
+HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const uint8_t* const* bank_layers,
                                int32_t max_tokens);
 void host_branch_destroy(HostBranch* hb);
 // Pinned staging owned by the host branch (device-visible for async copies).
@@ -129,10 +130,25 @@ struct PlanBuffers {
     int32_t* tile_active;   // [max tiles]
     int32_t* tile_row0;     // [max tiles]
     int32_t* tile_first;    // [cap + 1]: first tile of each active slot (then the tile count)
-    int32_t* chunk_counts;  // [chunks x keyspace] (large planner)
+    int32_t* chunk_counts;  // [chunks x kLargeKeySpace] (large planner)
+    // (sized for any slot count at creation, so resize never reallocates them)
     int64_t max_tiles;
 };
 
+}  // namespace ftmoe
+
+namespace ftmoe {
+// Cache state the kernels read at run time rather than from their arguments,
+// so that a call captured into a graph sees it as it is at replay: the profile
+// (ft_cache_set_profile) and the generation of the slot pool, which
+// ft_cache_resize advances (classify compares it with the generation the
+// call was enqueued under).  Lives in device memory until the cache is
+// destroyed.
+struct DevState {
+    uint32_t gen;
+    uint32_t bp_mbps, bh_mbps;
+    int32_t max_fetch;
+};
 }  // namespace ftmoe
 
 struct ft_cache {
@@ -143,16 +159,18 @@ struct ft_cache {
     int32_t max_tokens;
     int32_t cap;               // max_tokens * k
     int device;
-    const uint8_t* bank_host;
-    const uint8_t* bank_dev;   // device-visible address of the pinned bank
+    const uint8_t** bank_host; // [L] host address of layer l's E records (pinned; entries may repeat)
+    const uint8_t** bank_dev;  // [L] in device memory: the device-visible addresses of the same banks
     uint8_t* pool;             // N * S bytes of HBM
     // control state (device)
     int32_t* slot_for_id;      // [L*E]
-    int32_t* id_of_slot;       // [N]
-    uint64_t* stamp;           // [N]
+    int32_t* id_of_slot;       // [kMaxSlots]: entries past N unused (never reallocated)
+    uint64_t* stamp;           // [kMaxSlots]
     uint64_t* clock;           // [1]
     unsigned long long* counters;  // [C_N]
     int32_t* errflag;          // [1]
+    ftmoe::DevState* dstate;   // [1] profile and pool generation (device)
+    uint32_t gen;              // the pool generation calls are enqueued under
     uint32_t host_wait_polls;  // bound of the combine's wait for the host branch (FTMOE_HOST_WAIT_POLLS)
     uint64_t* gseq_dev;        // [1] number of the last host-branch call made by a graph replay
     // internal copy of the last classify's fill worklist and counts

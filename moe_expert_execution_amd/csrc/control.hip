@@ -24,8 +24,8 @@ struct CtrlArgs {
     uint64_t* clock;
     unsigned long long* counters;
     int32_t* errflag;
-    uint32_t bp, bh;
-    int32_t max_fetch;
+    const DevState* ds;     // profile and pool generation, read at run time
+    uint32_t gen;           // the pool generation this call was enqueued under
     int64_t S;
     // caller outputs (any may be null)
     int32_t* o_counts;
@@ -109,6 +109,9 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
     const int E = a.E, N = a.N, R = a.R;
     const int ewords = (E + 31) >> 5, nwords = (N + 31) >> 5;
     const uint64_t clk = *a.clock;
+    const uint32_t gen_now = a.ds->gen;
+    const uint32_t bp = a.ds->bp_mbps, bh = a.ds->bh_mbps;
+    const int32_t max_fetch = a.ds->max_fetch;
 
     // Every map read of the call is issued here, together: the layer's
     // slot_for_id entries (expert tid + j * kCtrlThreads), and the stamp and
@@ -130,6 +133,21 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
         const int s = tid + j * kCtrlThreads;
         pst[j] = s < N ? a.stamp[s] : 0;
         pown[j] = s < N ? a.id_of_slot[s] : -1;
+    }
+
+    // A call replayed from a graph captured before ft_cache_resize: its slot
+    // count and pool are gone.  It changes nothing but its routes, which all
+    // become INT32_MIN (so the rest of the call has no expert to run), and
+    // raises error flag 16.  The loads above stay within the maps, which
+    // resize never reallocates.
+    if (gen_now != a.gen) {
+        for (int r = tid; r < R; r += kCtrlThreads) a.ids[r] = INT32_MIN;
+        if (tid < 4) {
+            a.wl_counts[tid] = 0;
+            if (a.o_counts) a.o_counts[tid] = 0;
+        }
+        if (tid == 0) atomicOr(a.errflag, 16);
+        return;
     }
 
     for (int i = tid; i < ewords; i += kCtrlThreads) ebits[i] = 0;
@@ -188,7 +206,7 @@ __global__ void __launch_bounds__(kCtrlThreads) classify_kernel(CtrlArgs a) {
     int htot;
     int hb = block_excl_scan(myhits, wsum, &htot);
     const int h = htot, m = nu - htot;
-    const int q = fill_count(m, h, N, a.bp, a.bh, a.max_fetch);
+    const int q = fill_count(m, h, N, bp, bh, max_fetch);
     for (int j = 0; j < per; ++j) {
         int i = i0 + j;
         if (i >= nu) break;
@@ -332,8 +350,8 @@ constexpr int kFillBlocks = 512;
 
 __global__ void __launch_bounds__(kFillThreads)
     fill_kernel(const int32_t* wl_counts, const int32_t* wl_slot, const int32_t* wl_src,
-                const uint8_t* __restrict__ bank, uint8_t* __restrict__ pool, int64_t S, int64_t P) {
-    fill_records<kFillThreads>(wl_counts, wl_slot, wl_src, bank, pool, S, P, blockIdx.x, gridDim.x);
+                const uint8_t* const* __restrict__ banks, int E, uint8_t* __restrict__ pool, int64_t S, int64_t P) {
+    fill_records<kFillThreads>(wl_counts, wl_slot, wl_src, banks, E, pool, S, P, blockIdx.x, gridDim.x);
 }
 
 // Clear the owners of full-layer buffer slots [s0, s0 + E) before a layer is
@@ -410,9 +428,8 @@ hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, 
     a.clock = c->clock;
     a.counters = c->counters;
     a.errflag = c->errflag;
-    a.bp = c->prof.bp_mbps;
-    a.bh = c->prof.bh_mbps;
-    a.max_fetch = c->prof.max_fetch;
+    a.ds = c->dstate;
+    a.gen = c->gen;
     a.S = c->rl.S;
     a.o_counts = out ? out->counts : nullptr;
     a.o_uniq = out ? out->uniq : nullptr;
@@ -438,7 +455,7 @@ hipError_t launch_classify(ft_cache* c, int32_t layer, int32_t* ids, int32_t R, 
 hipError_t launch_fill(ft_cache* c, hipStream_t st, TimedLaunch tl) {
     hipExtLaunchKernelGGL(fill_kernel, dim3(kFillBlocks), dim3(kFillThreads), 0, st, tl.start, tl.stop, 0,
                           (const int32_t*)c->wl_counts, (const int32_t*)c->wl_slot, (const int32_t*)c->wl_src,
-                          c->bank_dev, c->pool, c->rl.S, c->rl.P);
+                          (const uint8_t* const*)c->bank_dev, (int)c->sh.experts, c->pool, c->rl.S, c->rl.P);
     return hipGetLastError();
 }
 

@@ -11,8 +11,9 @@ namespace ftmoe {
 constexpr int64_t kFillChunk = 64 * 1024;
 typedef uint32_t fill_vec_t __attribute__((ext_vector_type(4)));   // 16 bytes
 
-// Record wl_src[i] of the bank (records S bytes apart) -> slot wl_slot[i] of
-// the pool (slots P bytes apart, P a multiple of 256), for i < q =
+// Record wl_src[i] (a flat id: layer wl_src[i] / E, expert wl_src[i] % E) of
+// the host bank -> slot wl_slot[i] of the pool (slots P bytes apart, P a
+// multiple of 256), for i < q =
 // wl_counts[3] (device data, so the grid is fixed).  Workgroup `blk` of
 // `nblk`, NT threads, walks 64 KiB chunks of the q records, one 16-byte load
 // in flight per thread; a record size that is not a multiple of 16 bytes
@@ -22,8 +23,8 @@ typedef uint32_t fill_vec_t __attribute__((ext_vector_type(4)));   // 16 bytes
 // (256 threads x 1 load) 55.6-56.5 GB/s, 16 KiB 52.4-53.5, 32 KiB 49.8-52.2.
 template <int NT>
 __device__ __forceinline__ void fill_records(const int32_t* wl_counts, const int32_t* wl_slot,
-                                             const int32_t* wl_src, const uint8_t* __restrict__ bank,
-                                             uint8_t* __restrict__ pool, int64_t S, int64_t P, int blk,
+                                             const int32_t* wl_src, const uint8_t* const* __restrict__ banks,
+                                             int E, uint8_t* __restrict__ pool, int64_t S, int64_t P, int blk,
                                              int nblk) {
     const int q = wl_counts[3];
     const int64_t cpr = (S + kFillChunk - 1) / kFillChunk;
@@ -32,7 +33,8 @@ __device__ __forceinline__ void fill_records(const int32_t* wl_counts, const int
         const int64_t i = c / cpr;
         const int64_t off = (c - i * cpr) * kFillChunk;
         const int64_t len = (S - off) < kFillChunk ? (S - off) : kFillChunk;
-        const uint8_t* s8 = bank + (int64_t)wl_src[i] * S + off;
+        const int flat = wl_src[i];
+        const uint8_t* s8 = banks[flat / E] + (int64_t)(flat % E) * S + off;
         uint8_t* d8 = pool + (int64_t)wl_slot[i] * P + off;
         // streaming (nontemporal) stores: the records go to HBM without
         // leaving dirty L2 lines whose write-back would delay the expert

@@ -50,7 +50,7 @@ struct Job {
 struct HostBranch {
     ft_shape sh;
     RecordLayout rl;
-    const uint8_t* bank;
+    std::vector<const uint8_t*> bank;   // [L]: layer l's E records (host addresses)
     int32_t max_tokens;
     HostStaging stg;
     int nthreads;
@@ -258,7 +258,7 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
             const int xi = x0 + it / per, b = it % per;
             const int e = jb.experts[xi];
             const int t0 = jb.tok_off[xi], nt = jb.tok_off[xi + 1] - t0;
-            const uint8_t* rec = hb->bank + ((int64_t)jb.layer * E + e) * S;
+            const uint8_t* rec = hb->bank[jb.layer] + (int64_t)e * S;
             ws.fit(nt);
             for (int i = 0; i < nt; ++i) ws.vec[i] = hb->xf.data() + (int64_t)jb.tok[t0 + i] * d;
             const int p = b >> 1, h = b & 1;
@@ -281,7 +281,7 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
             for (int xi = x0; xi < x1; ++xi) {
                 const int e = jb.experts[xi];
                 const int t0 = jb.tok_off[xi], nt = jb.tok_off[xi + 1] - t0;
-                const uint8_t* rec = hb->bank + ((int64_t)jb.layer * E + e) * S;
+                const uint8_t* rec = hb->bank[jb.layer] + (int64_t)e * S;
                 ws.fit(nt);
                 const int64_t hrow0 = together ? t0 : 0;
                 for (int i = 0; i < nt; ++i) ws.vec[i] = hb->hbuf.data() + (hrow0 + i) * f;
@@ -463,12 +463,12 @@ void poller_main(HostBranch* hb, int cpu) {
 
 }  // namespace
 
-HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const uint8_t* bank_host,
+HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const uint8_t* const* bank_layers,
                                int32_t max_tokens) {
     auto* hb = new HostBranch();
     hb->sh = sh;
     hb->rl = rl;
-    hb->bank = bank_host;
+    hb->bank.assign(bank_layers, bank_layers + sh.layers);
     hb->max_tokens = max_tokens;
     const int64_t d = sh.d_model, k = sh.top_k, f = sh.d_ff;
     void* p = nullptr;

@@ -23,7 +23,6 @@ namespace ftmoe {
 namespace {
 
 constexpr int kPlanThreads = 1024;
-constexpr int kLargeKeySpace = 8192;   // slots addressable by the chunked planner
 
 struct PlanArgs {
     const int32_t* routes;
@@ -90,14 +89,21 @@ __device__ __forceinline__ void stage_to_host(const PlanArgs& a, int tid, int nt
 }
 
 // Slot of route r, or -1 when it is not a GPU route (host, invalid, duplicate).
+// A value that is neither a route of the call's mode nor INT32_MIN (the mark
+// classify leaves on an id it already flagged) raises error flag 1 and is
+// ignored, as the host branch and the combine ignore it.
 __device__ __forceinline__ int route_slot(const PlanArgs& a, int r) {
     int v = a.routes[r];
     int s;
-    if (a.slot_base >= 0) {
-        s = (v >= 0 && v < a.E) ? a.slot_base + v : -1;
-    } else {
+    bool ok;
+    if (a.slot_base >= 0) {            // raw expert ids of a full-layer buffer
+        ok = v >= 0 && v < a.E;
+        s = ok ? a.slot_base + v : -1;
+    } else {                           // slot ids, or host routes -(1 + e)
+        ok = (v >= 0 && v < a.N) || (v < 0 && v >= -a.E);
         s = (v >= 0 && v < a.N) ? v : -1;
     }
+    if (!ok && v != INT32_MIN) atomicOr(a.errflag, 1);
     if (s < 0) return -1;
     const int t = r / a.k, j = r - t * a.k;
     for (int jj = 0; jj < j; ++jj) {          // drop a repeated expert of the same token
@@ -235,7 +241,8 @@ struct FillArgs {
     const int32_t* wl_counts;
     const int32_t* wl_slot;
     const int32_t* wl_src;
-    const uint8_t* bank;
+    const uint8_t* const* banks;   // device addresses of each layer's host bank
+    int E;
     uint8_t* pool;
     int64_t S, P;   // bank record stride, pool slot stride
 };
@@ -253,7 +260,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_fill_kernel(PlanArgs a, Fil
     // 256 threads per workgroup pull, as in the fill kernel: a workgroup's
     // host reads in flight set the PCIe rate
     if (threadIdx.x < 256)
-        fill_records<256>(f.wl_counts, f.wl_slot, f.wl_src, f.bank, f.pool, f.S, f.P, blockIdx.x - 1,
+        fill_records<256>(f.wl_counts, f.wl_slot, f.wl_src, f.banks, f.E, f.pool, f.S, f.P, blockIdx.x - 1,
                           gridDim.x - 1);
 }
 
@@ -421,7 +428,8 @@ hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base,
     a.work = c->counters + work_counter;
     if (fill) {
         if (a.R > kSmallPlanRoutes) return hipErrorInvalidValue;
-        FillArgs f{c->wl_counts, c->wl_slot, c->wl_src, c->bank_dev, c->pool, c->rl.S, c->rl.P};
+        FillArgs f{c->wl_counts, c->wl_slot, c->wl_src, (const uint8_t* const*)c->bank_dev, (int)c->sh.experts,
+                   c->pool, c->rl.S, c->rl.P};
         hipExtLaunchKernelGGL(plan_fill_kernel, dim3(1 + kPlanFillBlocks), dim3(kPlanThreads), 0, st, fill->start,
                               fill->stop, 0, a, f);
     } else if (a.R <= kSmallPlanRoutes) {

@@ -6,8 +6,8 @@ pinned host banks from ft_host_alloc exposed as NumPy views.
 import numpy as np
 import torch
 
-from . import (FtClassifyOut, ft_cache_create, ft_cache_destroy, ft_host_alloc, ft_host_free, host_array,
-               profile, shape)
+from . import (FtClassifyOut, ft_cache_create, ft_cache_create_layers, ft_cache_destroy, ft_host_alloc,
+               ft_host_free, host_array, profile, shape)
 
 
 class ClassifyBuffers:
@@ -68,13 +68,18 @@ class PinnedBank:
 
 
 class SlotCache:
-    """An ft_cache handle with its shape and profile (closed on close())."""
+    """An ft_cache handle with its shape and profile (closed on close()).
+    `bank_ptr` is one pinned bank of all layers, or a list of per-layer bank
+    addresses (ft_cache_create_layers)."""
 
     def __init__(self, layers, experts, top_k, d_model, d_ff, fmt, bank_ptr, num_slots, max_tokens,
                  bp_mbps, bh_mbps, max_fetch=-1):
         self.shape = shape(layers, experts, top_k, d_model, d_ff, fmt)
         self.profile = profile(bp_mbps, bh_mbps, max_fetch)
-        self.handle = ft_cache_create(self.shape, self.profile, bank_ptr, num_slots, max_tokens)
+        if isinstance(bank_ptr, (list, tuple)):
+            self.handle = ft_cache_create_layers(self.shape, self.profile, list(bank_ptr), num_slots, max_tokens)
+        else:
+            self.handle = ft_cache_create(self.shape, self.profile, bank_ptr, num_slots, max_tokens)
         self.num_slots = num_slots
 
     def close(self):
