@@ -407,3 +407,43 @@ def test_control_at_the_maxima(slots):
         assert fills > slots and s.evictions > 0 and hits > 0
     finally:
         tr.close()
+
+
+@gpu
+def test_many_route_call_refused_past_planner_key_space():
+    """A CACHED forward of more than 1,024 routes on a cache of more than
+    8,192 slots is refused (FT_ERR_UNSUPPORTED) before it takes any state:
+    the next call (1,024 routes) still matches the simulator and the oracle,
+    and no error flag is raised."""
+    cuda()
+    cfg = synth.CONFIGS["tiny"].with_(E=16, k=8, slots=8193, cfg_id=94)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, 129, cfg.bp_mbps, cfg.bh_mbps)
+    sim = OC.SlotCacheSim(1, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+    st = torch.cuda.current_stream().cuda_stream
+    lib = M.lib()
+    wr = synth.router(cfg, 0)
+    try:
+        for T, refused in ((129, True), (128, False)):
+            x = synth.tokens(cfg, T, 900 + T)
+            ids, w, _ = OR.route(x, wr, cfg.k)
+            r = sim.classify(0, ids)
+            xd, idd, wd = dev_u16(x), dev(ids.astype(np.int32)), dev(w)
+            y = torch.zeros((T, cfg.d), dtype=torch.int16, device="cuda")
+            M.ft_cache_classify(sc.handle, 0, idd.data_ptr(), T, None, st)
+            status = lib.ft_moe_forward(sc.handle, 0, M.FT_MODE_CACHED, xd.data_ptr(), idd.data_ptr(), wd.data_ptr(),
+                                        T, y.data_ptr(), st)
+            torch.cuda.synchronize()
+            assert np.array_equal(idd.cpu().numpy(), r.routes), f"T {T}"
+            if refused:
+                assert status == M.FT_ERR_UNSUPPORTED and "8192" in M.ft_last_error(), M.ft_last_error()
+                continue
+            assert status == M.FT_OK, M.ft_last_error()
+            ref = OM.moe_layer(x, ids, w, expert_fn(recs, cfg, 0, maxsize=cfg.E))
+            assert_close_rel(bf16_bits_to_f64(y), ref, 2e-2, f"T {T}")
+        s = M.ft_cache_stats(sc.handle)
+        assert s.error_flags == 0 and s.calls == 2
+    finally:
+        sc.close()
+        bank.close()

@@ -6,11 +6,10 @@ ft_moe_forward on one stream, all calls issued before one sync.
 
 Every call's rewritten routes are compared bit for bit with those of the
 oracle's slot-cache simulator fed by the oracle's routing (so the GPU's ids
-are checked through them), every call's weights with the oracle's, and the
-outputs of sampled calls with the oracle's fp64 layer.  With q about m/3 and
-at least one fill per call, every call here has fills and host experts; the
-samples are calls without hits (the cold start) and calls with hits spread
-over the later steps."""
+are checked through them), every call's weights with the oracle's, and every
+call's output with the oracle's fp64 layer.  With q about m/3 and at least
+one fill per call, every call here has fills and host experts; the first
+step's calls have no hits (the cold start), later ones mix hits in."""
 import numpy as np
 import torch
 
@@ -19,14 +18,13 @@ import synth
 from moe_expert_execution_amd.tensors import SlotCache
 from oracle import cache as OC, route as OR
 
-from gpu_util import assert_close_rel, bf16_bits_to_f64, cuda, expert_fn, gpu, make_bank, oracle_rows
+from gpu_util import assert_close_rel, bf16_bits_to_f64, cuda, gpu, make_bank, oracle_layer_all_rows, record_decoder
 
 STEPS = 6
-PER_KIND = 5      # sampled calls per kind (no hits, hits)
 
 
 @gpu
-def test_decode_full_config_sampled():
+def test_decode_full_config():
     cuda()
     cfg = synth.CONFIGS["decode"]
     L, E, k, d = cfg.layers, cfg.E, cfg.k, cfg.d
@@ -70,17 +68,13 @@ def test_decode_full_config_sampled():
                 hits, fills, host = hits + r.hits, fills + r.q, host + r.m - r.q
                 kinds["hits" if r.hits else "no_hits"].append(i)
         assert fills > 0 and host > 0 and all(kinds.values()), {key: len(v) for key, v in kinds.items()}
-        kinds = {key: [v[j] for j in np.linspace(0, len(v) - 1, min(PER_KIND, len(v))).astype(int)]
-                 for key, v in kinds.items()}
         s_ = M.ft_cache_stats(sc.handle)
         assert (s_.hits, s_.fills, s_.cpu_experts, s_.error_flags) == (hits, fills, host, 0)
 
         y_h = bf16_bits_to_f64(y)
-        for kind, idx in kinds.items():
-            for i in idx:
-                l, x, ids_o, w_o = calls[i]
-                ref = oracle_rows(x, ids_o, w_o, expert_fn(recs, cfg, l, maxsize=k), [0])
-                assert_close_rel(y_h[i:i + 1], ref, 2e-2, f"call {i} ({kind}, layer {l})")
+        for i, (l, x, ids_o, w_o) in enumerate(calls):
+            ref = oracle_layer_all_rows(x, ids_o, w_o, record_decoder(recs, cfg, l))
+            assert_close_rel(y_h[i:i + 1], ref, 2e-2, f"call {i} (step {i // L}, layer {l})")
     finally:
         sc.close()
         bank.close()

@@ -148,3 +148,72 @@ def test_uncapturable_calls_are_refused():
         torch.cuda.synchronize()
         sc.close()
         bank.close()
+
+
+@gpu
+def test_graph_sees_new_profile_and_recapture_after_resize():
+    """A replay uses the cache's profile at replay time: after
+    ft_cache_set_profile (max_fetch 0, every miss to the host) the graph
+    captured before it makes the eager cache's decisions and fills nothing.
+    After ft_cache_resize the graph is captured again (the old one is void and
+    is not replayed) and again equals the eager cache step for step, with
+    outputs matching the oracle."""
+    cuda()
+    cfg = synth.CONFIGS["decode"].with_(layers=4, d=256, E=16, k=4, f=128, slots=12, bp_mbps=20000, bh_mbps=60000)
+    steps, T = 12, 1
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    xs, wr = _setup(cfg, steps, T)
+    mk = lambda: SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, T, cfg.bp_mbps,
+                           cfg.bh_mbps)
+    a, b = mk(), mk()
+    n_ids = cfg.layers * cfg.E
+
+    def capture(step):
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step.enqueue()
+        torch.cuda.synchronize()
+        return g
+
+    try:
+        ea, gb = Step(cfg, a, wr, T), Step(cfg, b, wr, T)
+        g = capture(gb)
+        slots = cfg.slots
+        for s in range(steps):
+            if s == 4:
+                for c in (a, b):
+                    M.ft_cache_set_profile(c.handle, M.profile(cfg.bp_mbps, cfg.bh_mbps, 0))
+                fills_before = M.ft_cache_stats(b.handle).fills
+            if s == 8:
+                assert M.ft_cache_stats(b.handle).fills == fills_before, "max_fetch 0 did not reach the replays"
+                slots = 7
+                for c in (a, b):
+                    M.ft_cache_resize(c.handle, slots)
+                    M.ft_cache_set_profile(c.handle, M.profile(cfg.bp_mbps, cfg.bh_mbps, -1))
+                del g
+                g = capture(gb)
+            ea.x.copy_(xs[:, s])
+            ea.enqueue()
+            gb.x.copy_(xs[:, s])
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(ea.routes, gb.routes) and torch.equal(ea.y, gb.y), f"step {s}"
+            sa = M.ft_cache_snapshot(a.handle, n_ids, slots)
+            sb = M.ft_cache_snapshot(b.handle, n_ids, slots)
+            for u, v in zip(sa[:3], sb[:3]):
+                assert np.array_equal(u, v), f"cache state differs at step {s}"
+            assert sa[3] == sb[3]
+            if s in (5, steps - 1):
+                x = xs[:, s].cpu().numpy().view(np.uint16)
+                ids, w = ea.ids.cpu().numpy(), ea.w.cpu().numpy()
+                for l in range(cfg.layers):
+                    ref = OM.moe_layer(x[l], ids[l], w[l], expert_fn(recs, cfg, l))
+                    assert_close_rel(bf16_bits_to_f64(gb.y[l]), ref, 2e-2, f"graph step {s} layer {l}")
+        cb = M.ft_cache_stats(b.handle)
+        assert cb.fills > fills_before and cb.error_flags == 0 and cb.num_slots == slots
+    finally:
+        a.close()
+        b.close()
+        bank.close()

@@ -205,3 +205,42 @@ def test_resize_keeps_most_recent_packed():
     assert len(sim.residents()) == 3 and sim.N == 10
     r = sim.classify(0, np.array([[5, 6]]))
     assert r.q == 2 and all(v >= 3 for v, _, _ in r.evictions)   # new empty slots first
+
+
+@settings(max_examples=60, deadline=None)
+@given(seed=st.integers(0, 10 ** 6), N=st.integers(1, 12), N2=st.integers(1, 12), E=st.integers(2, 9),
+       L=st.integers(1, 3), k=st.integers(1, 3))
+def test_resize_equals_textbook_lru_truncation(seed, N, N2, E, L, k):
+    """Resize keeps exactly what a textbook LRU cut down to N2 entries keeps:
+    the N2 most recently used entries of a collections.OrderedDict that saw
+    the same accesses, in the same recency order; they are packed into slots
+    0.. in ascending old-slot order; and the resized cache then goes on to
+    behave as a textbook LRU of capacity N2 holding those entries."""
+    k = min(k, E)
+    rng = np.random.default_rng(seed)
+    sim = SlotCacheSim(L, E, N, 60000, 60000)     # q = m while slots allow: every admitted miss is an insert
+
+    def run(lru, n):
+        for l, ids in _calls(L, E, k, n, rng):
+            r = sim.classify(l, ids)
+            uniq = sorted({l * E + int(e) for e in ids.reshape(-1)})
+            for u in uniq:
+                if u in lru.d:
+                    lru.touch(u)
+            evicted = [lru.insert(u) for u in [u for u in uniq if u not in lru.d][: r.q]]
+            assert [old for _, old, _ in r.evictions if old >= 0] == [e for e in evicted if e is not None]
+            assert set(sim.residents()) == set(lru.d)
+
+    lru = TextbookLRU(N)
+    run(lru, 30)
+    before = {u: s for u, s in sim.residents().items()}
+    keep = list(lru.d)[-N2:]                       # the N2 most recent, least recent first
+    moves = sim.resize(N2)
+    assert set(sim.residents()) == set(keep)
+    assert sorted(sim.residents(), key=lambda u: sim.stamp[sim.slot_for_id[u]]) == keep
+    assert sorted(sim.residents().values()) == list(range(len(keep)))
+    assert [o for o, _ in moves] == sorted(before[u] for u in keep)
+    lru2 = TextbookLRU(N2)
+    for u in keep:
+        lru2.d[u] = True
+    run(lru2, 30)
