@@ -147,22 +147,29 @@ def decode_bench(args):
     gu_gbs = experts * gu_bytes / (ms_gu / 1e3) / 1e9
     dn_gbs = experts * dn_bytes / (ms_dn / 1e3) / 1e9
     both_gbs = experts * (gu_bytes + dn_bytes) / ((ms_gu + ms_dn) / 1e3) / 1e9
-    kernel_key = "gemv_gateup_kernel<bf16,1>"
+    kernel_key = "gemv_gateup_kernel<bf16,1>+gemv_down_kernel<bf16,1>"
     traffic = measured_traffic(kernel_key)
     res = {
         "value": args.steps / elapsed,
         "ms_per_step": elapsed / args.steps * 1e3,
         "ms_per_step_kernel_timed_run": el2 / args.steps * 1e3,
+        # the decode expert GEMV of one layer call is two launches, gate/up
+        # (with SwiGLU) then down; the unit is the GPU-executed experts'
+        # records (G x S bytes), so achieved = their bytes / the pair's time
         "roofline": {
-            "bound": "hbm", "kernel": kernel_key, "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic,
-            "bytes_per_launch": experts * gu_bytes / max(n_gu, 1),
-            "avg_launch_us": ms_gu / max(n_gu, 1) * 1e3, "launches": n_gu,
+            "bound": "hbm", "kernel": kernel_key, "achieved": both_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": both_gbs / HBM_PEAK_GBS, "traffic": traffic,
+            "bytes_per_launch": experts * (gu_bytes + dn_bytes) / max(n_gu, 1),
+            "avg_launch_us": (ms_gu + ms_dn) / max(n_gu, 1) * 1e3, "launches": n_gu,
+            "timing": "HIP events stamped by each launch on the caller's stream (kernel-timed run)",
+            "gateup": {"achieved": gu_gbs, "frac": gu_gbs / HBM_PEAK_GBS,
+                       "bytes_per_launch": experts * gu_bytes / max(n_gu, 1),
+                       "avg_launch_us": ms_gu / max(n_gu, 1) * 1e3},
+            "down": {"achieved": dn_gbs, "frac": dn_gbs / HBM_PEAK_GBS,
+                     "bytes_per_launch": experts * dn_bytes / max(n_gu, 1),
+                     "avg_launch_us": ms_dn / max(n_gu, 1) * 1e3},
         },
         "decode_kernels": {
-            # per layer call (a call may launch a SwiGLU finalize kernel before the down GEMV)
-            "gemv_down": {"achieved_gbs": dn_gbs, "avg_launch_us": ms_dn / max(n_gu, 1) * 1e3},
-            "gemv_pair": {"achieved_gbs": both_gbs, "frac": both_gbs / HBM_PEAK_GBS},
             "gpu_experts_per_layer_step": experts / max(n_gu, 1),
         },
         "cache": {**delta, "layer_calls": delta["calls"],
@@ -679,6 +686,403 @@ def miss_replay_bench():
     return out
 
 
+def _stats_delta(a, b, keys=("calls", "unique", "hits", "misses", "fills", "cpu_experts", "evictions",
+                               "bytes_filled", "host_experts", "host_bytes", "host_seconds")):
+    return {key: b[key] - a[key] for key in keys}
+
+
+def _kernel_figures(M, tm, fmt, d, f, calls):
+    """Expert-kernel rooflines of a kernel-timed run: GEMV (HBM) and grouped
+    GEMM (bf16 MFMA, HBM) over the algorithmic bytes and flops of the
+    GPU-executed experts."""
+    gu_b, dn_b = expert_bytes(fmt, d, f)
+    out = {}
+    n_gu = tm.launches[M.FT_K_GEMV_GU]
+    if n_gu:
+        ms = tm.ms[M.FT_K_GEMV_GU] + tm.ms[M.FT_K_GEMV_DOWN]
+        by = tm.gemv_experts * (gu_b + dn_b)
+        out["gemv"] = {"experts_per_call": tm.gemv_experts / n_gu,
+                       "gateup_gbs": tm.gemv_experts * gu_b / (tm.ms[M.FT_K_GEMV_GU] / 1e3) / 1e9,
+                       "pair_gbs": by / (ms / 1e3) / 1e9, "pair_frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                       "pair_us_per_call": ms / n_gu * 1e3}
+    n_gm = tm.launches[M.FT_K_GEMM_GU]
+    if n_gm:
+        ms = tm.ms[M.FT_K_GEMM_GU] + tm.ms[M.FT_K_GEMM_DOWN]
+        fl = 2.0 * tm.gemm_rows * 3 * d * f
+        by = tm.gemm_experts * (gu_b + dn_b)
+        t_roof = max(fl / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), by / (HBM_PEAK_GBS * 1e9))
+        out["gemm"] = {"mfma_dtype": "bf16", "tflops": fl / (ms / 1e3) / 1e12,
+                       "frac_bf16_mfma": fl / (ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"],
+                       "weight_gbs": by / (ms / 1e3) / 1e9, "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                       "roofline_frac": t_roof / (ms / 1e3), "rows_per_call": tm.gemm_rows / n_gm,
+                       "experts_per_call": tm.gemm_experts / n_gm, "ms_per_call": ms / n_gm}
+    if tm.launches[M.FT_K_FILL]:
+        out["fill_ms_total"] = tm.ms[M.FT_K_FILL]
+    return out
+
+
+def fp8_config_bench(args):
+    """The block-FP8 configuration as configured: one layer (d=4096, E=256,
+    top-8, f=2048, e4m3 + 128x128 fp32 scales) through the CACHED path, a
+    64-slot cache that starts cold for each token count, Zipf(1.1) routes
+    (routing bypassed: ids and weights are inputs), B_P/B_H 20/60 GB/s;
+    T = 1, 64, 2048 for 256, 256, 16 steps.  Per T: tokens/s of the whole
+    run (no instrumentation), then the same calls from cold with the expert
+    kernels event-timed (identical decisions) for their rooflines; at T = 2048
+    the one run is event-timed (its steps take seconds, the events microseconds)."""
+    import numpy as np
+    import torch
+
+    import moe_expert_execution_amd as M
+    import synth
+    from moe_expert_execution_amd.tensors import PinnedBank, SlotCache
+
+    cfg = synth.CONFIGS["fp8"]
+    E, k, d, f, S = cfg.E, cfg.k, cfg.d, cfg.f, cfg.S
+    t = time.time()
+    bank = PinnedBank(E * S)
+    synth.bank(cfg, out=bank.records(S), nthreads=min(16, len(os.sched_getaffinity(0))))
+    log(f"fp8 bank {E * S / 1e9:.1f} GB in {time.time() - t:.1f}s")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {"workload": f"block-FP8 layer d={d}, E={E}, top-{k}, f={f}, CACHED, {cfg.slots} slots cold per T, "
+                       f"Zipf(1.1) routes, B_P/B_H {cfg.bp_mbps // 1000}/{cfg.bh_mbps // 1000} GB/s", "runs": {}}
+    for T, steps in zip(cfg.tokens, cfg.steps):
+        xs = torch.stack([torch.from_numpy(synth.tokens(cfg, T, 300 + s, T).view(np.int16))
+                          for s in range(steps)]).cuda()
+        zr = [synth.zipf_routes(cfg, T, s) for s in range(steps)]
+        ids_all = torch.from_numpy(np.stack([z[0] for z in zr]).astype(np.int32)).cuda()
+        w_all = torch.from_numpy(np.stack([z[1] for z in zr])).cuda()
+        work = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        y = torch.empty((T, d), dtype=torch.int16, device="cuda")
+
+        def run(timed):
+            sc = SlotCache(1, E, k, d, f, "fp8", bank.ptr, cfg.slots, T, cfg.bp_mbps, cfg.bh_mbps)
+            M.ft_cache_set_timing(sc.handle, timed)
+            torch.cuda.synchronize()
+            a = M.ft_cache_stats(sc.handle).as_dict()
+            t0 = time.perf_counter()
+            for s in range(steps):
+                work.copy_(ids_all[s])
+                M.ft_cache_classify(sc.handle, 0, work.data_ptr(), T, None, stream)
+                M.ft_moe_forward(sc.handle, 0, M.FT_MODE_CACHED, xs[s].data_ptr(), work.data_ptr(),
+                                 w_all[s].data_ptr(), T, y.data_ptr(), stream)
+                if T >= 2048:
+                    torch.cuda.synchronize()
+                    log(f"fp8 T={T}: step {s + 1} of {steps} ({time.perf_counter() - t0:.1f}s)")
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            b = M.ft_cache_stats(sc.handle).as_dict()
+            assert b["error_flags"] == 0, b
+            tm = M.ft_cache_timing(sc.handle) if timed else None
+            sc.close()
+            return el, _stats_delta(a, b), tm
+
+        if T >= 2048:
+            el, dl, tm = run(True)
+        else:
+            el, dl, _ = run(False)
+            _, _, tm = run(True)
+        r = {"T": T, "steps": steps, "tokens_per_s": T * steps / el, "seconds": el,
+             "miss_rate": dl["misses"] / max(dl["unique"], 1), "per_call": {key: v / steps for key, v in dl.items()},
+             "host_gbs": dl["host_bytes"] / max(dl["host_seconds"], 1e-12) / 1e9,
+             "event_timed_run": T >= 2048, **_kernel_figures(M, tm, "fp8", d, f, steps)}
+        if dl["bytes_filled"] and tm.ms[M.FT_K_FILL]:
+            r["fill_gbs"] = dl["bytes_filled"] / (tm.ms[M.FT_K_FILL] / 1e3) / 1e9
+        res["runs"][f"T{T}"] = r
+        log(f"fp8 T={T}: {r['tokens_per_s']:.1f} tok/s over {steps} steps ({el:.2f}s), miss rate "
+            f"{r['miss_rate']:.2f}, host experts {r['per_call']['cpu_experts']:.1f}/call at {r['host_gbs']:.1f} GB/s" +
+            (f", GEMV pair {r['gemv']['pair_gbs']:.0f} GB/s" if "gemv" in r else "") +
+            (f", GEMM {r['gemm']['tflops']:.0f} TFLOP/s" if "gemm" in r else ""))
+        del xs, ids_all, w_all
+    bank.close()
+    return res
+
+
+def mxfp4_config_bench(args, phys_layers=8):
+    """The MXFP4 configuration as configured: 61 layers (d=7168, E=256, top-8,
+    f=2048, e2m1 + e8m0 per 32).  The 365 GB host bank cannot be pinned, so the
+    layer banks alias: layer l reads physical layer l mod `phys_layers`
+    (ft_cache_create_layers; flat ids, and every control decision, stay per
+    layer).  Decode: 128 steps x 61 layers, one token per step, from a cold
+    cache of 7,385 slots (60% of 288e9 bytes), B_P/B_H 20/60 GB/s, AR(1)
+    hidden states, routing on the GPU; then the same steps from cold with the
+    expert kernels event-timed.  Prefill: a 4,096-token chunk streamed through
+    all 61 layers with the double buffer (2E slots), the grouped GEMM's MFMA
+    utilisation measured with one layer resident."""
+    import numpy as np
+    import torch
+
+    import moe_expert_execution_amd as M
+    import synth
+    from moe_expert_execution_amd.tensors import PinnedBank, SlotCache
+
+    cfg = synth.CONFIGS["mxfp4"]
+    L, E, k, d, f, S = cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, cfg.S
+    LP = phys_layers
+    t = time.time()
+    bank = PinnedBank(LP * E * S)
+    synth.bank(cfg.with_(layers=LP), out=bank.records(S), nthreads=min(16, len(os.sched_getaffinity(0))))
+    ptrs = [bank.ptr + (l % LP) * E * S for l in range(L)]
+    log(f"mxfp4 bank: {LP} physical layers, {LP * E * S / 1e9:.1f} GB pinned in {time.time() - t:.1f}s")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {"workload": f"MXFP4, {L} layers (banks of {LP} physical layers, aliased l mod {LP}), d={d}, E={E}, "
+                       f"top-{k}, f={f}"}
+    # ---- decode
+    steps = cfg.steps[cfg.tokens.index(1)]
+    xs = torch.stack([torch.from_numpy(synth.ar1_tokens(cfg, l, steps).view(np.int16)) for l in range(L)]).cuda()
+    wr = torch.stack([torch.from_numpy(synth.router(cfg, l).view(np.int16)) for l in range(L)]).cuda()
+    ids = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((L, d), dtype=torch.int16, device="cuda")
+
+    def decode_run(timed):
+        sc = SlotCache(L, E, k, d, f, "mxfp4", ptrs, cfg.slots, 1, cfg.bp_mbps, cfg.bh_mbps)
+        h, shp = sc.handle, sc.shape
+        M.ft_cache_set_timing(h, timed)
+        torch.cuda.synchronize()
+        a = M.ft_cache_stats(h).as_dict()
+        t0 = time.perf_counter()
+        marks = []
+        for s in range(steps):
+            for l in range(L):
+                xp = xs[l, s].data_ptr()
+                M.ft_moe_route(shp, xp, wr[l].data_ptr(), 1, ids[l].data_ptr(), w[l].data_ptr(), stream)
+                M.ft_cache_classify(h, l, ids[l].data_ptr(), 1, None, stream)
+                M.ft_moe_forward(h, l, M.FT_MODE_CACHED, xp, ids[l].data_ptr(), w[l].data_ptr(), 1, y[l].data_ptr(),
+                                 stream)
+            if s + 1 in (steps // 2, steps):
+                torch.cuda.synchronize()
+                marks.append(time.perf_counter() - t0)
+        b = M.ft_cache_stats(h).as_dict()
+        assert b["error_flags"] == 0, b
+        tm = M.ft_cache_timing(h) if timed else None
+        sc.close()
+        return marks, _stats_delta(a, b), tm
+
+    marks, dl, _ = decode_run(False)
+    _, _, tm = decode_run(True)
+    calls = steps * L
+    dec = {"steps": steps, "slots": cfg.slots, "tokens_per_s": steps / marks[-1], "seconds": marks[-1],
+           "tokens_per_s_second_half": (steps - steps // 2) / (marks[1] - marks[0]),
+           "miss_rate": dl["misses"] / max(dl["unique"], 1), "per_call": {key: v / calls for key, v in dl.items()},
+           "host_gbs": dl["host_bytes"] / max(dl["host_seconds"], 1e-12) / 1e9,
+           **_kernel_figures(M, tm, "mxfp4", d, f, calls)}
+    if tm.ms[M.FT_K_FILL]:
+        dec["fill_gbs"] = dl["bytes_filled"] / (tm.ms[M.FT_K_FILL] / 1e3) / 1e9
+    res["decode"] = dec
+    log(f"mxfp4 decode: {dec['tokens_per_s']:.1f} tok/s over {steps} steps from cold "
+        f"({dec['tokens_per_s_second_half']:.1f} in the second half), miss rate {dec['miss_rate']:.2f}, GEMV pair "
+        f"{dec['gemv']['pair_gbs']:.0f} GB/s ({dec['gemv']['pair_frac_hbm']:.1%})")
+    del xs, wr
+    # ---- prefill
+    T = cfg.tokens[0]
+    sc = SlotCache(L, E, k, d, f, "mxfp4", ptrs, 2 * E, T, cfg.bp_mbps, cfg.bh_mbps)
+    h, shp = sc.handle, sc.shape
+    x = torch.from_numpy(synth.tokens(cfg, T, 7).view(np.int16)).cuda()
+    pids = torch.empty((L, T, k), dtype=torch.int32, device="cuda")
+    pw = torch.empty((L, T, k), dtype=torch.float32, device="cuda")
+    py = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    for l in range(L):
+        wl = torch.from_numpy(synth.router(cfg, l).view(np.int16)).cuda()
+        M.ft_moe_route(shp, x.data_ptr(), wl.data_ptr(), T, pids[l].data_ptr(), pw[l].data_ptr(), stream)
+    torch.cuda.synchronize()
+
+    def fwd(l, flags=M.FT_PREFETCH_NEXT):
+        M.ft_moe_forward(h, l, M.FT_MODE_STREAMED | flags, x.data_ptr(), pids[l].data_ptr(), pw[l].data_ptr(), T,
+                         py.data_ptr(), stream)
+
+    fwd(0, 0)
+    torch.cuda.synchronize()
+    M.ft_cache_set_timing(h, True)
+    reps = 5
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fwd(0, 0)
+    torch.cuda.synchronize()
+    t_layer = (time.perf_counter() - t0) / reps
+    tm = M.ft_cache_timing(h)
+    M.ft_cache_set_timing(h, False)
+    gem = _kernel_figures(M, tm, "mxfp4", d, f, reps)["gemm"]
+    for l in range(L):          # untimed pass: the timed one then loads every layer
+        fwd(l)
+    torch.cuda.synchronize()
+    loads0 = M.ft_cache_stats(h).layers_streamed
+    t0 = time.perf_counter()
+    for l in range(L):
+        fwd(l)
+        if l % 20 == 19:
+            log(f"mxfp4 prefill stream: layer {l + 1} of {L} enqueued ({time.perf_counter() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    t_stream = time.perf_counter() - t0
+    stt = M.ft_cache_stats(h)
+    assert stt.error_flags == 0
+    loads = stt.layers_streamed - loads0
+    res["prefill"] = {"T": T, "gemm": gem, "layer_ms_resident": t_layer * 1e3,
+                      "stream": {"layers": L, "layer_loads": loads, "bytes": loads * E * S, "seconds": t_stream,
+                                 "pcie_gbs": loads * E * S / t_stream / 1e9, "tokens_per_s": T / t_stream,
+                                 "compute_only_s": L * t_layer, "gpu_busy_frac": L * t_layer / t_stream}}
+    log(f"mxfp4 prefill: GEMM {gem['tflops']:.0f} TFLOP/s ({gem['frac_bf16_mfma']:.1%} of bf16 MFMA), stream "
+        f"{res['prefill']['stream']['pcie_gbs']:.1f} GB/s over {L} layers, {T / t_stream:.0f} tok/s")
+    sc.close()
+    bank.close()
+    return res
+
+
+def tiny_config_bench(args, calls=8):
+    """The tiny configuration: one layer (d=256, E=8, top-2, f=128, bf16), a
+    4-slot cache from cold, B_P/B_H 25/50 GB/s; `calls` calls of 16 fresh
+    tokens (route, classify, CACHED forward)."""
+    import numpy as np
+    import torch
+
+    import moe_expert_execution_amd as M
+    import synth
+    from moe_expert_execution_amd.tensors import PinnedBank, SlotCache
+
+    cfg = synth.CONFIGS["tiny"]
+    T = cfg.tokens[0]
+    bank = PinnedBank(cfg.E * cfg.S)
+    synth.bank(cfg, out=bank.records(cfg.S))
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, T, cfg.bp_mbps, cfg.bh_mbps)
+    stream = torch.cuda.current_stream().cuda_stream
+    xs = torch.stack([torch.from_numpy(synth.tokens(cfg, T, 0 if c == 0 else 100 + c).view(np.int16))
+                      for c in range(calls)]).cuda()
+    wr = torch.from_numpy(synth.router(cfg, 0).view(np.int16)).cuda()
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, cfg.d), dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for c in range(calls):
+        M.ft_moe_route(sc.shape, xs[c].data_ptr(), wr.data_ptr(), T, ids.data_ptr(), w.data_ptr(), stream)
+        M.ft_cache_classify(sc.handle, 0, ids.data_ptr(), T, None, stream)
+        M.ft_moe_forward(sc.handle, 0, M.FT_MODE_CACHED, xs[c].data_ptr(), ids.data_ptr(), w.data_ptr(), T,
+                         y.data_ptr(), stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    st = M.ft_cache_stats(sc.handle)
+    assert st.error_flags == 0
+    sc.close()
+    bank.close()
+    return {"workload": f"tiny layer d={cfg.d}, E={cfg.E}, top-{cfg.k}, f={cfg.f}, bf16, {cfg.slots} slots from "
+                        f"cold, {calls} calls of {T} tokens", "tokens_per_s": calls * T / el,
+            "us_per_call": el / calls * 1e6, "fills": st.fills, "host_experts": st.cpu_experts, "hits": st.hits}
+
+
+def oracle_subsets():
+    """The oracle as it stands (route + slot-cache simulator + fp64 layer),
+    timed on the host cores on a bounded subset of every configuration.  The
+    record decodes of the oracle dominate its float layer (about 0.07 s per
+    bf16 decode record, 0.5 s per block-FP8 record and 1 s per MXFP4 record
+    on one core), so the float subsets are small; the control subsets are
+    whole traces.  Each entry: what ran, seconds, tokens/s on exactly that."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import cache as OC, formats as OF, moe as OM, route as OR
+    clk = time.perf_counter
+    out = {"cores": len(os.sched_getaffinity(0)),
+           "blas": [{key: p_.get(key) for key in ("internal_api", "num_threads")} for p_ in threadpool_info()
+                    if p_.get("user_api") == "blas"]}
+
+    def rec(name, what, tokens, seconds, **kw):
+        out[name] = {"sample": what, "tokens": tokens, "seconds": seconds, "tokens_per_s": tokens / seconds, **kw}
+        log(f"oracle {name}: {tokens / seconds:.4g} tok/s ({what}, {seconds:.1f}s)")
+
+    def decoder(recs, cfg, layer, phys=None):
+        lp = layer if phys is None else layer % phys
+        return lambda e: OF.decode_record(recs[lp * cfg.E + e], cfg.fmt, cfg.d, cfg.f)
+
+    # tiny: all 8 calls
+    cfg = synth.CONFIGS["tiny"]
+    recs = synth.bank(cfg)
+    wr = synth.router(cfg, 0)
+    sim = OC.SlotCacheSim(1, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+    t0 = clk()
+    for c in range(8):
+        x = synth.tokens(cfg, 16, 0 if c == 0 else 100 + c)
+        ids, w, _ = OR.route(x, wr, cfg.k)
+        sim.classify(0, ids)
+        OM.moe_layer(x, ids, w, decoder(recs, cfg, 0))
+    rec("tiny", "8 calls of 16 tokens (route + simulator + layer)", 128, clk() - t0)
+    # decode: control over the whole trace; the float layer on 2 steps x 48 layers
+    cfg = synth.CONFIGS["decode"]
+    L, steps = cfg.layers, cfg.steps[0]
+    xs = [synth.ar1_tokens(cfg, l, steps) for l in range(L)]
+    wrs = [synth.router(cfg, l) for l in range(L)]
+    sim = OC.SlotCacheSim(L, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+    t0 = clk()
+    for s in range(steps):
+        for l in range(L):
+            ids, w, _ = OR.route(xs[l][s:s + 1], wrs[l], cfg.k)
+            sim.classify(l, ids)
+    el = clk() - t0
+    rec("decode_control", f"route + simulator, all {steps} steps x {L} layers", steps, el,
+        us_per_call=el / (steps * L) * 1e6)
+    recs = synth.bank(cfg, 0, 2 * cfg.E).reshape(2, cfg.E, -1)
+    t0 = clk()
+    for s in range(2):
+        for l in range(L):
+            ids, w, _ = OR.route(xs[l][s:s + 1], wrs[l], cfg.k)
+            r_ = synth.bank(cfg, l * cfg.E, (l + 1) * cfg.E) if l >= 2 else recs[l]
+            OM.moe_layer(xs[l][s:s + 1], ids, w, lambda e: OF.decode_record(r_[e], cfg.fmt, cfg.d, cfg.f))
+    rec("decode_layer", f"route + fp64 layer, steps 0-1 x {L} layers (bank generation included)", 2, clk() - t0)
+    # prefill: one layer of the 8,192-token chunk
+    cfg = synth.CONFIGS["prefill"]
+    T = cfg.tokens[0]
+    x = synth.tokens(cfg, T, 7)
+    recs = synth.bank(cfg, 0, cfg.E)
+    t0 = clk()
+    ids, w, _ = OR.route(x, synth.router(cfg, 0), cfg.k)
+    OM.moe_layer(x, ids, w, decoder(recs, cfg, 0))
+    rec("prefill_layer", f"one layer, T={T} (route + fp64 layer)", T, clk() - t0)
+    # fp8: control over all three traces; the float layer on T=1 x 4 steps and T=64 x 1 step
+    cfg = synth.CONFIGS["fp8"]
+    t0 = clk()
+    ntok = 0
+    for T, steps in zip(cfg.tokens, cfg.steps):
+        sim = OC.SlotCacheSim(1, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+        for s in range(steps):
+            ids, _ = synth.zipf_routes(cfg, T, s)
+            sim.classify(0, ids)
+        ntok += T * steps
+    rec("fp8_control", "simulator over the T=1/64/2048 traces (256/256/16 steps; Zipf draws included)", ntok,
+        clk() - t0)
+    recs = synth.bank(cfg)
+    for T, n in ((1, 4), (64, 1)):
+        t0 = clk()
+        for s in range(n):
+            x = synth.tokens(cfg, T, 300 + s, T)
+            ids, w = synth.zipf_routes(cfg, T, s)
+            OM.moe_layer(x, ids, w, decoder(recs, cfg, 0))
+        rec(f"fp8_layer_T{T}", f"fp64 layer, T={T} x {n} step(s)", T * n, clk() - t0)
+    del recs
+    # mxfp4: control over the 128-step decode trace (7,385 slots); the float
+    # layer on one decode step x 4 layers
+    cfg = synth.CONFIGS["mxfp4"]
+    L, steps = cfg.layers, cfg.steps[1]
+    xs = [synth.ar1_tokens(cfg, l, steps) for l in range(L)]
+    wrs = [synth.router(cfg, l) for l in range(L)]
+    sim = OC.SlotCacheSim(L, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+    t0 = clk()
+    for s in range(steps):
+        for l in range(L):
+            ids, w, _ = OR.route(xs[l][s:s + 1], wrs[l], cfg.k)
+            sim.classify(l, ids)
+    el = clk() - t0
+    rec("mxfp4_decode_control", f"route + simulator ({cfg.slots} slots), all {steps} steps x {L} layers", steps, el,
+        us_per_call=el / (steps * L) * 1e6)
+    recs = synth.bank(cfg, 0, 4 * cfg.E)
+    t0 = clk()
+    for l in range(4):
+        ids, w, _ = OR.route(xs[l][:1], wrs[l], cfg.k)
+        OM.moe_layer(xs[l][:1], ids, w, decoder(recs, cfg, l))
+    el = clk() - t0
+    rec("mxfp4_decode_layer", "route + fp64 layer, step 0 x layers 0-3", 4 / L, el, s_per_layer_call=el / 4)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -702,6 +1106,12 @@ def main():
                     help="only replay routing traces through the placement policies (miss rate vs capacity)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny, block-FP8 and MXFP4 configuration runs")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="only the tiny, block-FP8 and MXFP4 configuration runs (one JSON line)")
+    ap.add_argument("--oracle-subsets", action="store_true",
+                    help="only time the oracle on bounded subsets of every configuration (host cores)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer and its slot cache run on a single device and this build has "
@@ -713,6 +1123,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.oracle_subsets:
+        print(json.dumps({"oracle_subsets": oracle_subsets()}), flush=True)
+        return
 
     if args.calibrate_copy:
         n = 1 << 30
@@ -736,6 +1150,10 @@ def main():
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_bench(args)}), flush=True)
         return
+    if args.configs_only:
+        print(json.dumps({"configs": {"tiny": tiny_config_bench(args), "fp8": fp8_config_bench(args),
+                                      "mxfp4": mxfp4_config_bench(args)}}), flush=True)
+        return
     dec, bank, cfg = decode_bench(args)
     cpu = None
     if not args.no_cpu_baseline:
@@ -743,6 +1161,9 @@ def main():
         log(f"cpu oracle: {cpu['value']:.4f} tok/s over {cpu['seconds']:.1f}s on {cpu['cores']} cores")
     bank.close()
     pre = None if args.no_prefill else prefill_bench(args)
+    configs = None
+    if not args.no_configs:
+        configs = {"tiny": tiny_config_bench(args), "fp8": fp8_config_bench(args), "mxfp4": mxfp4_config_bench(args)}
 
     line = {
         "metric": "MoE-layer tokens/s: decode HBM GB/s %peak; prefill MFMA %peak",
@@ -763,6 +1184,7 @@ def main():
         "graph": dec.get("graph"),
         "latency_us": dec.get("latency_us"),
         "prefill": pre,
+        "configs": configs,
     }
     print(json.dumps(line), flush=True)
 

@@ -1,0 +1,243 @@
+// Dot products of the host branch over panel-ordered expert records (AVX-512,
+// plain C++: no HIP).  A host-run expert reads its record straight from the
+// pinned host bank ("The Expert Cache That Follows the Router": a host-run
+// miss reads the source without changing residency).
+//
+// Panel order: rows 32p..32p+31 of a [rows x K] matrix form one contiguous
+// block; inside it the 16-byte unit c of row r sits at unit (c/2)*64 +
+// (c%2)*32 + r%32.  So the 16 rows [32p + 16h, +16) at chunk column c are
+// 256 contiguous bytes: a worker that owns a half panel streams 256-byte runs.
+#pragma once
+#include <immintrin.h>
+#include <stdint.h>
+
+#include <cmath>
+
+namespace ftmoe {
+namespace hostk {
+
+enum { FMT_BF16 = 0, FMT_FP8_B128 = 1, FMT_MXFP4_B32 = 2 };   // the ft_shape formats
+
+inline const float* e2m1_table() {
+    alignas(64) static const float t[16] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f,
+                                            -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
+    return t;
+}
+
+// 16 e4m3 codes -> fp32 / 256.  OCP E4M3 (bias 7): normal (1 + m/8) 2^(e-7),
+// subnormal m 2^-9.  The code's 7 magnitude bits shifted left by 7 are an
+// fp16 bit pattern (bias 15) with the same exponent and mantissa fields:
+// normal (1 + m/8) 2^(e-15), subnormal m 2^-17, i.e. exactly 2^-8 times the
+// e4m3 value in both cases, so the hardware fp16 -> fp32 conversion decodes
+// it and the caller folds the 2^8 into its scale.  (NaN codes are not
+// produced by the encoder and decode as finite values here.)
+constexpr float kE4M3Fp16Scale = 256.0f;
+inline __m512 e4m3x16_div256(const uint8_t* p) {
+    const __m256i v = _mm256_cvtepu8_epi16(_mm_loadu_si128(reinterpret_cast<const __m128i*>(p)));
+    const __m256i mag = _mm256_slli_epi16(_mm256_and_si256(v, _mm256_set1_epi16(0x7F)), 7);
+    const __m256i sgn = _mm256_slli_epi16(_mm256_and_si256(v, _mm256_set1_epi16(0x80)), 8);
+    return _mm512_cvtph_ps(_mm256_or_si256(mag, sgn));
+}
+
+// e8m0 scale byte -> 2^(e - 127) as fp32 bits (e = 0 gives the subnormal
+// 2^-127; 255, the NaN code, is not produced by the encoder)
+inline float e8m0(uint32_t e) {
+    const uint32_t bits = e ? e << 23 : 0x00400000u;
+    float f;
+    __builtin_memcpy(&f, &bits, 4);
+    return f;
+}
+
+// 8 bytes of packed e2m1 (low nibble first) -> 16 fp32 values
+inline __m512 e2m1x16(const uint8_t* p, __m512 lut) {
+    const __m128i b = _mm_loadl_epi64(reinterpret_cast<const __m128i*>(p));
+    const __m512i v = _mm512_cvtepu8_epi32(_mm_unpacklo_epi8(b, b));      // b0 b0 b1 b1 ...
+    const __m512i sh = _mm512_set_epi32(4, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 0);
+    const __m512i idx = _mm512_and_si512(_mm512_srlv_epi32(v, sh), _mm512_set1_epi32(0xF));
+    return _mm512_permutexvar_ps(idx, lut);
+}
+
+// Where the half panel (p, h) of a [rows x K] code matrix at `off` starts.
+inline const uint8_t* half_panel_base(int fmt, const uint8_t* rec, int64_t off, int p, int h, int K) {
+    const int64_t row_bytes = fmt == FMT_BF16 ? 2ll * K : fmt == FMT_FP8_B128 ? (int64_t)K : (int64_t)K / 2;
+    return rec + off + (int64_t)p * 32 * row_bytes + h * 256;
+}
+
+// One pass over the half panel for NT <= 3 vectors: each chunk of codes is
+// decoded once and dotted with the NT vectors; rows go in two groups of 8, so
+// the 8 * NT accumulators stay in registers.  Suits few vectors (decode: one
+// token), where the record's bytes set the pace.
+template <int NT>
+inline void half_panel_dots_stream(int fmt, const uint8_t* rec, int64_t off, int64_t soff, int p, int h, int K,
+                                   const float* const* vec, float* out) {
+    const uint8_t* base = half_panel_base(fmt, rec, off, p, h, K);
+    for (int r0 = 0; r0 < 16; r0 += 8) {
+        __m512 a[8][NT];
+        for (int j = 0; j < 8; ++j)
+            for (int i = 0; i < NT; ++i) a[j][i] = _mm512_setzero_ps();
+        if (fmt == FMT_BF16) {
+            // a zmm holds rows (r0 + 2q, r0 + 2q + 1) x 8 values: a[q] for q < 4, the two
+            // halves reduced separately
+            for (int c = 0; c < K / 8; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512 + 16 * r0;
+                __m512 x[NT];
+                for (int i = 0; i < NT; ++i) x[i] = _mm512_broadcast_f32x8(_mm256_loadu_ps(vec[i] + 8 * c));
+                for (int q = 0; q < 4; ++q) {
+                    const __m256i w16 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(u + 32 * q));
+                    const __m512 w = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(w16), 16));
+                    for (int i = 0; i < NT; ++i) a[q][i] = _mm512_fmadd_ps(w, x[i], a[q][i]);
+                }
+            }
+            for (int i = 0; i < NT; ++i)
+                for (int q = 0; q < 4; ++q) {
+                    out[i * 16 + r0 + 2 * q] = _mm512_mask_reduce_add_ps(0x00FF, a[q][i]);
+                    out[i * 16 + r0 + 2 * q + 1] = _mm512_mask_reduce_add_ps(0xFF00, a[q][i]);
+                }
+            continue;
+        }
+        if (fmt == FMT_FP8_B128) {
+            const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
+            for (int c = 0; c < K / 16; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512 + 16 * r0;
+                const __m512 s = _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale);
+                __m512 x[NT];
+                for (int i = 0; i < NT; ++i) x[i] = _mm512_loadu_ps(vec[i] + 16 * c);
+                for (int j = 0; j < 8; ++j) {
+                    const __m512 w = _mm512_mul_ps(e4m3x16_div256(u + 16 * j), s);
+                    for (int i = 0; i < NT; ++i) a[j][i] = _mm512_fmadd_ps(w, x[i], a[j][i]);
+                }
+            }
+        } else {
+            const __m512 lut = _mm512_load_ps(e2m1_table());
+            const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h + r0;     // scale panel: 32 x K/32 bytes
+            for (int c = 0; c < K / 32; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512 + 16 * r0;
+                const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
+                __m512 x0[NT], x1[NT];
+                for (int i = 0; i < NT; ++i) {
+                    x0[i] = _mm512_loadu_ps(vec[i] + 32 * c);
+                    x1[i] = _mm512_loadu_ps(vec[i] + 32 * c + 16);
+                }
+                for (int j = 0; j < 8; ++j) {
+                    const __m512 s = _mm512_set1_ps(e8m0(su[j]));
+                    const __m512 w0 = _mm512_mul_ps(e2m1x16(u + 16 * j, lut), s);
+                    const __m512 w1 = _mm512_mul_ps(e2m1x16(u + 16 * j + 8, lut), s);
+                    for (int i = 0; i < NT; ++i)
+                        a[j][i] = _mm512_fmadd_ps(w1, x1[i], _mm512_fmadd_ps(w0, x0[i], a[j][i]));
+                }
+            }
+        }
+        for (int i = 0; i < NT; ++i)
+            for (int j = 0; j < 8; ++j) out[i * 16 + r0 + j] = _mm512_reduce_add_ps(a[j][i]);
+    }
+}
+
+// Decode the half panel (p, h) into w[r * K + k], r < 16 (fp32, row-major).
+inline void half_panel_decode(int fmt, const uint8_t* rec, int64_t off, int64_t soff, int p, int h, int K, float* w) {
+    const uint8_t* base = half_panel_base(fmt, rec, off, p, h, K);
+    switch (fmt) {
+        case FMT_BF16:
+            for (int c = 0; c < K / 8; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                for (int r = 0; r < 16; r += 2) {
+                    const __m256i w16 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(u + 16 * r));
+                    const __m512 v = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(w16), 16));
+                    _mm256_storeu_ps(w + (int64_t)r * K + 8 * c, _mm512_castps512_ps256(v));
+                    _mm256_storeu_ps(w + (int64_t)(r + 1) * K + 8 * c,
+                                     _mm256_castpd_ps(_mm512_extractf64x4_pd(_mm512_castps_pd(v), 1)));
+                }
+            }
+            return;
+        case FMT_FP8_B128: {
+            const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
+            for (int c = 0; c < K / 16; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                const __m512 s = _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale);
+                for (int r = 0; r < 16; ++r)
+                    _mm512_storeu_ps(w + (int64_t)r * K + 16 * c, _mm512_mul_ps(e4m3x16_div256(u + 16 * r), s));
+            }
+            return;
+        }
+        default: {
+            const __m512 lut = _mm512_load_ps(e2m1_table());
+            const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h;
+            for (int c = 0; c < K / 32; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
+                for (int r = 0; r < 16; ++r) {
+                    const __m512 s = _mm512_set1_ps(e8m0(su[r]));
+                    _mm512_storeu_ps(w + (int64_t)r * K + 32 * c, _mm512_mul_ps(e2m1x16(u + 16 * r, lut), s));
+                    _mm512_storeu_ps(w + (int64_t)r * K + 32 * c + 16,
+                                     _mm512_mul_ps(e2m1x16(u + 16 * r + 8, lut), s));
+                }
+            }
+            return;
+        }
+    }
+}
+
+// out[i * 16 + r0 + j] = sum_k w[(r0 + j) * K + k] * vec[t0 + i][k] for
+// j < 4, i < TB: 4 rows x TB vectors of accumulators in registers, each
+// K-step of 16 loads 4 + TB vectors for 4 * TB multiply-adds.
+template <int TB>
+inline void dots_4xTB(const float* w, int K, const float* const* vec, int t0, int r0, float* out) {
+    __m512 a[4][TB];
+    for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < TB; ++i) a[j][i] = _mm512_setzero_ps();
+    const float* w0 = w + (int64_t)r0 * K;
+    for (int k = 0; k < K; k += 16) {
+        const __m512 wv0 = _mm512_loadu_ps(w0 + k);
+        const __m512 wv1 = _mm512_loadu_ps(w0 + K + k);
+        const __m512 wv2 = _mm512_loadu_ps(w0 + 2 * (int64_t)K + k);
+        const __m512 wv3 = _mm512_loadu_ps(w0 + 3 * (int64_t)K + k);
+        for (int i = 0; i < TB; ++i) {
+            const __m512 x = _mm512_loadu_ps(vec[t0 + i] + k);
+            a[0][i] = _mm512_fmadd_ps(wv0, x, a[0][i]);
+            a[1][i] = _mm512_fmadd_ps(wv1, x, a[1][i]);
+            a[2][i] = _mm512_fmadd_ps(wv2, x, a[2][i]);
+            a[3][i] = _mm512_fmadd_ps(wv3, x, a[3][i]);
+        }
+    }
+    for (int i = 0; i < TB; ++i)
+        for (int j = 0; j < 4; ++j) out[(t0 + i) * 16 + r0 + j] = _mm512_reduce_add_ps(a[j][i]);
+}
+
+// Dots of 16 decoded rows w [16 x K] with nt vectors: out[i * 16 + r].
+inline void dots_16xT(const float* w, int K, const float* const* vec, int nt, float* out) {
+    for (int r0 = 0; r0 < 16; r0 += 4) {
+        int t0 = 0;
+        for (; t0 + 6 <= nt; t0 += 6) dots_4xTB<6>(w, K, vec, t0, r0, out);
+        switch (nt - t0) {
+            case 5: dots_4xTB<5>(w, K, vec, t0, r0, out); break;
+            case 4: dots_4xTB<4>(w, K, vec, t0, r0, out); break;
+            case 3: dots_4xTB<3>(w, K, vec, t0, r0, out); break;
+            case 2: dots_4xTB<2>(w, K, vec, t0, r0, out); break;
+            case 1: dots_4xTB<1>(w, K, vec, t0, r0, out); break;
+            default: break;
+        }
+    }
+}
+
+// Vectors at which the half panel is decoded once into `wdec` (16 * K
+// floats) and dotted by register-blocked tiles: there the multiply-adds, not
+// the record's bytes, set the pace.
+constexpr int kBlockedMinVectors = 4;
+
+// Dots of the 16 rows [32p + 16h, +16) of a panel-ordered [rows x K] matrix
+// (codes at `off`, scales at `soff`) with nt >= 1 fp32 vectors vec[i] (length
+// K): out[i * 16 + r].  wdec: scratch of 16 * K floats.
+inline void half_panel_dots(int fmt, const uint8_t* rec, int64_t off, int64_t soff, int p, int h, int K,
+                            const float* const* vec, int nt, float* wdec, float* out) {
+    static_assert(kBlockedMinVectors == 4, "the streaming pass is instantiated for 1..3 vectors");
+    switch (nt) {
+        case 1: half_panel_dots_stream<1>(fmt, rec, off, soff, p, h, K, vec, out); return;
+        case 2: half_panel_dots_stream<2>(fmt, rec, off, soff, p, h, K, vec, out); return;
+        case 3: half_panel_dots_stream<3>(fmt, rec, off, soff, p, h, K, vec, out); return;
+        default:
+            half_panel_decode(fmt, rec, off, soff, p, h, K, wdec);
+            dots_16xT(wdec, K, vec, nt, out);
+    }
+}
+
+}  // namespace hostk
+}  // namespace ftmoe

@@ -29,6 +29,7 @@
 #include <vector>
 
 #include "common.h"
+#include "host_dots.h"
 
 namespace ftmoe {
 namespace {
@@ -69,7 +70,8 @@ struct HostBranch {
     std::atomic<int> finished{0};
     // per-call scratch shared by the workers
     std::vector<float> xf;             // [max_tokens x d] fp32 activations of the tokens with host routes
-    std::vector<float> hbuf;           // SwiGLU outputs: [rows x f], rows = max(max_tokens, 2k)
+    std::vector<float> hbuf;           // SwiGLU outputs [rows x f]: every (expert, token) entry of a call
+                                       // with up to max(max_tokens, 2k, min(max_tokens k, 2^21 / f)) entries
     // host-function contexts of calls captured into graphs: each captured
     // call owns one for the life of the branch (a graph may replay it any
     // number of times)
@@ -102,107 +104,6 @@ struct HostBranch {
 
 namespace {
 
-// ---- weight decoding ------------------------------------------------------------
-// Panel order: rows 32p..32p+31 of a [rows x K] matrix form one contiguous
-// block; inside it the 16-byte unit c of row r sits at unit (c/2)*64 +
-// (c%2)*32 + r%32.  So the 16 rows [32p + 16h, +16) at chunk column c are
-// 256 contiguous bytes: a worker that owns a half panel streams 256-byte runs.
-
-const float kE2M1[16] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f,
-                         -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
-
-// 16 e4m3 codes -> fp32 (OCP E4M3: bias 7, subnormals m * 2^-9; NaN codes are
-// not produced by the encoder and decode as large finite values here).
-inline __m512 e4m3x16(const uint8_t* p) {
-    const __m512i v = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(p)));
-    const __m512i sgn = _mm512_slli_epi32(_mm512_and_si512(v, _mm512_set1_epi32(0x80)), 24);
-    const __m512i e = _mm512_and_si512(_mm512_srli_epi32(v, 3), _mm512_set1_epi32(0xF));
-    const __m512i m = _mm512_and_si512(v, _mm512_set1_epi32(7));
-    const __m512i nrm = _mm512_or_si512(_mm512_slli_epi32(_mm512_add_epi32(e, _mm512_set1_epi32(120)), 23),
-                                        _mm512_slli_epi32(m, 20));
-    const __m512 sub = _mm512_mul_ps(_mm512_cvtepi32_ps(m), _mm512_set1_ps(1.0f / 512.0f));
-    const __mmask16 isn = _mm512_cmpneq_epi32_mask(e, _mm512_setzero_si512());
-    const __m512 mag = _mm512_mask_mov_ps(sub, isn, _mm512_castsi512_ps(nrm));
-    return _mm512_castsi512_ps(_mm512_or_si512(_mm512_castps_si512(mag), sgn));
-}
-
-// 8 bytes of packed e2m1 (low nibble first) -> 16 fp32 values
-inline __m512 e2m1x16(const uint8_t* p, __m512 lut) {
-    const __m128i b = _mm_loadl_epi64(reinterpret_cast<const __m128i*>(p));
-    const __m512i v = _mm512_cvtepu8_epi32(_mm_unpacklo_epi8(b, b));      // b0 b0 b1 b1 ...
-    const __m512i sh = _mm512_set_epi32(4, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 0);
-    const __m512i idx = _mm512_and_si512(_mm512_srlv_epi32(v, sh), _mm512_set1_epi32(0xF));
-    return _mm512_permutexvar_ps(idx, lut);
-}
-
-// Dots of the 16 rows [32p + 16h, +16) of a panel-ordered [rows x K] matrix
-// (codes at `off`, scales at `soff`) with nt fp32 vectors vec[i] (length K):
-// out[i * 16 + r].  acc is caller scratch of 16 * nt vectors.
-void half_panel_dots(const HostBranch* hb, const uint8_t* rec, int64_t off, int64_t soff, int p, int h, int K,
-                     const float* const* vec, int nt, __m512* acc, float* out) {
-    for (int i = 0; i < 16 * nt; ++i) acc[i] = _mm512_setzero_ps();
-    switch (hb->sh.fmt) {
-        case FT_FMT_BF16: {
-            // a zmm holds rows (2q, 2q + 1) x 8 values; acc[i * 16 + q] for q < 8
-            const uint8_t* base = rec + off + (int64_t)p * 32 * (2ll * K) + h * 256;
-            for (int c = 0; c < K / 8; ++c) {
-                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
-                __m512 w[8];
-                for (int q = 0; q < 8; ++q) {
-                    const __m256i w16 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(u + 32 * q));
-                    w[q] = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(w16), 16));
-                }
-                for (int i = 0; i < nt; ++i) {
-                    const __m512 xv = _mm512_broadcast_f32x8(_mm256_loadu_ps(vec[i] + 8 * c));
-                    for (int q = 0; q < 8; ++q) acc[i * 16 + q] = _mm512_fmadd_ps(w[q], xv, acc[i * 16 + q]);
-                }
-            }
-            for (int i = 0; i < nt; ++i)
-                for (int q = 0; q < 8; ++q) {
-                    const __m512 a = acc[i * 16 + q];
-                    out[i * 16 + 2 * q] = _mm512_mask_reduce_add_ps(0x00FF, a);
-                    out[i * 16 + 2 * q + 1] = _mm512_mask_reduce_add_ps(0xFF00, a);
-                }
-            return;
-        }
-        case FT_FMT_FP8_B128: {
-            const uint8_t* base = rec + off + (int64_t)p * 32 * K + h * 256;
-            const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
-            for (int c = 0; c < K / 16; ++c) {
-                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
-                const float s = sc[(16 * c) >> 7];
-                for (int r = 0; r < 16; ++r) {
-                    const __m512 w = _mm512_mul_ps(e4m3x16(u + 16 * r), _mm512_set1_ps(s));
-                    for (int i = 0; i < nt; ++i)
-                        acc[i * 16 + r] = _mm512_fmadd_ps(w, _mm512_loadu_ps(vec[i] + 16 * c), acc[i * 16 + r]);
-                }
-            }
-            break;
-        }
-        case FT_FMT_MXFP4_B32: {
-            const __m512 lut = _mm512_loadu_ps(kE2M1);
-            const uint8_t* base = rec + off + (int64_t)p * 32 * (K / 2) + h * 256;
-            const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h;     // scale panel: 32 x K/32 bytes
-            for (int c = 0; c < K / 32; ++c) {
-                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
-                const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
-                for (int r = 0; r < 16; ++r) {
-                    const __m512 s = _mm512_set1_ps(ldexpf(1.0f, (int)su[r] - 127));
-                    const __m512 w0 = _mm512_mul_ps(e2m1x16(u + 16 * r, lut), s);
-                    const __m512 w1 = _mm512_mul_ps(e2m1x16(u + 16 * r + 8, lut), s);
-                    for (int i = 0; i < nt; ++i) {
-                        __m512 a = _mm512_fmadd_ps(w0, _mm512_loadu_ps(vec[i] + 32 * c), acc[i * 16 + r]);
-                        acc[i * 16 + r] = _mm512_fmadd_ps(w1, _mm512_loadu_ps(vec[i] + 32 * c + 16), a);
-                    }
-                }
-            }
-            break;
-        }
-    }
-    for (int i = 0; i < nt; ++i)
-        for (int r = 0; r < 16; ++r) out[i * 16 + r] = _mm512_reduce_add_ps(acc[i * 16 + r]);
-}
-
 inline float silu(float z) { return z / (1.0f + std::exp(-z)); }
 
 // spin barrier over all participants (workers + the calling thread)
@@ -219,12 +120,12 @@ void barrier(HostBranch* hb, int participants) {
 
 // Per-thread scratch of the host workers.
 struct WorkerScratch {
-    std::vector<__m512> acc;            // 16 * tokens accumulators
     std::vector<float> g, u, y;         // 16 * tokens dot results
     std::vector<const float*> vec;      // token vectors
-    void fit(int nt) {
+    std::vector<float> wdec;            // one decoded half panel, 16 x K (many-token dots)
+    void fit(int nt, int kmax) {
+        if ((int64_t)wdec.size() < 16ll * kmax) wdec.resize(16 * (size_t)kmax);
         if ((int)vec.size() < nt) {
-            acc.resize(16 * (size_t)nt);
             g.resize(16 * (size_t)nt);
             u.resize(16 * (size_t)nt);
             y.resize(16 * (size_t)nt);
@@ -243,7 +144,7 @@ struct WorkerScratch {
 // experts run one after the other, two phases each.
 void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
     const Job& jb = hb->job;
-    const int d = hb->sh.d_model, f = hb->sh.d_ff, E = hb->sh.experts;
+    const int d = hb->sh.d_model, f = hb->sh.d_ff, E = hb->sh.experts, fmt = hb->sh.fmt;
     const int64_t S = hb->rl.S;
     float* P = hb->stg.P;
     const int nx = (int)jb.experts.size();
@@ -259,13 +160,13 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
             const int e = jb.experts[xi];
             const int t0 = jb.tok_off[xi], nt = jb.tok_off[xi + 1] - t0;
             const uint8_t* rec = hb->bank[jb.layer] + (int64_t)e * S;
-            ws.fit(nt);
+            ws.fit(nt, std::max(d, f));
             for (int i = 0; i < nt; ++i) ws.vec[i] = hb->xf.data() + (int64_t)jb.tok[t0 + i] * d;
             const int p = b >> 1, h = b & 1;
-            half_panel_dots(hb, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.vec.data(), nt, ws.acc.data(),
-                            ws.g.data());
-            half_panel_dots(hb, rec, hb->rl.off_up, hb->rl.off_su, p, h, d, ws.vec.data(), nt, ws.acc.data(),
-                            ws.u.data());
+            hostk::half_panel_dots(fmt, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.vec.data(), nt,
+                                   ws.wdec.data(), ws.g.data());
+            hostk::half_panel_dots(fmt, rec, hb->rl.off_up, hb->rl.off_su, p, h, d, ws.vec.data(), nt,
+                                   ws.wdec.data(), ws.u.data());
             const int64_t hrow0 = together ? t0 : 0;
             for (int i = 0; i < nt; ++i)
                 for (int r = 0; r < 16; ++r)
@@ -282,11 +183,11 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
                 const int e = jb.experts[xi];
                 const int t0 = jb.tok_off[xi], nt = jb.tok_off[xi + 1] - t0;
                 const uint8_t* rec = hb->bank[jb.layer] + (int64_t)e * S;
-                ws.fit(nt);
+                ws.fit(nt, std::max(d, f));
                 const int64_t hrow0 = together ? t0 : 0;
                 for (int i = 0; i < nt; ++i) ws.vec[i] = hb->hbuf.data() + (hrow0 + i) * f;
-                half_panel_dots(hb, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f, ws.vec.data(), nt,
-                                ws.acc.data(), ws.y.data());
+                hostk::half_panel_dots(fmt, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f, ws.vec.data(),
+                                       nt, ws.wdec.data(), ws.y.data());
                 for (int i = 0; i < nt; ++i) {
                     float* pr = P + (int64_t)jb.tok[t0 + i] * d + 16 * b;
                     const float wt = jb.wt[t0 + i];
@@ -496,7 +397,9 @@ HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const
     hb->xf.resize((size_t)max_tokens * d);
     // SwiGLU outputs: one row per token for experts run one at a time, or one
     // row per (expert, token) entry when a call's entries fit (at least 2k rows)
-    hb->hbuf.resize((size_t)std::max<int64_t>(max_tokens, 2 * (int64_t)sh.top_k) * f);
+    const int64_t hrows = std::max<int64_t>(std::max<int64_t>(max_tokens, 2 * (int64_t)sh.top_k),
+                                            std::min<int64_t>((int64_t)max_tokens * sh.top_k, (1 << 21) / f));
+    hb->hbuf.resize((size_t)hrows * f);
     for (int i = 0; i < kRing; ++i) hb->ring[i].hb = hb;
     // worker count: cores in the affinity mask minus four (the caller's thread,
     // the mailbox poller, the HIP runtime's threads), at least one: spinning

@@ -1,0 +1,94 @@
+"""The host branch's dot kernels (moe_expert_execution_amd/csrc/host_dots.h)
+on the CPU: for every record format, both paths (one streaming pass for few
+vectors; decode once + register-blocked tiles for many) give the dots of the
+oracle-decoded matrix rows with the vectors, within fp32 rounding (the
+streaming pass exists for 1..3 vectors; above that the dispatcher is used).  A small
+g++ harness includes the header as the library does.  CPU only."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import formats as OF
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "moe_expert_execution_amd", "csrc")
+FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
+
+HARNESS = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include <vector>
+#include "host_dots.h"
+using namespace ftmoe::hostk;
+int main(int argc, char** argv) {
+    const int fmt = atoi(argv[1]), K = atoi(argv[2]), nt = atoi(argv[3]), p = atoi(argv[4]), h = atoi(argv[5]);
+    const long long off = atoll(argv[6]), soff = atoll(argv[7]);
+    const int blocked = atoi(argv[11]);
+    FILE* f = fopen(argv[8], "rb"); fseek(f, 0, SEEK_END); long n = ftell(f); fseek(f, 0, SEEK_SET);
+    std::vector<unsigned char> rec(n); if (fread(rec.data(), 1, n, f) != (size_t)n) return 2; fclose(f);
+    std::vector<float> v((size_t)nt * K);
+    f = fopen(argv[9], "rb"); if (fread(v.data(), 4, v.size(), f) != v.size()) return 3; fclose(f);
+    std::vector<const float*> vec(nt);
+    for (int i = 0; i < nt; ++i) vec[i] = v.data() + (size_t)i * K;
+    std::vector<float> wdec(16 * (size_t)K), out(16 * nt);
+    if (blocked) { half_panel_decode(fmt, rec.data(), off, soff, p, h, K, wdec.data());
+                   dots_16xT(wdec.data(), K, vec.data(), nt, out.data()); }
+    else if (nt == 1) half_panel_dots_stream<1>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
+    else if (nt == 2) half_panel_dots_stream<2>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
+    else if (nt == 3) half_panel_dots_stream<3>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
+    else half_panel_dots(fmt, rec.data(), off, soff, p, h, K, vec.data(), nt, wdec.data(), out.data());
+    f = fopen(argv[10], "wb"); fwrite(out.data(), 4, out.size(), f); fclose(f);
+    return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def harness(tmp_path_factory):
+    d = tmp_path_factory.mktemp("hostdots")
+    src = d / "h.cpp"
+    src.write_text(HARNESS)
+    exe = d / "h"
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-mavx512f", "-mavx512bw", "-mavx512vl", "-mavx512dq",
+                           "-I", CSRC, str(src), "-o", str(exe)])
+    return exe, d
+
+
+def offsets(fmt, d, f):
+    """(gate, down, gate scales, down scales) byte offsets of the record layout."""
+    fd = d * f
+    if fmt == "bf16":
+        return 0, 4 * fd, 0, 0
+    if fmt == "fp8":
+        nb = (d // 128) * (f // 128)
+        return 0, 2 * fd, 3 * fd, 3 * fd + 8 * nb
+    cb, sb = fd // 2, fd // 32
+    return 0, 2 * cb, 3 * cb, 3 * cb + 2 * sb
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("blocked", [0, 1])
+@pytest.mark.parametrize("nt", [1, 2, 3, 4, 7, 13])
+def test_half_panel_dots_match_decoded_rows(harness, fmt, blocked, nt):
+    exe, tmp = harness
+    d, f = 256, 128
+    cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=d, f=f, E=2, cfg_id=93)
+    rec = synth.bank(cfg, 0, 1)[0]
+    Wg, Wu, Wd = OF.decode_record(rec, fmt, d, f)
+    og, od, osg, osd = offsets(fmt, d, f)
+    rng = np.random.default_rng(nt + 10 * blocked)
+    (tmp / "rec.bin").write_bytes(rec.tobytes())
+    for mat, K, rows, off, soff in (("gate", d, Wg.T, og, osg), ("down", f, Wd.T, od, osd)):
+        v = rng.standard_normal((nt, K)).astype(np.float32)
+        (tmp / "v.bin").write_bytes(v.tobytes())
+        for p in range(rows.shape[0] // 32):
+            for h in (0, 1):
+                subprocess.check_call([str(exe), str(FMT[fmt]), str(K), str(nt), str(p), str(h), str(off), str(soff),
+                                       str(tmp / "rec.bin"), str(tmp / "v.bin"), str(tmp / "o.bin"), str(blocked)])
+                got = np.fromfile(tmp / "o.bin", dtype=np.float32).reshape(nt, 16)
+                ref = v.astype(np.float64) @ rows[32 * p + 16 * h: 32 * p + 16 * h + 16].T
+                bound = 1e-5 * (np.abs(v).astype(np.float64) @ np.abs(rows[32 * p + 16 * h: 32 * p + 16 * h + 16]).T)
+                assert np.all(np.abs(got - ref) <= bound + 1e-30), (mat, p, h, np.abs(got - ref).max())
