@@ -315,6 +315,25 @@ ft_status ft_moe_forward(ft_cache* cache, int32_t layer, int32_t mode, const uin
                          const int32_t* routes, const float* w, int32_t T, uint16_t* y, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ft_moe_forward_noalloc — ft_moe_forward in FT_MODE_CACHED for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid it): the same computation and results, with
+ * the call's scratch (planner lists, GEMV K-part sums, h, expert outputs)
+ * taken from one static device array of 16 MiB per GPU instead of the
+ * cache's buffers; the call allocates and frees nothing.
+ * Arguments, ordering and errors are those of ft_moe_forward with mode
+ * FT_MODE_CACHED, plus: calls of more than 4 tokens, or whose scratch would
+ * exceed the 16 MiB (about 2 kq T k f 4 + T k (f + d) 2 bytes, kq <= 8),
+ * are refused with FT_ERR_UNSUPPORTED before anything is enqueued.  The
+ * array lives from the first cache created on a GPU until the process ends
+ * and keeps the last call's contents; every call on a GPU uses the same
+ * array, so calls that overlap in time on one GPU (on different streams, or
+ * from several caches) race: order them on one stream.
+ * ------------------------------------------------------------------------- */
+ft_status ft_moe_forward_noalloc(ft_cache* cache, int32_t layer, const uint16_t* x, const int32_t* routes,
+                                 const float* w, int32_t T, uint16_t* y, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ft_cache_resize — rebuild the slot cache for a new slot count at a safe
  * point (METAL MEDIA summary, item 4; hyper.ai summary, section 方法: the GPU
  * expert cache is rebuilt against a revised VRAM budget without restarting).

@@ -74,6 +74,7 @@ _SIGS = {
     "ft_moe_route": (i32, [ctypes.POINTER(FtShape), vp, vp, i32, vp, vp, vp]),
     "ft_cache_classify": (i32, [vp, i32, vp, i32, ctypes.POINTER(FtClassifyOut), vp]),
     "ft_moe_forward": (i32, [vp, i32, i32, vp, vp, vp, i32, vp, vp]),
+    "ft_moe_forward_noalloc": (i32, [vp, i32, vp, vp, vp, i32, vp, vp]),
     "ft_cache_resize": (i32, [vp, i64]),
     "ft_cache_profile": (i32, [vp, i32, ctypes.POINTER(FtProfile)]),
     "ft_cache_set_profile": (i32, [vp, ctypes.POINTER(FtProfile)]),
@@ -170,6 +171,10 @@ def ft_cache_classify(h: int, layer: int, ids: int, T: int, out=None, stream: in
 def ft_moe_forward(h: int, layer: int, mode: int, x: int, routes: int, w: int, T: int, y: int,
                    stream: int = 0) -> None:
     _check(lib().ft_moe_forward(h, layer, mode, x, routes, w, T, y, stream))
+
+
+def ft_moe_forward_noalloc(h: int, layer: int, x: int, routes: int, w: int, T: int, y: int, stream: int = 0) -> None:
+    _check(lib().ft_moe_forward_noalloc(h, layer, x, routes, w, T, y, stream))
 
 
 def ft_cache_resize(h: int, num_slots: int) -> None:

@@ -239,6 +239,58 @@ ft_status enqueue_load(ft_cache* c, int layer, int buf, hipStream_t st) {
     return FT_OK;
 }
 
+// A CACHED call: host-branch staging, the pending fills, the planner, the GPU
+// experts and the combine.  `c` holds the cache's state; `bufs` supplies the
+// per-call scratch the kernels use (planner lists, GEMV K-part sums, h, expert
+// outputs): the cache itself, or a view of it over the static scratch.
+ft_status forward_cached(ft_cache* c, ft_cache* bufs, int32_t layer, const uint16_t* x, const int32_t* routes,
+                         const float* w, int32_t T, uint16_t* y, hipStream_t st, bool capturing) {
+    const int k = c->sh.top_k;
+    const bool gemv = T <= kGemvMaxTokens;
+    if ((int64_t)T * k > kSmallPlanRoutes && c->N > kLargeKeySpace) {
+        set_error("a CACHED call of more than %d routes needs num_slots <= %d (the chunked planner's key space)",
+                  kSmallPlanRoutes, kLargeKeySpace);
+        return FT_ERR_UNSUPPORTED;
+    }
+    // host branch: the planner copies the call's routes, weights and
+    // activations into pinned staging and, with the mailbox, posts the
+    // call's sequence number; the host workers run the host experts and
+    // leave their partial sums in pinned memory.  A call being captured
+    // into a graph posts to the mailbox's graph words instead, numbered by
+    // a device counter so that every replay posts a new number; the
+    // combine kernel waits for the answer (bounded).  Without a poller,
+    // it uses a captured host function.
+    HostStaging hs = host_branch_staging(c->host);
+    HostSignal sig = capturing ? host_branch_graph_signal(c->host, c->gseq_dev, layer, T)
+                               : host_branch_prepare(c->host, layer, T);
+    // with a mailbox, this call's pending fill rides in the planner's
+    // launch (a host function, in contrast, must follow the staging at once)
+    const bool plan_fill =
+        c->fill_pending && (sig.mailbox || sig.gmbox) && (int64_t)T * k <= kSmallPlanRoutes;
+    const TimedLaunch ftl = plan_fill ? timing_launch(c->timing, FT_K_FILL) : TimedLaunch();
+    FT_HIP(launch_plan(bufs, routes, T, -1, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, w, x, &hs, &sig,
+                       st, plan_fill ? &ftl : nullptr));
+    if (plan_fill) c->fill_pending = false;
+    if (!sig.mailbox && !sig.gmbox) {
+        FT_HIP(hipEventRecord(c->ev_fwd, st));
+        FT_HIP(hipStreamWaitEvent(c->hstream, c->ev_fwd, 0));
+        FT_HIP(capturing ? host_branch_enqueue_captured(c->host, layer, T, c->hstream)
+                         : host_branch_enqueue(c->host, layer, T, c->hstream));
+        FT_HIP(hipEventRecord(c->ev_host, c->hstream));
+    }
+    // this layer's fills, then the GPU experts (hits and fills) from the slot pool
+    ft_status fs = flush_fill(c, st);
+    if (fs != FT_OK) return fs;
+    if (c->xfer_pending) FT_HIP(hipStreamWaitEvent(st, c->ev_xlast, 0));
+    FT_HIP(gemv ? launch_gemv(bufs, x, T, st) : launch_gemm(bufs, x, T, st));
+    // the combine waits for the host branch's answer itself (a stream wait
+    // packet costs ~4.5 us even when the answer is already there); with
+    // a host function, the stream waits for its event
+    if (!sig.mailbox && !sig.gmbox) FT_HIP(hipStreamWaitEvent(st, c->ev_host, 0));
+    FT_HIP(launch_combine(bufs, routes, w, T, hs.P, y, st, &sig));
+    return FT_OK;
+}
+
 }  // namespace
 }  // namespace ftmoe
 
@@ -309,6 +361,7 @@ ft_status ft_cache_create_layers(const ft_shape* shape, const ft_profile* profil
         }                                                                                    \
     } while (0)
     CK(hipGetDevice(&c->device));
+    CK(static_scratch_setup(c->device));      // ft_moe_forward_noalloc's array on this device
     const int64_t L = shape->layers, E = shape->experts, S = c->rl.S, d = shape->d_model, f = shape->d_ff;
     c->bank_host = new (std::nothrow) const uint8_t*[L];
     if (!c->bank_host) {
@@ -483,50 +536,7 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         set_error("kernel timing must be off while a call is captured into a graph");
         return FT_ERR_STATE;
     }
-    if (m == FT_MODE_CACHED) {
-        if ((int64_t)T * k > kSmallPlanRoutes && c->N > kLargeKeySpace) {
-            set_error("a CACHED call of more than %d routes needs num_slots <= %d (the chunked planner's key space)",
-                      kSmallPlanRoutes, kLargeKeySpace);
-            return FT_ERR_UNSUPPORTED;
-        }
-        // host branch: the planner copies the call's routes, weights and
-        // activations into pinned staging and, with the mailbox, posts the
-        // call's sequence number; the host workers run the host experts and
-        // leave their partial sums in pinned memory.  A call being captured
-        // into a graph posts to the mailbox's graph words instead, numbered by
-        // a device counter so that every replay posts a new number; the
-        // combine kernel waits for the answer (bounded).  Without a poller,
-        // it uses a captured host function.
-        HostStaging hs = host_branch_staging(c->host);
-        HostSignal sig = capturing ? host_branch_graph_signal(c->host, c->gseq_dev, layer, T)
-                                   : host_branch_prepare(c->host, layer, T);
-        // with a mailbox, this call's pending fill rides in the planner's
-        // launch (a host function, in contrast, must follow the staging at once)
-        const bool plan_fill =
-            c->fill_pending && (sig.mailbox || sig.gmbox) && (int64_t)T * k <= kSmallPlanRoutes;
-        const TimedLaunch ftl = plan_fill ? timing_launch(c->timing, FT_K_FILL) : TimedLaunch();
-        FT_HIP(launch_plan(c, routes, T, -1, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, w, x, &hs, &sig,
-                           st, plan_fill ? &ftl : nullptr));
-        if (plan_fill) c->fill_pending = false;
-        if (!sig.mailbox && !sig.gmbox) {
-            FT_HIP(hipEventRecord(c->ev_fwd, st));
-            FT_HIP(hipStreamWaitEvent(c->hstream, c->ev_fwd, 0));
-            FT_HIP(capturing ? host_branch_enqueue_captured(c->host, layer, T, c->hstream)
-                             : host_branch_enqueue(c->host, layer, T, c->hstream));
-            FT_HIP(hipEventRecord(c->ev_host, c->hstream));
-        }
-        // this layer's fills, then the GPU experts (hits and fills) from the slot pool
-        ft_status fs = flush_fill(c, st);
-        if (fs != FT_OK) return fs;
-        if (c->xfer_pending) FT_HIP(hipStreamWaitEvent(st, c->ev_xlast, 0));
-        FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
-        // the combine waits for the host branch's answer itself (a stream wait
-        // packet costs ~4.5 us even when the answer is already there); with
-        // a host function, the stream waits for its event
-        if (!sig.mailbox && !sig.gmbox) FT_HIP(hipStreamWaitEvent(st, c->ev_host, 0));
-        FT_HIP(launch_combine(c, routes, w, T, hs.P, y, st, &sig));
-        return FT_OK;
-    }
+    if (m == FT_MODE_CACHED) return forward_cached(c, c, layer, x, routes, w, T, y, st, capturing);
     if (capturing) {
         set_error("STREAMED calls cannot be captured into a graph (their loads follow host-side buffer state)");
         return FT_ERR_UNSUPPORTED;
@@ -563,6 +573,60 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
         }
     }
     return FT_OK;
+}
+
+ft_status ft_moe_forward_noalloc(ft_cache* c, int32_t layer, const uint16_t* x, const int32_t* routes, const float* w,
+                                 int32_t T, uint16_t* y, void* stream) {
+    clear_error();
+    FT_REQUIRE(c, "cache is null");
+    FT_REQUIRE(layer >= 0 && layer < c->sh.layers, "layer %d out of range", layer);
+    FT_REQUIRE(T >= 1 && T <= c->max_tokens, "T must be in 1..max_tokens (%d)", c->max_tokens);
+    FT_REQUIRE(x && routes && w && y, "null pointer");
+    if (T > kGemvMaxTokens) {
+        set_error("ft_moe_forward_noalloc serves calls of at most %d tokens", kGemvMaxTokens);
+        return FT_ERR_UNSUPPORTED;
+    }
+    uint8_t* base = static_cast<uint8_t*>(static_scratch(c->device));
+    if (!base) {
+        set_error("the static scratch of device %d is not set up", c->device);
+        return FT_ERR_STATE;
+    }
+    // the call's scratch, carved from the static array (256-byte aligned pieces)
+    const int64_t R = (int64_t)T * c->sh.top_k, d = c->sh.d_model, f = c->sh.d_ff;
+    size_t off = 0;
+    auto take = [&](int64_t bytes) {
+        uint8_t* p = base + off;
+        off = (off + (size_t)bytes + 255) & ~(size_t)255;
+        return p;
+    };
+    ft_cache v = *c;
+    v.plan.meta = reinterpret_cast<int32_t*>(take(4 * sizeof(int32_t)));
+    v.plan.active_slot = reinterpret_cast<int32_t*>(take(R * sizeof(int32_t)));
+    v.plan.seg = reinterpret_cast<int32_t*>(take((R + 1) * sizeof(int32_t)));
+    v.plan.perm = reinterpret_cast<int32_t*>(take(R * sizeof(int32_t)));
+    v.plan.route_pos = reinterpret_cast<int32_t*>(take(R * sizeof(int32_t)));
+    v.plan.max_tiles = R + 2;                 // one tile per active slot on the GEMV path
+    v.plan.tile_active = reinterpret_cast<int32_t*>(take(v.plan.max_tiles * sizeof(int32_t)));
+    v.plan.tile_row0 = reinterpret_cast<int32_t*>(take(v.plan.max_tiles * sizeof(int32_t)));
+    v.plan.tile_first = reinterpret_cast<int32_t*>(take((R + 1) * sizeof(int32_t)));
+    v.plan.chunk_counts = nullptr;            // the one-workgroup planner only (R <= 64)
+    v.cap_gemv = (int32_t)R;
+    v.gv_part = reinterpret_cast<float*>(take(2ll * c->gv_kq * R * f * sizeof(float)));
+    v.H = reinterpret_cast<uint16_t*>(take(R * f * sizeof(uint16_t)));
+    v.Y = reinterpret_cast<uint16_t*>(take(R * d * sizeof(uint16_t)));
+    if (off > kStaticScratchBytes) {
+        set_error("this call needs %zu bytes of scratch; the static scratch holds %zu", off, kStaticScratchBytes);
+        return FT_ERR_UNSUPPORTED;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    FT_HIP(hipStreamIsCapturing(st, &cap));
+    const bool capturing = cap != hipStreamCaptureStatusNone;
+    if (capturing && c->timing) {
+        set_error("kernel timing must be off while a call is captured into a graph");
+        return FT_ERR_STATE;
+    }
+    return forward_cached(c, &v, layer, x, routes, w, T, y, st, capturing);
 }
 
 ft_status ft_cache_resize(ft_cache* c, int64_t new_num_slots) {

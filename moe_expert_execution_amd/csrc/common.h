@@ -22,6 +22,7 @@ constexpr int kChunkTokens = 64;       // tokens per stable-sort chunk (one 64-b
 constexpr int kSmallPlanRoutes = 1024; // routes handled by the one-workgroup planner
 constexpr int kLargeKeySpace = 8192;   // slots (or experts) addressable by the chunked planner
 constexpr int kGemvMaxTokens = 4;      // tokens per call served by the GEMV path
+constexpr size_t kStaticScratchBytes = 16u << 20;   // the per-GPU static scratch of ft_moe_forward_noalloc
 
 // device counters (ft_stats order)
 enum { C_CALLS, C_ROUTES, C_UNIQUE, C_HITS, C_MISSES, C_FILLS, C_CPU, C_EVICT, C_BYTES, C_STREAMED,
@@ -231,4 +232,8 @@ hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, const float* P,
                           uint16_t* y, hipStream_t st, const HostSignal* wait = nullptr);
 int gemm_tile_m();
+// The per-GPU static scratch: its device address is looked up once per device
+// (setup: `device` current), then read back by static_scratch (null if not set up).
+hipError_t static_scratch_setup(int device);
+void* static_scratch(int device);
 }  // namespace ftmoe
