@@ -144,30 +144,25 @@ def decode_bench(args):
     n_gu, n_dn = tm.launches[M.FT_K_GEMV_GU], tm.launches[M.FT_K_GEMV_DOWN]
     ms_gu, ms_dn = tm.ms[M.FT_K_GEMV_GU], tm.ms[M.FT_K_GEMV_DOWN]
     experts = tm.gemv_experts
-    gu_gbs = experts * gu_bytes / (ms_gu / 1e3) / 1e9
-    dn_gbs = experts * dn_bytes / (ms_dn / 1e3) / 1e9
+    fused = n_dn == 0          # one launch per call: gate/up, SwiGLU and down together
     both_gbs = experts * (gu_bytes + dn_bytes) / ((ms_gu + ms_dn) / 1e3) / 1e9
-    kernel_key = "gemv_gateup_kernel<bf16,1>+gemv_down_kernel<bf16,1>"
+    gu_gbs = experts * gu_bytes / (ms_gu / 1e3) / 1e9
+    dn_gbs = experts * dn_bytes / (ms_dn / 1e3) / 1e9 if n_dn else None
+    kernel_key = "decode_kernel<bf16,all>" if fused else "gemv_gateup_kernel<bf16,1>+gemv_down_kernel<bf16,1>"
     traffic = measured_traffic(kernel_key)
     res = {
         "value": args.steps / elapsed,
         "ms_per_step": elapsed / args.steps * 1e3,
         "ms_per_step_kernel_timed_run": el2 / args.steps * 1e3,
-        # the decode expert GEMV of one layer call is two launches, gate/up
-        # (with SwiGLU) then down; the unit is the GPU-executed experts'
-        # records (G x S bytes), so achieved = their bytes / the pair's time
+        # the decode expert GEMV of one layer call: gate/up with SwiGLU, then
+        # down; the unit is the GPU-executed experts' records (G x S bytes),
+        # so achieved = their bytes / the time of the call's expert launch(es)
         "roofline": {
             "bound": "hbm", "kernel": kernel_key, "achieved": both_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": both_gbs / HBM_PEAK_GBS, "traffic": traffic,
             "bytes_per_launch": experts * (gu_bytes + dn_bytes) / max(n_gu, 1),
             "avg_launch_us": (ms_gu + ms_dn) / max(n_gu, 1) * 1e3, "launches": n_gu,
             "timing": "HIP events stamped by each launch on the caller's stream (kernel-timed run)",
-            "gateup": {"achieved": gu_gbs, "frac": gu_gbs / HBM_PEAK_GBS,
-                       "bytes_per_launch": experts * gu_bytes / max(n_gu, 1),
-                       "avg_launch_us": ms_gu / max(n_gu, 1) * 1e3},
-            "down": {"achieved": dn_gbs, "frac": dn_gbs / HBM_PEAK_GBS,
-                     "bytes_per_launch": experts * dn_bytes / max(n_gu, 1),
-                     "avg_launch_us": ms_dn / max(n_gu, 1) * 1e3},
         },
         "decode_kernels": {
             "gpu_experts_per_layer_step": experts / max(n_gu, 1),
@@ -184,8 +179,15 @@ def decode_bench(args):
             "host_threads_env": os.environ.get("FTMOE_HOST_THREADS", "default"),
         },
     }
-    log(f"decode: {res['value']:.1f} tok/s, {res['ms_per_step']:.2f} ms/step, gate/up GEMV {gu_gbs:.0f} GB/s "
-        f"({gu_gbs / HBM_PEAK_GBS:.1%}), pair {both_gbs:.0f} GB/s, miss rate {res['cache']['miss_rate']:.2f}, "
+    if not fused:
+        res["roofline"]["gateup"] = {"achieved": gu_gbs, "frac": gu_gbs / HBM_PEAK_GBS,
+                                     "bytes_per_launch": experts * gu_bytes / max(n_gu, 1),
+                                     "avg_launch_us": ms_gu / max(n_gu, 1) * 1e3}
+        res["roofline"]["down"] = {"achieved": dn_gbs, "frac": dn_gbs / HBM_PEAK_GBS,
+                                   "bytes_per_launch": experts * dn_bytes / max(n_gu, 1),
+                                   "avg_launch_us": ms_dn / max(n_gu, 1) * 1e3}
+    log(f"decode: {res['value']:.1f} tok/s, {res['ms_per_step']:.2f} ms/step, expert kernels {both_gbs:.0f} GB/s "
+        f"({both_gbs / HBM_PEAK_GBS:.1%}, {res['roofline']['avg_launch_us']:.2f} us per call), miss rate {res['cache']['miss_rate']:.2f}, "
         f"fill {res['branches']['fill_gbs']:.1f} GB/s, host {res['branches']['host_gbs']:.1f} GB/s "
         f"({delta['host_seconds']:.2f}s busy of {el2:.2f}s in the kernel-timed run)")
     # (3) hits only: the last step replayed on the warm cache with fills off
@@ -208,16 +210,16 @@ def decode_bench(args):
     # back to the configured profile (ft_cache_profile keeps the cache's max_fetch)
     M.ft_cache_set_profile(h, M.profile(cfg.bp_mbps, cfg.bh_mbps, cfg.max_fetch))
     hx = th.gemv_experts
+    ms_h = th.ms[M.FT_K_GEMV_GU] + th.ms[M.FT_K_GEMV_DOWN]
     res["decode_kernels"]["hits_only"] = {
-        "gateup_gbs": hx * gu_bytes / (th.ms[M.FT_K_GEMV_GU] / 1e3) / 1e9,
-        "gateup_frac": hx * gu_bytes / (th.ms[M.FT_K_GEMV_GU] / 1e3) / 1e9 / HBM_PEAK_GBS,
-        "down_gbs": hx * dn_bytes / (th.ms[M.FT_K_GEMV_DOWN] / 1e3) / 1e9,
-        "avg_gateup_launch_us": th.ms[M.FT_K_GEMV_GU] / max(th.launches[M.FT_K_GEMV_GU], 1) * 1e3,
+        "expert_kernels_gbs": hx * (gu_bytes + dn_bytes) / (ms_h / 1e3) / 1e9,
+        "frac": hx * (gu_bytes + dn_bytes) / (ms_h / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "avg_us_per_call": ms_h / max(th.launches[M.FT_K_GEMV_GU], 1) * 1e3,
         "gpu_experts_per_layer_step": hx / max(th.launches[M.FT_K_GEMV_GU], 1),
         "launches": th.launches[M.FT_K_GEMV_GU], "fills": q1["fills"] - q0["fills"],
         "workload": f"decode step {steps - 1} replayed {args.hits_only_reps} times on the warm cache, max_fetch 0",
     }
-    log(f"decode hits only: gate/up GEMV {res['decode_kernels']['hits_only']['gateup_gbs']:.0f} GB/s, "
+    log(f"decode hits only: expert kernels {res['decode_kernels']['hits_only']['expert_kernels_gbs']:.0f} GB/s, "
         f"{res['decode_kernels']['hits_only']['gpu_experts_per_layer_step']:.2f} experts per launch")
     if not args.no_measured_profile:
         # the same decode run again from a cold cache, with q* fed by this machine's measured B_P / B_H

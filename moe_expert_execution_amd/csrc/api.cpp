@@ -139,6 +139,8 @@ hipError_t dalloc(T** p, size_t n) {
     return hipMalloc(reinterpret_cast<void**>(p), n * sizeof(T) + 256);
 }
 
+constexpr int64_t kDecodePartMaxBytes = 256ll << 20;   // partial outputs of the one-token decode kernel
+
 ft_status check_shape(const ft_shape* s) {
     FT_REQUIRE(s, "shape is null");
     FT_REQUIRE(s->layers >= 1, "layers must be >= 1");
@@ -161,7 +163,7 @@ void free_cache(ft_cache* c) {
                     c->dstate,
                     c->wl_counts, c->wl_slot, c->wl_src, c->plan.meta, c->plan.active_slot, c->plan.seg,
                     c->plan.perm, c->plan.route_pos, c->plan.tile_active, c->plan.tile_row0, c->plan.tile_first,
-                    c->plan.chunk_counts, c->H, c->Y, c->gv_part, c->bank_dev};
+                    c->plan.chunk_counts, c->H, c->Y, c->gv_part, c->bank_dev, c->dpart};
     for (void* b : bufs)
         if (b) (void)hipFree(b);
     hipEvent_t evs[] = {c->ev_ctrl, c->ev_fwd, c->ev_host, c->ev_xlast, c->ev_fence,
@@ -247,6 +249,8 @@ ft_status forward_cached(ft_cache* c, ft_cache* bufs, int32_t layer, const uint1
                          const float* w, int32_t T, uint16_t* y, hipStream_t st, bool capturing) {
     const int k = c->sh.top_k;
     const bool gemv = T <= kGemvMaxTokens;
+    // one token: the one-launch decode kernel (gate/up, SwiGLU, down partials)
+    const bool fused = T == 1 && bufs->dpart != nullptr;
     if ((int64_t)T * k > kSmallPlanRoutes && c->N > kLargeKeySpace) {
         set_error("a CACHED call of more than %d routes needs num_slots <= %d (the chunked planner's key space)",
                   kSmallPlanRoutes, kLargeKeySpace);
@@ -268,8 +272,12 @@ ft_status forward_cached(ft_cache* c, ft_cache* bufs, int32_t layer, const uint1
     const bool plan_fill =
         c->fill_pending && (sig.mailbox || sig.gmbox) && (int64_t)T * k <= kSmallPlanRoutes;
     const TimedLaunch ftl = plan_fill ? timing_launch(c->timing, FT_K_FILL) : TimedLaunch();
+    // the hit experts' decode workgroups ride in that launch too, beside the
+    // pull (with kernel timing on they run in the decode launch, so that its
+    // events time every GPU expert)
+    const bool hits_in_fill = fused && plan_fill && !c->timing;
     FT_HIP(launch_plan(bufs, routes, T, -1, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, w, x, &hs, &sig,
-                       st, plan_fill ? &ftl : nullptr));
+                       st, plan_fill ? &ftl : nullptr, hits_in_fill));
     if (plan_fill) c->fill_pending = false;
     if (!sig.mailbox && !sig.gmbox) {
         FT_HIP(hipEventRecord(c->ev_fwd, st));
@@ -282,12 +290,16 @@ ft_status forward_cached(ft_cache* c, ft_cache* bufs, int32_t layer, const uint1
     ft_status fs = flush_fill(c, st);
     if (fs != FT_OK) return fs;
     if (c->xfer_pending) FT_HIP(hipStreamWaitEvent(st, c->ev_xlast, 0));
-    FT_HIP(gemv ? launch_gemv(bufs, x, T, st) : launch_gemm(bufs, x, T, st));
+    if (fused)
+        FT_HIP(launch_decode(bufs, x, routes, hits_in_fill ? DEC_FILLS : DEC_ALL, st));
+    else
+        FT_HIP(gemv ? launch_gemv(bufs, x, T, st) : launch_gemm(bufs, x, T, st));
     // the combine waits for the host branch's answer itself (a stream wait
     // packet costs ~4.5 us even when the answer is already there); with
     // a host function, the stream waits for its event
     if (!sig.mailbox && !sig.gmbox) FT_HIP(hipStreamWaitEvent(st, c->ev_host, 0));
-    FT_HIP(launch_combine(bufs, routes, w, T, hs.P, y, st, &sig));
+    FT_HIP(fused ? launch_combine_part(bufs, routes, w, hs.P, y, st, &sig)
+                 : launch_combine(bufs, routes, w, T, hs.P, y, st, &sig));
     return FT_OK;
 }
 
@@ -424,6 +436,9 @@ ft_status ft_cache_create_layers(const ft_shape* shape, const ft_profile* profil
     c->cap_gemv = std::min<int32_t>(max_tokens, kGemvMaxTokens) * shape->top_k;
     c->gv_kq = gemv_kparts(*shape);
     CK(dalloc(&c->gv_part, 2ll * c->gv_kq * c->cap_gemv * f));
+    // the one-token decode kernel's partial outputs (shapes it serves)
+    if (decode_fits(*shape) && (int64_t)decode_groups(*shape) * shape->top_k * d * 4 <= kDecodePartMaxBytes)
+        CK(dalloc(&c->dpart, (int64_t)decode_groups(*shape) * shape->top_k * d));
     // seconds of polls, each a PCIe read: far beyond any host call (a test
     // lowers it to force the time-out path)
     c->host_wait_polls = 1u << 22;
@@ -611,9 +626,16 @@ ft_status ft_moe_forward_noalloc(ft_cache* c, int32_t layer, const uint16_t* x, 
     v.plan.tile_first = reinterpret_cast<int32_t*>(take((R + 1) * sizeof(int32_t)));
     v.plan.chunk_counts = nullptr;            // the one-workgroup planner only (R <= 64)
     v.cap_gemv = (int32_t)R;
-    v.gv_part = reinterpret_cast<float*>(take(2ll * c->gv_kq * R * f * sizeof(float)));
-    v.H = reinterpret_cast<uint16_t*>(take(R * f * sizeof(uint16_t)));
-    v.Y = reinterpret_cast<uint16_t*>(take(R * d * sizeof(uint16_t)));
+    if (T == 1 && c->dpart) {        // the one-token decode kernel: its partial outputs only
+        v.dpart = reinterpret_cast<float*>(take((int64_t)decode_groups(c->sh) * R * d * sizeof(float)));
+        v.gv_part = nullptr;
+        v.H = v.Y = nullptr;
+    } else {                         // the two-kernel GEMV
+        v.dpart = nullptr;
+        v.gv_part = reinterpret_cast<float*>(take(2ll * c->gv_kq * R * f * sizeof(float)));
+        v.H = reinterpret_cast<uint16_t*>(take(R * f * sizeof(uint16_t)));
+        v.Y = reinterpret_cast<uint16_t*>(take(R * d * sizeof(uint16_t)));
+    }
     if (off > kStaticScratchBytes) {
         set_error("this call needs %zu bytes of scratch; the static scratch holds %zu", off, kStaticScratchBytes);
         return FT_ERR_UNSUPPORTED;

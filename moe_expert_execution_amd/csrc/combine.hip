@@ -37,23 +37,36 @@ __global__ void __launch_bounds__(kCombThreads)
     const int t = blockIdx.y;
     const int c = (blockIdx.x * kCombThreads + threadIdx.x) * 4;
     if (t >= T || c >= d) return;
+    // the token's route metadata first, then all its expert rows at once
+    // (a route not run on the GPU loads row 0 and adds nothing)
+    int rp[kMaxTopK], rv[kMaxTopK];
+    float wj[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) {
+            const int r = t * k + j;
+            rp[j] = route_pos[r];
+            rv[j] = routes[r];
+            wj[j] = w[r];
+        }
+    uint2 v[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) v[j] = *reinterpret_cast<const uint2*>(Y + (int64_t)(rp[j] > 0 ? rp[j] : 0) * d + c);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     bool host = false;
-    for (int j = 0; j < k; ++j) {
-        const int r = t * k + j;
-        const int p = route_pos[r];
-        if (p >= 0) {
-            const float wj = w[r];
-            const uint2 v = *reinterpret_cast<const uint2*>(Y + (int64_t)p * d + c);
-            acc.x = fmaf(wj, bf16lo(v.x), acc.x);
-            acc.y = fmaf(wj, bf16hi(v.x), acc.y);
-            acc.z = fmaf(wj, bf16lo(v.y), acc.z);
-            acc.w = fmaf(wj, bf16hi(v.y), acc.w);
-        } else {
-            const int rv = routes[r];
-            host |= (rv < 0 && rv >= -E);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) {
+            if (rp[j] >= 0) {
+                acc.x = fmaf(wj[j], bf16lo(v[j].x), acc.x);
+                acc.y = fmaf(wj[j], bf16hi(v[j].x), acc.y);
+                acc.z = fmaf(wj[j], bf16lo(v[j].y), acc.z);
+                acc.w = fmaf(wj[j], bf16hi(v[j].y), acc.w);
+            } else {
+                host |= (rv[j] < 0 && rv[j] >= -E);
+            }
         }
-    }
     if (P && host) {
         // pinned host memory written by the host workers: system-scope loads
         const float* p = P + (int64_t)t * d + c;
@@ -66,6 +79,95 @@ __global__ void __launch_bounds__(kCombThreads)
     o.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
     o.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
     *reinterpret_cast<uint2*>(y + (int64_t)t * d + c) = o;
+}
+
+// The one-token decode's combine (decode_wg.h): route j's expert output is
+// the sum of its G neuron groups' partial rows part[g][j][0..d).  A
+// workgroup covers 64 output columns: 16 column quads x 16 slices of the
+// groups; slice s sums groups s, s + 16, ... of every GPU route (weighted),
+// and the slices are added in order, so the result is deterministic.
+constexpr int kCPSlices = 16;
+__global__ void __launch_bounds__(kCombThreads)
+    combine_part_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ route_pos,
+                        const float* __restrict__ w, const float* __restrict__ part, const float* P, int k, int d,
+                        int G, int E, uint16_t* __restrict__ y, const uint64_t* done, const uint64_t* seq_dev,
+                        uint64_t seq, uint32_t limit, int32_t* errflag) {
+    __shared__ float4 red[kCPSlices][16];
+    const int quad = threadIdx.x & 15, sl = threadIdx.x >> 4;
+    const int c = blockIdx.x * 64 + quad * 4;
+    // every load at once: the routes' metadata, then all partial rows of this
+    // slice (whether a route ran on the GPU decides only what is added)
+    int rp[kMaxTopK], rv[kMaxTopK];
+    float wj[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) {
+            rp[j] = route_pos[j];
+            rv[j] = routes[j];
+            wj[j] = w[j];
+        }
+    float4 s[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) s[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int g = sl; g < G; g += kCPSlices) {
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if (j < k) {
+                const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)g * k + j) * d + c);
+                s[j].x += v.x;
+                s[j].y += v.y;
+                s[j].z += v.z;
+                s[j].w += v.w;
+            }
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool host = false;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) {
+            if (rp[j] >= 0) {
+                acc.x = fmaf(wj[j], s[j].x, acc.x);
+                acc.y = fmaf(wj[j], s[j].y, acc.y);
+                acc.z = fmaf(wj[j], s[j].z, acc.z);
+                acc.w = fmaf(wj[j], s[j].w, acc.w);
+            } else {
+                host |= (rv[j] < 0 && rv[j] >= -E);
+            }
+        }
+    red[sl][quad] = acc;
+    if (done && threadIdx.x == 0) {
+        const uint64_t n = seq_dev ? *seq_dev : seq;
+        for (uint32_t it = 0; __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < n; ++it) {
+            if (it >= limit) {
+                atomicOr(errflag, 8);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+    }
+    __syncthreads();
+    if (sl == 0) {
+        float4 t = red[0][quad];
+        for (int s2 = 1; s2 < kCPSlices; ++s2) {
+            const float4 v = red[s2][quad];
+            t.x += v.x;
+            t.y += v.y;
+            t.z += v.z;
+            t.w += v.w;
+        }
+        if (P && host) {
+            // pinned host memory written by the host workers: system-scope loads
+            const float* p = P + c;
+            t.x += __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            t.y += __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            t.z += __hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            t.w += __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16_rne(t.x) | ((uint32_t)f32_to_bf16_rne(t.y) << 16);
+        o.y = (uint32_t)f32_to_bf16_rne(t.z) | ((uint32_t)f32_to_bf16_rne(t.w) << 16);
+        *reinterpret_cast<uint2*>(y + c) = o;
+    }
 }
 
 }  // namespace
@@ -87,6 +189,25 @@ hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, in
     }
     hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, st, routes, c->plan.route_pos, w, c->Y, P, T,
                        c->sh.top_k, d, c->sh.experts, y, done, seq_dev, seq, c->host_wait_polls, c->errflag);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_part(ft_cache* c, const int32_t* routes, const float* w, const float* P, uint16_t* y,
+                               hipStream_t st, const HostSignal* wait) {
+    const int d = c->sh.d_model;
+    const uint64_t* done = nullptr;
+    const uint64_t* seq_dev = nullptr;
+    uint64_t seq = 0;
+    if (wait && wait->gmbox) {
+        done = wait->gmbox + 8;
+        seq_dev = wait->gseq_dev;
+    } else if (wait && wait->mailbox) {
+        done = wait->done_word;
+        seq = wait->seq;
+    }
+    hipLaunchKernelGGL(combine_part_kernel, dim3(d / 64), dim3(kCombThreads), 0, st, routes, c->plan.route_pos, w,
+                       c->dpart, P, c->sh.top_k, d, decode_groups(c->sh), c->sh.experts, y, done, seq_dev, seq,
+                       c->host_wait_polls, c->errflag);
     return hipGetLastError();
 }
 

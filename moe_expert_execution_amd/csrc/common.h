@@ -185,6 +185,8 @@ struct ft_cache {
     int32_t cap_gemv;          // rows served by the GEMV path
     int32_t gv_kq;             // K-parts of the gate/up GEMV
     float* gv_part;            // [2 x gv_kq x cap_gemv x f] fp32 K-part sums of g and u (GEMV path)
+    float* dpart;              // [groups x k x d] fp32 partial outputs of the one-token decode kernel
+                               // (null: one-token calls take the two-kernel GEMV path)
     // streams and events
     hipStream_t xfer;          // transfer stream (fills, full-layer loads)
     hipStream_t hstream;       // host-branch copies and host function
@@ -219,9 +221,12 @@ hipError_t launch_resize_gather(const uint8_t* old_pool, uint8_t* new_pool, int6
 // With `stage`, routes, w and x of the call are also copied into the host
 // branch's pinned staging.  With `fill` (R <= kSmallPlanRoutes only), the
 // pending fill runs in the same launch, timed by those events.
+// With `decode_hits` (and `fill`), the launch also runs the one-token decode
+// kernel's workgroups for the call's GPU routes whose slots are not being
+// filled (the filled ones follow in a launch of their own).
 hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, int work_counter,
                        const float* w, const uint16_t* x, const HostStaging* stage, const HostSignal* sig,
-                       hipStream_t st, const TimedLaunch* fill = nullptr);
+                       hipStream_t st, const TimedLaunch* fill = nullptr, bool decode_hits = false);
 hipError_t launch_gemv(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 int gemv_kparts(const ft_shape& s);
 hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
@@ -232,6 +237,14 @@ hipError_t launch_gemm(ft_cache* c, const uint16_t* x, int T, hipStream_t st);
 hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, int T, const float* P,
                           uint16_t* y, hipStream_t st, const HostSignal* wait = nullptr);
 int gemm_tile_m();
+enum { DEC_ALL = 0, DEC_HITS = 1, DEC_FILLS = 2 };   // the GPU routes a decode launch serves
+// The one-token decode kernel (one launch: gate/up, SwiGLU, down partials)
+// and its combine.  subset: DEC_ALL / DEC_HITS / DEC_FILLS (decode_wg.h).
+int decode_groups(const ft_shape& s);          // neuron groups (workgroups per route)
+bool decode_fits(const ft_shape& s);           // shapes the kernel serves
+hipError_t launch_decode(ft_cache* c, const uint16_t* x, const int32_t* routes, int subset, hipStream_t st);
+hipError_t launch_combine_part(ft_cache* c, const int32_t* routes, const float* w, const float* P, uint16_t* y,
+                               hipStream_t st, const HostSignal* wait);
 // The per-GPU static scratch: its device address is looked up once per device
 // (setup: `device` current), then read back by static_scratch (null if not set up).
 hipError_t static_scratch_setup(int device);

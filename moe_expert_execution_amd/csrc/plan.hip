@@ -17,6 +17,7 @@
 // More: three kernels over 64-token chunks — per-chunk slot masks and counts,
 // one scan, then rank = chunk offset + popcount(mask below the token).
 #include "common.h"
+#include "decode_wg.h"
 #include "fill.h"
 
 namespace ftmoe {
@@ -248,20 +249,41 @@ struct FillArgs {
 };
 constexpr int kPlanFillBlocks = 512;   // fill workgroups of kPlanThreads beside the planner: one 64 KiB chunk each for q <= 3 at decode sizes
 
-// The planner and the call's fill in one launch: workgroup 0 plans, the rest
-// pull the filled records.  Neither reads what the other writes (the plan
-// reads the routes, the fill the worklist; classify wrote both), and the
-// planner's few microseconds disappear under the PCIe pull.
-__global__ void __launch_bounds__(kPlanThreads) plan_fill_kernel(PlanArgs a, FillArgs f) {
+// The planner and the call's fill in one launch: workgroup 0 plans, the next
+// kPlanFillBlocks pull the filled records.  Neither reads what the other
+// writes (the plan reads the routes, the fill the worklist; classify wrote
+// both), and the planner's few microseconds disappear under the PCIe pull.
+// DECODE: the workgroups after them run the one-token decode kernel for the
+// GPU routes whose slots this call does not fill (hits), beside the pull; the
+// filled routes' workgroups follow in the next launch.
+constexpr int kDecFillWaves = kPlanThreads / 64;   // the decode workgroups use all 16 waves (fewer loads per lane)
+template <int FMT, bool DECODE>
+__global__ void __launch_bounds__(kPlanThreads) plan_fill_kernel(PlanArgs a, FillArgs f, DecodeArgs da) {
     if (blockIdx.x == 0) {
         plan_small(a);
         return;
     }
-    // 256 threads per workgroup pull, as in the fill kernel: a workgroup's
-    // host reads in flight set the PCIe rate
-    if (threadIdx.x < 256)
-        fill_records<256>(f.wl_counts, f.wl_slot, f.wl_src, f.banks, f.E, f.pool, f.S, f.P, blockIdx.x - 1,
-                          gridDim.x - 1);
+    if (blockIdx.x <= kPlanFillBlocks) {
+        // 256 threads per workgroup pull, as in the fill kernel: a workgroup's
+        // host reads in flight set the PCIe rate
+        if (threadIdx.x < 256)
+            fill_records<256>(f.wl_counts, f.wl_slot, f.wl_src, f.banks, f.E, f.pool, f.S, f.P, blockIdx.x - 1,
+                              kPlanFillBlocks);
+        return;
+    }
+    if constexpr (DECODE) {
+        extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+        decode_route_group<FMT, kDecFillWaves, DecodeShape<FMT>::BU16, DEC_HITS>(da, blockIdx.x - 1 - kPlanFillBlocks, xs);
+    }
+}
+
+template <int FMT, bool DECODE>
+void launch_plan_fill(const PlanArgs& a, const FillArgs& f, const DecodeArgs& da, const TimedLaunch* fill,
+                      hipStream_t st) {
+    const unsigned grid = 1 + kPlanFillBlocks + (DECODE ? (unsigned)(da.k * (da.f / DecodeShape<FMT>::NPW)) : 0u);
+    const size_t lds = DECODE ? decode_lds_bytes(da.d) : 0;
+    hipExtLaunchKernelGGL((plan_fill_kernel<FMT, DECODE>), dim3(grid), dim3(kPlanThreads), lds, st, fill->start,
+                          fill->stop, 0, a, f, da);
 }
 
 // ---- chunked planner (any R; key space <= 8192) --------------------------------
@@ -393,7 +415,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_scatter_kernel(PlanArgs a) 
 
 hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base, int bm, int work_counter,
                        const float* w, const uint16_t* x, const HostStaging* stage, const HostSignal* sig,
-                       hipStream_t st, const TimedLaunch* fill) {
+                       hipStream_t st, const TimedLaunch* fill, bool decode_hits) {
     PlanArgs a;
     a.seq_word = (sig && sig->mailbox) ? sig->seq_word : nullptr;
     a.seq = sig ? sig->seq : 0;
@@ -430,8 +452,14 @@ hipError_t launch_plan(ft_cache* c, const int32_t* routes, int T, int slot_base,
         if (a.R > kSmallPlanRoutes) return hipErrorInvalidValue;
         FillArgs f{c->wl_counts, c->wl_slot, c->wl_src, (const uint8_t* const*)c->bank_dev, (int)c->sh.experts,
                    c->pool, c->rl.S, c->rl.P};
-        hipExtLaunchKernelGGL(plan_fill_kernel, dim3(1 + kPlanFillBlocks), dim3(kPlanThreads), 0, st, fill->start,
-                              fill->stop, 0, a, f);
+        if (decode_hits && (T != 1 || !c->dpart)) return hipErrorInvalidValue;
+        const DecodeArgs da = decode_args(c, x, routes);
+        switch (decode_hits ? c->sh.fmt : -1) {
+            case FT_FMT_BF16: launch_plan_fill<FT_FMT_BF16, true>(a, f, da, fill, st); break;
+            case FT_FMT_FP8_B128: launch_plan_fill<FT_FMT_FP8_B128, true>(a, f, da, fill, st); break;
+            case FT_FMT_MXFP4_B32: launch_plan_fill<FT_FMT_MXFP4_B32, true>(a, f, da, fill, st); break;
+            default: launch_plan_fill<FT_FMT_BF16, false>(a, f, da, fill, st); break;
+        }
     } else if (a.R <= kSmallPlanRoutes) {
         hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
     } else {
