@@ -19,7 +19,7 @@ OUT = os.path.join(HERE, "libftmoe.so")
 BUILD = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-HIP_SOURCES = ["control.hip", "route.hip", "plan.hip", "gemv.hip", "gemm.hip", "combine.hip", "scratch.hip"]
+HIP_SOURCES = ["control.hip", "route.hip", "plan.hip", "gemv.hip", "gemm.hip", "combine.hip", "scratch.hip", "decode.hip"]
 HOST_SOURCES = ["api.cpp", "host_exec.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
           "-Wno-unused-variable"]

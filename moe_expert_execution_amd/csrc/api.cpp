@@ -437,7 +437,8 @@ ft_status ft_cache_create_layers(const ft_shape* shape, const ft_profile* profil
     c->gv_kq = gemv_kparts(*shape);
     CK(dalloc(&c->gv_part, 2ll * c->gv_kq * c->cap_gemv * f));
     // the one-token decode kernel's partial outputs (shapes it serves)
-    if (decode_fits(*shape) && (int64_t)decode_groups(*shape) * shape->top_k * d * 4 <= kDecodePartMaxBytes)
+    if (decode_fits(*shape) && decode_groups(*shape) <= 64 &&
+        (int64_t)decode_groups(*shape) * shape->top_k * d * 4 <= kDecodePartMaxBytes)
         CK(dalloc(&c->dpart, (int64_t)decode_groups(*shape) * shape->top_k * d));
     // seconds of polls, each a PCIe read: far beyond any host call (a test
     // lowers it to force the time-out path)

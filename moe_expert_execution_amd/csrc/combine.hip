@@ -84,9 +84,12 @@ __global__ void __launch_bounds__(kCombThreads)
 // The one-token decode's combine (decode_wg.h): route j's expert output is
 // the sum of its G neuron groups' partial rows part[g][j][0..d).  A
 // workgroup covers 64 output columns: 16 column quads x 16 slices of the
-// groups; slice s sums groups s, s + 16, ... of every GPU route (weighted),
-// and the slices are added in order, so the result is deterministic.
+// groups; slice s sums groups s, s + 16, ... (at most kCPMaxPerSlice) of
+// every GPU route, weighted, and the slices are added in order, so the result
+// is deterministic.  Every load is issued at once, and the wait for the host
+// branch's answer overlaps them; only the host partial is read after it.
 constexpr int kCPSlices = 16;
+constexpr int kCPMaxPerSlice = 4;       // groups per slice: G <= 64
 __global__ void __launch_bounds__(kCombThreads)
     combine_part_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ route_pos,
                         const float* __restrict__ w, const float* __restrict__ part, const float* P, int k, int d,
@@ -95,8 +98,11 @@ __global__ void __launch_bounds__(kCombThreads)
     __shared__ float4 red[kCPSlices][16];
     const int quad = threadIdx.x & 15, sl = threadIdx.x >> 4;
     const int c = blockIdx.x * 64 + quad * 4;
-    // every load at once: the routes' metadata, then all partial rows of this
-    // slice (whether a route ran on the GPU decides only what is added)
+    uint64_t want = 0, seen = ~0ull;
+    if (done && threadIdx.x == 0) {          // the first poll goes out with the loads
+        want = seq_dev ? *seq_dev : seq;
+        seen = __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
     int rp[kMaxTopK], rv[kMaxTopK];
     float wj[kMaxTopK];
 #pragma unroll
@@ -106,54 +112,59 @@ __global__ void __launch_bounds__(kCombThreads)
             rv[j] = routes[j];
             wj[j] = w[j];
         }
-    float4 s[kMaxTopK];
+    // partial rows of every route (a route not run on the GPU reads rows it
+    // does not add)
+    float4 v[kCPMaxPerSlice][kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) s[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int g = sl; g < G; g += kCPSlices) {
+    for (int i = 0; i < kCPMaxPerSlice; ++i)
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j)
-            if (j < k) {
-                const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)g * k + j) * d + c);
-                s[j].x += v.x;
-                s[j].y += v.y;
-                s[j].z += v.z;
-                s[j].w += v.w;
-            }
-    }
+        for (int j = 0; j < kMaxTopK; ++j) {
+            const int g = sl + i * kCPSlices;
+            v[i][j] = (j < k && g < G) ? *reinterpret_cast<const float4*>(part + ((int64_t)g * k + j) * d + c)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     bool host = false;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
         if (j < k) {
             if (rp[j] >= 0) {
-                acc.x = fmaf(wj[j], s[j].x, acc.x);
-                acc.y = fmaf(wj[j], s[j].y, acc.y);
-                acc.z = fmaf(wj[j], s[j].z, acc.z);
-                acc.w = fmaf(wj[j], s[j].w, acc.w);
+                float4 s = v[0][j];
+#pragma unroll
+                for (int i = 1; i < kCPMaxPerSlice; ++i) {
+                    s.x += v[i][j].x;
+                    s.y += v[i][j].y;
+                    s.z += v[i][j].z;
+                    s.w += v[i][j].w;
+                }
+                acc.x = fmaf(wj[j], s.x, acc.x);
+                acc.y = fmaf(wj[j], s.y, acc.y);
+                acc.z = fmaf(wj[j], s.z, acc.z);
+                acc.w = fmaf(wj[j], s.w, acc.w);
             } else {
                 host |= (rv[j] < 0 && rv[j] >= -E);
             }
         }
     red[sl][quad] = acc;
     if (done && threadIdx.x == 0) {
-        const uint64_t n = seq_dev ? *seq_dev : seq;
-        for (uint32_t it = 0; __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < n; ++it) {
+        for (uint32_t it = 0; seen < want; ++it) {
             if (it >= limit) {
                 atomicOr(errflag, 8);
                 break;
             }
             __builtin_amdgcn_s_sleep(8);
+            seen = __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
     __syncthreads();
     if (sl == 0) {
         float4 t = red[0][quad];
         for (int s2 = 1; s2 < kCPSlices; ++s2) {
-            const float4 v = red[s2][quad];
-            t.x += v.x;
-            t.y += v.y;
-            t.z += v.z;
-            t.w += v.w;
+            const float4 u = red[s2][quad];
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
         }
         if (P && host) {
             // pinned host memory written by the host workers: system-scope loads
