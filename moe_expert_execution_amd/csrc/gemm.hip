@@ -359,8 +359,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) h[j] = silu(acc[mi][0][4 * q + j]) * acc[mi][1][4 * q + j];
                     uint2 o;
-                    o.x = (uint32_t)f32_to_bf16_rne(h[0]) | ((uint32_t)f32_to_bf16_rne(h[1]) << 16);
-                    o.y = (uint32_t)f32_to_bf16_rne(h[2]) | ((uint32_t)f32_to_bf16_rne(h[3]) << 16);
+                    o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{h[0], h[1]}, bf16x2_t));
+                    o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{h[2], h[3]}, bf16x2_t));
                     *reinterpret_cast<uint2*>(&Hs[(mi * 32 + m) * LDH + 32 * w + 8 * q + 4 * g]) = o;
                 }
             __syncthreads();
@@ -385,10 +385,10 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(GemmArgs a) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         uint2 o;
-                        o.x = (uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q]) |
-                              ((uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 1]) << 16);
-                        o.y = (uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 2]) |
-                              ((uint32_t)f32_to_bf16_rne(acc[mi][ni][4 * q + 3]) << 16);
+                        o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                  f32x2_t{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]}, bf16x2_t));
+                        o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                  f32x2_t{acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]}, bf16x2_t));
                         *reinterpret_cast<uint2*>(&Ys[m * LDY + 32 * ni + 8 * q + 4 * g]) = o;
                     }
                 // the wave reads back what it wrote (LDS operations of a wave stay in order)
