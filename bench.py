@@ -36,18 +36,20 @@ def log(*a):
 
 
 def kernel_source_sha():
+    """Hash of the sources that define the one-token decode kernel."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemv.hip", "wfmt.h"):
+    for f in ("decode.hip", "decode_wg.h", "wfmt.h"):
         with open(os.path.join(ROOT, "moe_expert_execution_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "gemv_traffic.json")
+    """The committed rocprofv3 counter summary of the decode kernel (HBM bytes
+    per launch, and their ratio to the algorithmic bytes of the same run), if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     try:
         with open(path) as fh:
             d = json.load(fh)
@@ -55,7 +57,7 @@ def measured_traffic(kernel_key):
         return None
     if d.get("source_sha") != kernel_source_sha() or d.get("kernel") != kernel_key:
         return None
-    return d.get("traffic_bytes_per_launch")
+    return d
 
 
 def time_route(M, shp, x, wr, T, ids, w, stream, reps=10):
@@ -159,7 +161,9 @@ def decode_bench(args):
         # so achieved = their bytes / the time of the call's expert launch(es)
         "roofline": {
             "bound": "hbm", "kernel": kernel_key, "achieved": both_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": both_gbs / HBM_PEAK_GBS, "traffic": traffic,
+            "frac": both_gbs / HBM_PEAK_GBS, "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+            # the counters' run has its own experts per launch: their ratio to that run's algorithmic bytes
+            "traffic_over_algorithmic": traffic["traffic_over_algorithmic"] if traffic else None,
             "bytes_per_launch": experts * (gu_bytes + dn_bytes) / max(n_gu, 1),
             "avg_launch_us": (ms_gu + ms_dn) / max(n_gu, 1) * 1e3, "launches": n_gu,
             "timing": "HIP events stamped by each launch on the caller's stream (kernel-timed run)",
@@ -539,10 +543,13 @@ def formats_bench(args):
         ex = tm.gemv_experts / n
         gu_us = tm.ms[M.FT_K_GEMV_GU] / n * 1e3
         dn_us = tm.ms[M.FT_K_GEMV_DOWN] / n * 1e3
+        # one launch per call (gate/up, SwiGLU and down) unless down launches too
+        fused = tm.launches[M.FT_K_GEMV_DOWN] == 0
+        pair_gbs = ex * (gu_b + dn_b) / (gu_us + dn_us) / 1e3
         res["gemv_T1"] = {"experts_per_launch": ex,
-                          "gateup_us": gu_us, "gateup_gbs": ex * gu_b / gu_us / 1e3,
-                          "gateup_frac": ex * gu_b / gu_us / 1e3 / HBM_PEAK_GBS,
-                          "down_us": dn_us, "down_gbs": ex * dn_b / dn_us / 1e3}
+                          "kernel": "decode_kernel (gate/up, SwiGLU, down in one launch)" if fused else
+                                    "gate/up GEMV + down GEMV",
+                          "us_per_call": gu_us + dn_us, "pair_gbs": pair_gbs, "pair_frac": pair_gbs / HBM_PEAK_GBS}
         M.ft_cache_set_timing(h, False)
         # grouped GEMM
         for T in Ts:
@@ -575,8 +582,8 @@ def formats_bench(args):
             M.ft_cache_set_timing(h, False)
         st = M.ft_cache_stats(h)
         assert st.error_flags == 0
-        log(f"{name}: GEMV T=1 gate/up {res['gemv_T1']['gateup_gbs']:.0f} GB/s "
-            f"({res['gemv_T1']['gateup_frac']:.1%}), " +
+        log(f"{name}: T=1 expert kernel(s) {res['gemv_T1']['pair_gbs']:.0f} GB/s "
+            f"({res['gemv_T1']['pair_frac']:.1%}, {res['gemv_T1']['us_per_call']:.1f} us per call), " +
             ", ".join(f"GEMM T={T} {res[f'gemm_T{T}']['tflops']:.0f} TFLOP/s / {res[f'gemm_T{T}']['weight_gbs']:.0f}"
                       f" GB/s ({res[f'gemm_T{T}']['roofline_frac']:.1%} of roofline time)" for T in Ts))
         out[name] = res
@@ -704,9 +711,11 @@ def _kernel_figures(M, tm, fmt, d, f, calls):
         ms = tm.ms[M.FT_K_GEMV_GU] + tm.ms[M.FT_K_GEMV_DOWN]
         by = tm.gemv_experts * (gu_b + dn_b)
         out["gemv"] = {"experts_per_call": tm.gemv_experts / n_gu,
-                       "gateup_gbs": tm.gemv_experts * gu_b / (tm.ms[M.FT_K_GEMV_GU] / 1e3) / 1e9,
                        "pair_gbs": by / (ms / 1e3) / 1e9, "pair_frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                       "pair_us_per_call": ms / n_gu * 1e3}
+                       "pair_us_per_call": ms / n_gu * 1e3,
+                       "launches_per_call": 1 if tm.launches[M.FT_K_GEMV_DOWN] == 0 else 2}
+        if tm.launches[M.FT_K_GEMV_DOWN]:
+            out["gemv"]["gateup_gbs"] = tm.gemv_experts * gu_b / (tm.ms[M.FT_K_GEMV_GU] / 1e3) / 1e9
     n_gm = tm.launches[M.FT_K_GEMM_GU]
     if n_gm:
         ms = tm.ms[M.FT_K_GEMM_GU] + tm.ms[M.FT_K_GEMM_DOWN]
