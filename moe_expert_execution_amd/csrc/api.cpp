@@ -576,8 +576,16 @@ ft_status ft_moe_forward(ft_cache* c, int32_t layer, int32_t mode, const uint16_
     FT_HIP(hipStreamWaitEvent(st, c->ready[b], 0));
     FT_HIP(launch_plan(c, routes, T, b * E, gemm_tile_m(), gemv ? C_GEMV_EXPERTS : C_GEMM_EXPERTS, w, x, nullptr,
                        nullptr, st));
-    FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
-    FT_HIP(launch_combine(c, routes, w, T, nullptr, y, st));
+    if (T == 1 && c->dpart) {
+        // one token: the decode kernel over the buffer's records, then the
+        // combine of its partial outputs (the planner's route positions
+        // tell which routes it ran)
+        FT_HIP(launch_decode(c, x, routes, DEC_ALL, st, (int)(b * E)));
+        FT_HIP(launch_combine_part(c, routes, w, nullptr, y, st, nullptr));
+    } else {
+        FT_HIP(gemv ? launch_gemv(c, x, T, st) : launch_gemm(c, x, T, st));
+        FT_HIP(launch_combine(c, routes, w, T, nullptr, y, st));
+    }
     if (mode & FT_WARM_DECODE) FT_HIP(launch_register(c, layer, b, st));
     FT_HIP(hipEventRecord(c->release[b], st));
     c->release_recorded[b] = true;

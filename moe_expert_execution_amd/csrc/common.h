@@ -239,10 +239,13 @@ hipError_t launch_combine(ft_cache* c, const int32_t* routes, const float* w, in
 int gemm_tile_m();
 enum { DEC_ALL = 0, DEC_HITS = 1, DEC_FILLS = 2 };   // the GPU routes a decode launch serves
 // The one-token decode kernel (one launch: gate/up, SwiGLU, down partials)
-// and its combine.  subset: DEC_ALL / DEC_HITS / DEC_FILLS (decode_wg.h).
+// and its combine.  subset: DEC_ALL / DEC_HITS / DEC_FILLS (decode_wg.h);
+// slot_base < 0: routes are classify's slot ids, else expert ids of the
+// full-layer buffer starting at that slot (STREAMED, subset DEC_ALL).
 int decode_groups(const ft_shape& s);          // neuron groups (workgroups per route)
 bool decode_fits(const ft_shape& s);           // shapes the kernel serves
-hipError_t launch_decode(ft_cache* c, const uint16_t* x, const int32_t* routes, int subset, hipStream_t st);
+hipError_t launch_decode(ft_cache* c, const uint16_t* x, const int32_t* routes, int subset, hipStream_t st,
+                         int slot_base = -1);
 hipError_t launch_combine_part(ft_cache* c, const int32_t* routes, const float* w, const float* P, uint16_t* y,
                                hipStream_t st, const HostSignal* wait);
 // The per-GPU static scratch: its device address is looked up once per device

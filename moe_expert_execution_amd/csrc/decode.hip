@@ -43,8 +43,10 @@ int decode_groups(const ft_shape& s) {
 
 bool decode_fits(const ft_shape& s) { return s.d_model <= kDecodeMaxD; }
 
-DecodeArgs decode_args(const ft_cache* c, const uint16_t* x, const int32_t* routes) {
+DecodeArgs decode_args(const ft_cache* c, const uint16_t* x, const int32_t* routes, int slot_base) {
     DecodeArgs a;
+    a.slot_base = slot_base;
+    a.E = c->sh.experts;
     a.x = x;
     a.routes = routes;
     a.wl_counts = c->wl_counts;
@@ -65,8 +67,9 @@ DecodeArgs decode_args(const ft_cache* c, const uint16_t* x, const int32_t* rout
     return a;
 }
 
-hipError_t launch_decode(ft_cache* c, const uint16_t* x, const int32_t* routes, int subset, hipStream_t st) {
-    const DecodeArgs a = decode_args(c, x, routes);
+hipError_t launch_decode(ft_cache* c, const uint16_t* x, const int32_t* routes, int subset, hipStream_t st,
+                         int slot_base) {
+    const DecodeArgs a = decode_args(c, x, routes, slot_base);
     switch (c->sh.fmt) {
         case FT_FMT_BF16: return launch_fmt<FT_FMT_BF16>(a, subset, c->timing, st);
         case FT_FMT_FP8_B128: return launch_fmt<FT_FMT_FP8_B128>(a, subset, c->timing, st);

@@ -51,18 +51,22 @@ struct DecodeShape {
 
 struct DecodeArgs {
     const uint16_t* x;          // [d] bf16, the call's one token
-    const int32_t* routes;      // [k] rewritten by classify: slot, or negative (host run, invalid)
+    const int32_t* routes;      // [k] slot ids rewritten by classify (negative: host run, invalid), or expert ids
     const int32_t* wl_counts;   // [4] of the call's classify: q = wl_counts[3]
     const int32_t* wl_slot;     // [>= k] victim slots of the call's fills
     const uint8_t* pool;
     int64_t S;                  // slot stride of the pool (bytes)
     int64_t off_gate, off_up, off_down, off_sg, off_su, off_sd;
     int k, d, f, N;
+    int E;
+    int slot_base;              // < 0: routes are slot ids (CACHED); else expert ids in buffer slot_base + e (STREAMED)
     float* part;                // [f / NPW][k][d] fp32 partial outputs
 };
 
-// The arguments for a cache's pool, x and rewritten routes (decode.hip).
-DecodeArgs decode_args(const ft_cache* c, const uint16_t* x, const int32_t* routes);
+// The arguments for a cache's pool, x and routes (decode.hip): slot ids
+// rewritten by classify (slot_base < 0), or expert ids of the full-layer
+// buffer whose first slot is slot_base.
+DecodeArgs decode_args(const ft_cache* c, const uint16_t* x, const int32_t* routes, int slot_base = -1);
 
 namespace dec {
 
@@ -153,9 +157,10 @@ __device__ __forceinline__ void decode_route_group(const DecodeArgs& a, int item
         const int c = tid + i * NT;
         if (c < (d >> 3)) xr[i] = *reinterpret_cast<const u32x4_t*>(a.x + 8 * c);
     }
-    const int slot = __shfl(rl, j, 64);
+    const int rj = __shfl(rl, j, 64);
+    const int slot = a.slot_base < 0 ? rj : (rj >= 0 && rj < a.E ? a.slot_base + rj : -1);
     // a repeated expert of the token is computed once (the planner drops the repeat)
-    bool ok = slot >= 0 && slot < a.N && __ballot(lane < j && rl == slot) == 0;
+    bool ok = slot >= 0 && slot < a.N && __ballot(lane < j && rl == rj) == 0;
     if constexpr (SUBSET != DEC_ALL) {
         const bool filled = __ballot(lane < q && ws == slot) != 0;
         ok = ok && (SUBSET == DEC_FILLS ? filled : !filled);

@@ -96,6 +96,47 @@ def test_prefill_streamed_bf16():
 
 
 @gpu
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_streamed_one_token(fmt):
+    """One-token calls in STREAMED mode run the one-launch decode kernel over
+    the full-layer buffer (slot = buffer base + expert id): three layers, so
+    both buffers, with and without prefetch; every output against the oracle,
+    and the last call's kernel timing shows one expert launch and no down
+    launch."""
+    cuda()
+    cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=512, f=256, E=8, k=2, layers=3, slots=16, cfg_id=97)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(cfg.layers, cfg.E, cfg.k, cfg.d, cfg.f, fmt, bank.ptr, cfg.slots, 4, cfg.bp_mbps, cfg.bh_mbps)
+    st = torch.cuda.current_stream().cuda_stream
+    try:
+        for l in range(cfg.layers):
+            ex = expert_fn(recs, cfg, l, maxsize=cfg.E)
+            wr = synth.router(cfg, l)
+            for t in range(3):
+                x = synth.tokens(cfg, 1, 900 + 10 * l + t)
+                ids, w, _ = OR.route(x, wr, cfg.k)
+                xd, idd, wd = dev_u16(x), dev(ids.astype(np.int32)), dev(w.astype(np.float32))
+                y = torch.zeros((1, cfg.d), dtype=torch.int16, device="cuda")
+                last = l == cfg.layers - 1 and t == 2
+                if last:
+                    M.ft_cache_set_timing(sc.handle, True)
+                flags = M.FT_PREFETCH_NEXT if t == 2 else 0
+                M.ft_moe_forward(sc.handle, l, M.FT_MODE_STREAMED | flags, xd.data_ptr(), idd.data_ptr(),
+                                 wd.data_ptr(), 1, y.data_ptr(), st)
+                torch.cuda.synchronize()
+                assert_close_rel(bf16_bits_to_f64(y), oracle_rows(x, ids, w, ex, np.arange(1)), TOL[fmt],
+                                 f"{fmt} layer {l} token {t}")
+        tm = M.ft_cache_timing(sc.handle)
+        assert tm.launches[M.FT_K_GEMV_GU] == 1 and tm.launches[M.FT_K_GEMV_DOWN] == 0
+        s = M.ft_cache_stats(sc.handle)
+        assert s.error_flags == 0 and s.layers_streamed >= cfg.layers
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
 def test_prefill_streamed_single_buffer():
     """The one-buffer ablation: three layers through buffer 0 alone on a cache
     of exactly E slots (T = 300, every row against the oracle); the double
