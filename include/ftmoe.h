@@ -318,9 +318,11 @@ ft_status ft_moe_forward(ft_cache* cache, int32_t layer, int32_t mode, const uin
  * ft_moe_forward_noalloc — ft_moe_forward in FT_MODE_CACHED for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid it): the same computation and results, with
- * the call's scratch (planner lists, GEMV K-part sums, h, expert outputs)
- * taken from one static device array of 16 MiB per GPU instead of the
- * cache's buffers; the call allocates and frees nothing.
+ * the call's scratch (planner lists; at one token the decode kernel's
+ * partial outputs, (f/32) k d fp32 ((f/64) for MXFP4); at 2 to 4 tokens the
+ * GEMV K-part sums, h and expert outputs) taken from one static device array
+ * of 16 MiB per GPU instead of the cache's buffers; the call allocates and
+ * frees nothing.
  * Arguments, ordering and errors are those of ft_moe_forward with mode
  * FT_MODE_CACHED, plus: calls of more than 4 tokens, or whose scratch would
  * exceed the 16 MiB (about 2 kq T k f 4 + T k (f + d) 2 bytes, kq <= 8),
@@ -383,7 +385,9 @@ ft_status ft_cache_stats(const ft_cache* cache, ft_stats* out);
  * ft_moe_forward brackets its expert kernels, and every fill launch its
  * kernel, with HIP events on the stream the kernel runs on;
  * ft_cache_timing synchronises and returns, per kernel class (0 GEMV gate/up,
- * 1 GEMV down, 2 GEMM gate/up, 3 GEMM down, 4 fill), the number of launches
+ * or at one token the decode kernel doing gate/up, SwiGLU and down in one
+ * launch; 1 GEMV down, none at one token; 2 GEMM gate/up, 3 GEMM down,
+ * 4 fill), the number of launches
  * and their summed event durations, plus device-side counts of the work those
  * launches did: expert records read (one per active slot per call) and GPU
  * rows (routes) computed. */
