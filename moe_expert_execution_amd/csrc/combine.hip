@@ -98,20 +98,6 @@ __global__ void __launch_bounds__(kCombThreads)
     __shared__ float4 red[kCPSlices][16];
     const int quad = threadIdx.x & 15, sl = threadIdx.x >> 4;
     const int c = blockIdx.x * 64 + quad * 4;
-    uint64_t want = 0, seen = ~0ull;
-    if (done && threadIdx.x == 0) {          // the first poll goes out with the loads
-        want = seq_dev ? *seq_dev : seq;
-        seen = __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    int rp[kMaxTopK], rv[kMaxTopK];
-    float wj[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-        if (j < k) {
-            rp[j] = route_pos[j];
-            rv[j] = routes[j];
-            wj[j] = w[j];
-        }
     // partial rows of every route (a route not run on the GPU reads rows it
     // does not add)
     float4 v[kCPMaxPerSlice][kMaxTopK];
@@ -123,6 +109,28 @@ __global__ void __launch_bounds__(kCombThreads)
             v[i][j] = (j < k && g < G) ? *reinterpret_cast<const float4*>(part + ((int64_t)g * k + j) * d + c)
                                        : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    // the route metadata, issued behind the partial rows so that one round
+    // trip covers both: lane j of each wave loads route j's, then every route's values are broadcast from their lane
+    const int lane = threadIdx.x & 63;
+    const int rpl = lane < k ? route_pos[lane] : -1;
+    const int rvl = lane < k ? routes[lane] : INT32_MIN;
+    const int wl = lane < k ? __float_as_int(w[lane]) : 0;
+    int rp[kMaxTopK], rv[kMaxTopK];
+    float wj[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        rp[j] = __builtin_amdgcn_readlane(rpl, j);
+        rv[j] = __builtin_amdgcn_readlane(rvl, j);
+        wj[j] = __int_as_float(__builtin_amdgcn_readlane(wl, j));
+    }
+    // the first poll of the host's answer goes out behind the loads; polls are
+    // relaxed, and one acquire follows once the number is seen (a system-scope
+    // acquire invalidates L2 on this part, so it must not sit before the loads)
+    uint64_t want = 0, seen = ~0ull;
+    if (done && threadIdx.x == 0) {
+        want = seq_dev ? *seq_dev : seq;
+        seen = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     bool host = false;
 #pragma unroll
@@ -153,8 +161,12 @@ __global__ void __launch_bounds__(kCombThreads)
                 break;
             }
             __builtin_amdgcn_s_sleep(8);
-            seen = __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
+            seen = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
+        // synchronise with the host's release of its number: the host partial
+        // sums it wrote before are visible after this (read below only when the
+        // call has host experts)
+        if (P && host) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
     }
     __syncthreads();
     if (sl == 0) {
