@@ -256,6 +256,79 @@ def test_layer_at_the_size_limits(fmt, d, f):
 
 
 @gpu
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("d", [8192, 8320])
+def test_one_token_width_boundary(fmt, d):
+    """d = 8,192 is the widest token the one-launch decode kernel stages in
+    LDS; d = 8,320 takes the two-launch GEMV.  CACHED one-token calls with
+    hits, fills and host experts, every output against the oracle; the last
+    call's kernel timing shows which path ran (one expert launch and no down
+    launch, or a gate/up launch and the down side's)."""
+    cuda()
+    cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=d, f=256, E=8, k=2, slots=4, cfg_id=98)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, fmt, bank.ptr, cfg.slots, 1, cfg.bp_mbps, cfg.bh_mbps)
+    sim = OC.SlotCacheSim(1, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+    try:
+        ex = expert_fn(recs, cfg, 0, maxsize=cfg.E)
+        wr = synth.router(cfg, 0)
+        classes = set()
+        for t in range(8):
+            x = synth.tokens(cfg, 1, 700 + t)
+            ids, w, _ = OR.route(x, wr, cfg.k)
+            r = sim.classify(0, ids)
+            classes |= set(r.cls)
+            if t == 7:
+                M.ft_cache_set_timing(sc.handle, True)
+            y, routes = run_cached(sc, 0, x, ids, w)
+            assert np.array_equal(routes, r.routes)
+            assert_close_rel(y, oracle_rows(x, ids, w, ex, np.arange(1)), TOL[fmt], f"{fmt} d {d} token {t}")
+        assert classes == {OC.HIT, OC.FILL, OC.CPU}, classes
+        tm = M.ft_cache_timing(sc.handle)
+        if d <= 8192:
+            assert tm.launches[M.FT_K_GEMV_GU] == 1 and tm.launches[M.FT_K_GEMV_DOWN] == 0
+        else:   # with its K split in parts, the down side is a SwiGLU launch and the down launch
+            assert tm.launches[M.FT_K_GEMV_GU] == 1 and tm.launches[M.FT_K_GEMV_DOWN] >= 1
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_top16_layer(fmt):
+    """The largest top-k (16): E = 32 over 24 slots, so calls mix hits, fills
+    and host experts; T = 1 (one-launch decode kernel and its combine),
+    T = 3 (GEMV), T = 40 (grouped GEMM).  Routes as classify rewrote them
+    against the simulator, every output row against the oracle."""
+    cuda()
+    cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=256, f=256, E=32, k=16, slots=24, cfg_id=99)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, fmt, bank.ptr, cfg.slots, 40, cfg.bp_mbps, cfg.bh_mbps)
+    sim = OC.SlotCacheSim(1, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps)
+    try:
+        ex = expert_fn(recs, cfg, 0, maxsize=cfg.E)
+        wr = synth.router(cfg, 0)
+        classes = set()
+        for i, T in enumerate((1, 1, 3, 40, 1, 3, 40, 1)):
+            x = synth.tokens(cfg, T, 600 + i)
+            ids, w, _ = OR.route(x, wr, cfg.k)
+            r = sim.classify(0, ids)
+            classes |= set(r.cls)
+            y, routes = run_cached(sc, 0, x, ids, w)
+            assert np.array_equal(routes, r.routes)
+            assert_close_rel(y, oracle_rows(x, ids, w, ex, np.arange(T)), TOL[fmt], f"{fmt} call {i} T {T}")
+        assert classes == {OC.HIT, OC.FILL, OC.CPU}, classes
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
 @pytest.mark.parametrize("T,k", [(128, 8), (129, 8), (6, 1), (300, 1)])
 def test_planner_boundary_and_top1(T, k):
     """T * k = 1,024 routes is the largest call of the one-workgroup planner

@@ -45,7 +45,9 @@ def test_route_tiny_bit_exact():
     # general kernel at E = 200; d off a multiple of 128; a single expert
     ("tiny", 1, 5, 2, None), ("tiny", 7, 12, 3, None), ("fp8", 1, None, None, None),
     ("mxfp4", 16, None, None, None), ("decode", 17, 200, 6, None), ("tiny", 3, 24, 4, 200),
-    ("tiny", 33, 60, 5, 72), ("tiny", 4, 1, 1, None)])
+    ("tiny", 33, 60, 5, 72), ("tiny", 4, 1, 1, None),
+    # the largest top-k (16): one token, the small-T path, the matrix cores
+    ("decode", 1, None, 16, None), ("tiny", 9, 32, 16, None), ("decode", 40, None, 16, None)])
 def test_route_shapes_bit_exact(cfgname, T, E, k, d):
     """Routing ids bit-exact and weights to fp32 rounding against the oracle, for
     the small-T paths (one token, 16-byte router rows when E % 8 == 0; up to 16
