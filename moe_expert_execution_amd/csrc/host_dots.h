@@ -6,7 +6,8 @@
 // Panel order: rows 32p..32p+31 of a [rows x K] matrix form one contiguous
 // block; inside it the 16-byte unit c of row r sits at unit (c/2)*64 +
 // (c%2)*32 + r%32.  So the 16 rows [32p + 16h, +16) at chunk column c are
-// 256 contiguous bytes: a worker that owns a half panel streams 256-byte runs.
+// 256 contiguous bytes, and a panel's lane block (chunk columns 2i, 2i + 1)
+// is 1 KiB.
 #pragma once
 #include <immintrin.h>
 #include <stdint.h>
@@ -129,6 +130,67 @@ inline void half_panel_dots_stream(int fmt, const uint8_t* rec, int64_t off, int
         }
         for (int i = 0; i < NT; ++i)
             for (int j = 0; j < 8; ++j) out[i * 16 + r0 + j] = _mm512_reduce_add_ps(a[j][i]);
+    }
+}
+
+// One vector, a whole panel: out[r] = row 32p + r of the matrix dotted with
+// x, r < 32.  Every lane block is read front to back: bf16 in one pass with
+// two rows per accumulator (16 of them), block-FP8 and MXFP4 in two passes
+// of 16 rows (the halves), one row per accumulator.  For each row the
+// multiply-adds run in the order of half_panel_dots_stream<1>, so the sums
+// are the same numbers; what changes is that a 1 KiB lane block is read in
+// one or two passes instead of four.
+inline void panel_dots_1(int fmt, const uint8_t* rec, int64_t off, int64_t soff, int p, int K, const float* x,
+                         float* out) {
+    if (fmt == FMT_BF16) {
+        const uint8_t* base = half_panel_base(fmt, rec, off, p, 0, K);
+        __m512 a[16];
+        for (int q = 0; q < 16; ++q) a[q] = _mm512_setzero_ps();
+        for (int c = 0; c < K / 8; ++c) {
+            const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+            const __m512 xv = _mm512_broadcast_f32x8(_mm256_loadu_ps(x + 8 * c));
+            for (int q = 0; q < 16; ++q) {      // rows 2q, 2q + 1
+                const __m256i w16 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(u + 32 * q));
+                const __m512 w = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(w16), 16));
+                a[q] = _mm512_fmadd_ps(w, xv, a[q]);
+            }
+        }
+        for (int q = 0; q < 16; ++q) {
+            out[2 * q] = _mm512_mask_reduce_add_ps(0x00FF, a[q]);
+            out[2 * q + 1] = _mm512_mask_reduce_add_ps(0xFF00, a[q]);
+        }
+        return;
+    }
+    for (int h = 0; h < 2; ++h) {
+        const uint8_t* base = half_panel_base(fmt, rec, off, p, h, K);
+        __m512 a[16];
+        for (int j = 0; j < 16; ++j) a[j] = _mm512_setzero_ps();
+        if (fmt == FMT_FP8_B128) {
+            const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
+            for (int c = 0; c < K / 16; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                const __m512 s = _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale);
+                const __m512 xv = _mm512_loadu_ps(x + 16 * c);
+                for (int j = 0; j < 16; ++j)
+                    a[j] = _mm512_fmadd_ps(_mm512_mul_ps(e4m3x16_div256(u + 16 * j), s), xv, a[j]);
+            }
+        } else {
+            const __m512 lut = _mm512_load_ps(e2m1_table());
+            const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h;     // scale panel: 32 x K/32 bytes
+            for (int c = 0; c < K / 32; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
+                const __m512 x0 = _mm512_loadu_ps(x + 32 * c);
+                const __m512 x1 = _mm512_loadu_ps(x + 32 * c + 16);
+                for (int j = 0; j < 16; ++j) {
+                    const __m512 s = _mm512_set1_ps(e8m0(su[j]));
+                    const __m512 w0 = _mm512_mul_ps(e2m1x16(u + 16 * j, lut), s);
+                    const __m512 w1 = _mm512_mul_ps(e2m1x16(u + 16 * j + 8, lut), s);
+                    a[j] = _mm512_fmadd_ps(w1, x1, _mm512_fmadd_ps(w0, x0, a[j]));
+                }
+            }
+        }
+        for (int j = 0; j < 16; ++j) out[16 * h + j] = _mm512_reduce_add_ps(a[j]);
     }
 }
 

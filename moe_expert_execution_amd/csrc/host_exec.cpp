@@ -120,15 +120,16 @@ void barrier(HostBranch* hb, int participants) {
 
 // Per-thread scratch of the host workers.
 struct WorkerScratch {
-    std::vector<float> g, u, y;         // 16 * tokens dot results
+    std::vector<float> g, u, y;         // 16 * tokens dot results (32 for one token: a whole panel)
     std::vector<const float*> vec;      // token vectors
     std::vector<float> wdec;            // one decoded half panel, 16 x K (many-token dots)
     void fit(int nt, int kmax) {
         if ((int64_t)wdec.size() < 16ll * kmax) wdec.resize(16 * (size_t)kmax);
         if ((int)vec.size() < nt) {
-            g.resize(16 * (size_t)nt);
-            u.resize(16 * (size_t)nt);
-            y.resize(16 * (size_t)nt);
+            const size_t n = std::max<size_t>(32, 16 * (size_t)nt);
+            g.resize(n);
+            u.resize(n);
+            y.resize(n);
             vec.resize(nt);
         }
     }
@@ -168,6 +169,12 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
             ws.fit(nt, std::max(d, f));
             for (int i = 0; i < nt; ++i) ws.vec[i] = hb->xf.data() + (int64_t)jb.tok[t0 + i] * d;
             const int64_t hrow0 = together ? t0 : 0;
+            if (nt == 1) {      // one token: each lane block read in one or two passes
+                hostk::panel_dots_1(fmt, rec, hb->rl.off_gate, hb->rl.off_sg, p, d, ws.vec[0], ws.g.data());
+                hostk::panel_dots_1(fmt, rec, hb->rl.off_up, hb->rl.off_su, p, d, ws.vec[0], ws.u.data());
+                for (int r = 0; r < 32; ++r) hb->hbuf[hrow0 * f + 32 * p + r] = silu(ws.g[r]) * ws.u[r];
+                continue;
+            }
             for (int h = 0; h < 2; ++h) {
                 hostk::half_panel_dots(fmt, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.vec.data(), nt,
                                        ws.wdec.data(), ws.g.data());
@@ -186,20 +193,28 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
         for (;;) {
             const int p = hb->next_block.fetch_add(1, std::memory_order_relaxed);
             if (p >= nblk) break;
-            for (int xi = x0; xi < x1; ++xi)              // each output element: its experts in order
-            for (int b = 2 * p; b < 2 * p + 2; ++b) {    // output columns 16 b .. 16 b + 15
+            for (int xi = x0; xi < x1; ++xi) {            // each output element: its experts in order
                 const int e = jb.experts[xi];
                 const int t0 = jb.tok_off[xi], nt = jb.tok_off[xi + 1] - t0;
                 const uint8_t* rec = hb->bank[jb.layer] + (int64_t)e * S;
                 ws.fit(nt, std::max(d, f));
                 const int64_t hrow0 = together ? t0 : 0;
                 for (int i = 0; i < nt; ++i) ws.vec[i] = hb->hbuf.data() + (hrow0 + i) * f;
-                hostk::half_panel_dots(fmt, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f, ws.vec.data(),
-                                       nt, ws.wdec.data(), ws.y.data());
-                for (int i = 0; i < nt; ++i) {
-                    float* pr = P + (int64_t)jb.tok[t0 + i] * d + 16 * b;
-                    const float wt = jb.wt[t0 + i];
-                    for (int r = 0; r < 16; ++r) pr[r] += wt * ws.y[i * 16 + r];
+                if (nt == 1) {      // one token: the whole output panel in one call
+                    hostk::panel_dots_1(fmt, rec, hb->rl.off_down, hb->rl.off_sd, p, f, ws.vec[0], ws.y.data());
+                    float* pr = P + (int64_t)jb.tok[t0] * d + 32 * p;
+                    const float wt = jb.wt[t0];
+                    for (int r = 0; r < 32; ++r) pr[r] += wt * ws.y[r];
+                    continue;
+                }
+                for (int b = 2 * p; b < 2 * p + 2; ++b) {    // output columns 16 b .. 16 b + 15
+                    hostk::half_panel_dots(fmt, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f,
+                                           ws.vec.data(), nt, ws.wdec.data(), ws.y.data());
+                    for (int i = 0; i < nt; ++i) {
+                        float* pr = P + (int64_t)jb.tok[t0 + i] * d + 16 * b;
+                        const float wt = jb.wt[t0 + i];
+                        for (int r = 0; r < 16; ++r) pr[r] += wt * ws.y[i * 16 + r];
+                    }
                 }
             }
         }

@@ -2,8 +2,10 @@
 on the CPU: for every record format, both paths (one streaming pass for few
 vectors; decode once + register-blocked tiles for many) give the dots of the
 oracle-decoded matrix rows with the vectors, within fp32 rounding (the
-streaming pass exists for 1..3 vectors; above that the dispatcher is used).  A small
-g++ harness includes the header as the library does.  CPU only."""
+streaming pass exists for 1..3 vectors; above that the dispatcher is used);
+the one-vector whole-panel pass gives the same bits as the two half-panel
+passes.  A small g++ harness includes the header as the library does.  CPU
+only."""
 import os
 import subprocess
 
@@ -33,8 +35,9 @@ int main(int argc, char** argv) {
     f = fopen(argv[9], "rb"); if (fread(v.data(), 4, v.size(), f) != v.size()) return 3; fclose(f);
     std::vector<const float*> vec(nt);
     for (int i = 0; i < nt; ++i) vec[i] = v.data() + (size_t)i * K;
-    std::vector<float> wdec(16 * (size_t)K), out(16 * nt);
-    if (blocked) { half_panel_decode(fmt, rec.data(), off, soff, p, h, K, wdec.data());
+    std::vector<float> wdec(16 * (size_t)K), out(blocked == 2 ? 32 : 16 * nt);
+    if (blocked == 2) panel_dots_1(fmt, rec.data(), off, soff, p, K, vec[0], out.data());
+    else if (blocked) { half_panel_decode(fmt, rec.data(), off, soff, p, h, K, wdec.data());
                    dots_16xT(wdec.data(), K, vec.data(), nt, out.data()); }
     else if (nt == 1) half_panel_dots_stream<1>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
     else if (nt == 2) half_panel_dots_stream<2>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
@@ -92,3 +95,34 @@ def test_half_panel_dots_match_decoded_rows(harness, fmt, blocked, nt):
                 ref = v.astype(np.float64) @ rows[32 * p + 16 * h: 32 * p + 16 * h + 16].T
                 bound = 1e-5 * (np.abs(v).astype(np.float64) @ np.abs(rows[32 * p + 16 * h: 32 * p + 16 * h + 16]).T)
                 assert np.all(np.abs(got - ref) <= bound + 1e-30), (mat, p, h, np.abs(got - ref).max())
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_panel_dots_1_same_bits_as_halves(harness, fmt):
+    """One vector over a whole panel (rows 32p .. 32p + 31): the same float32
+    bits as the streaming pass over its two halves, and within the bound of
+    the oracle-decoded rows; gate (K = d) and down (K = f) panels."""
+    exe, tmp = harness
+    d, f = 384, 256
+    cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=d, f=f, E=2, cfg_id=92)
+    rec = synth.bank(cfg, 0, 1)[0]
+    Wg, Wu, Wd = OF.decode_record(rec, fmt, d, f)
+    og, od, osg, osd = offsets(fmt, d, f)
+    rng = np.random.default_rng(5)
+    (tmp / "rec.bin").write_bytes(rec.tobytes())
+
+    def run(K, p, h, off, soff, mode, n):
+        subprocess.check_call([str(exe), str(FMT[fmt]), str(K), "1", str(p), str(h), str(off), str(soff),
+                               str(tmp / "rec.bin"), str(tmp / "v.bin"), str(tmp / "o.bin"), str(mode)])
+        return np.fromfile(tmp / "o.bin", dtype=np.float32)[:n]
+
+    for K, rows, off, soff in ((d, Wg.T, og, osg), (f, Wd.T, od, osd)):
+        v = rng.standard_normal((1, K)).astype(np.float32)
+        (tmp / "v.bin").write_bytes(v.tobytes())
+        for p in range(rows.shape[0] // 32):
+            whole = run(K, p, 0, off, soff, 2, 32)
+            halves = np.concatenate([run(K, p, 0, off, soff, 0, 16), run(K, p, 1, off, soff, 0, 16)])
+            assert np.array_equal(whole.view(np.uint32), halves.view(np.uint32)), (K, p)
+            ref = v.astype(np.float64) @ rows[32 * p: 32 * p + 32].T
+            bound = 1e-5 * (np.abs(v).astype(np.float64) @ np.abs(rows[32 * p: 32 * p + 32]).T)
+            assert np.all(np.abs(whole - ref[0]) <= bound[0] + 1e-30), (K, p)
