@@ -25,7 +25,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wn
           "-Wno-unused-variable"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-munsafe-fp-atomics"]
-HOST_FLAGS = ["-I", "/opt/rocm/include", "-Wno-c++20-extensions", "-mavx512f", "-mavx512bw", "-mavx512vl", "-mavx512dq", "-mfma", "-pthread", "-D__HIP_PLATFORM_AMD__"]
+HOST_FLAGS = ["-I", "/opt/rocm/include", "-Wno-c++20-extensions", "-mavx512f", "-mavx512bw", "-mavx512vl", "-mavx512dq", "-mavx512bf16", "-mfma", "-pthread", "-D__HIP_PLATFORM_AMD__"]
 
 
 def _obj(src):

@@ -280,9 +280,100 @@ inline void dots_16xT(const float* w, int K, const float* const* vec, int nt, fl
     }
 }
 
-// Vectors at which the half panel is decoded once into `wdec` (16 * K
-// floats) and dotted by register-blocked tiles: there the multiply-adds, not
-// the record's bytes, set the pace.
+// ---- many vectors in bf16 (AVX512-BF16) ------------------------------------
+// With many vectors the multiply-adds set the pace and the decoded rows and
+// vectors stream through L2 for every 4-row x 6-vector tile; bf16 operands
+// halve those bytes and VDPBF16PS does two multiply-adds a lane.  Products
+// of bf16 values are exact in fp32; the sums are fp32.
+
+// Decode the half panel (p, h) into bf16 rows w[r * K + k], r < 16: bf16
+// codes as they are; e4m3 times its block scale rounded to bf16 (as the GPU
+// grouped GEMM does); e2m1 times its power-of-two scale, exact.
+inline void half_panel_decode_bf16(int fmt, const uint8_t* rec, int64_t off, int64_t soff, int p, int h, int K,
+                                   uint16_t* w) {
+    const uint8_t* base = half_panel_base(fmt, rec, off, p, h, K);
+    switch (fmt) {
+        case FMT_BF16:
+            for (int c = 0; c < K / 8; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                for (int r = 0; r < 16; ++r)
+                    _mm_storeu_si128(reinterpret_cast<__m128i*>(w + (int64_t)r * K + 8 * c),
+                                     _mm_loadu_si128(reinterpret_cast<const __m128i*>(u + 16 * r)));
+            }
+            return;
+        case FMT_FP8_B128: {
+            const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
+            for (int c = 0; c < K / 16; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                const __m512 s = _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale);
+                for (int r = 0; r < 16; ++r) {
+                    const __m256bh v = _mm512_cvtneps_pbh(_mm512_mul_ps(e4m3x16_div256(u + 16 * r), s));
+                    _mm256_storeu_si256(reinterpret_cast<__m256i*>(w + (int64_t)r * K + 16 * c), (__m256i)v);
+                }
+            }
+            return;
+        }
+        default: {
+            const __m512 lut = _mm512_load_ps(e2m1_table());
+            const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h;
+            for (int c = 0; c < K / 32; ++c) {
+                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+                const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
+                for (int r = 0; r < 16; ++r) {
+                    const __m512 s = _mm512_set1_ps(e8m0(su[r]));
+                    const __m512bh v = _mm512_cvtne2ps_pbh(_mm512_mul_ps(e2m1x16(u + 16 * r + 8, lut), s),
+                                                            _mm512_mul_ps(e2m1x16(u + 16 * r, lut), s));
+                    _mm512_storeu_si512(reinterpret_cast<__m512i*>(w + (int64_t)r * K + 32 * c), (__m512i)v);
+                }
+            }
+            return;
+        }
+    }
+}
+
+// out[i * 16 + r0 + j] = sum_k w[(r0 + j) * K + k] * vec[t0 + i][k] (bf16
+// rows and vectors, fp32 sums) for j < 4, i < TB.
+template <int TB>
+inline void dots_4xTB_bf16(const uint16_t* w, int K, const uint16_t* const* vec, int t0, int r0, float* out) {
+    __m512 a[4][TB];
+    for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < TB; ++i) a[j][i] = _mm512_setzero_ps();
+    const uint16_t* w0 = w + (int64_t)r0 * K;
+    for (int k = 0; k < K; k += 32) {
+        __m512bh wv[4];
+        for (int j = 0; j < 4; ++j)
+            wv[j] = (__m512bh)_mm512_loadu_si512(reinterpret_cast<const void*>(w0 + (int64_t)j * K + k));
+        for (int i = 0; i < TB; ++i) {
+            const __m512bh x = (__m512bh)_mm512_loadu_si512(reinterpret_cast<const void*>(vec[t0 + i] + k));
+            for (int j = 0; j < 4; ++j) a[j][i] = _mm512_dpbf16_ps(a[j][i], wv[j], x);
+        }
+    }
+    for (int i = 0; i < TB; ++i)
+        for (int j = 0; j < 4; ++j) out[(t0 + i) * 16 + r0 + j] = _mm512_reduce_add_ps(a[j][i]);
+}
+
+// Dots of 16 bf16 rows w [16 x K] with nt bf16 vectors: out[i * 16 + r].
+inline void dots_16xT_bf16(const uint16_t* w, int K, const uint16_t* const* vec, int nt, float* out) {
+    for (int r0 = 0; r0 < 16; r0 += 4) {
+        int t0 = 0;
+        for (; t0 + 6 <= nt; t0 += 6) dots_4xTB_bf16<6>(w, K, vec, t0, r0, out);
+        switch (nt - t0) {
+            case 5: dots_4xTB_bf16<5>(w, K, vec, t0, r0, out); break;
+            case 4: dots_4xTB_bf16<4>(w, K, vec, t0, r0, out); break;
+            case 3: dots_4xTB_bf16<3>(w, K, vec, t0, r0, out); break;
+            case 2: dots_4xTB_bf16<2>(w, K, vec, t0, r0, out); break;
+            case 1: dots_4xTB_bf16<1>(w, K, vec, t0, r0, out); break;
+            default: break;
+        }
+    }
+}
+
+// Vectors at which the half panel is decoded once and dotted by
+// register-blocked tiles: there the multiply-adds, not the record's bytes,
+// set the pace.  The host branch takes the bf16 form above from here on
+// (decode, FP8 configuration, one box: T = 64 calls +15%, T = 2,048 calls
+// +80% against the fp32 form); the fp32 form below (`wdec`, 16 * K floats)
+// is what half_panel_dots does for such counts.
 constexpr int kBlockedMinVectors = 4;
 
 // Dots of the 16 rows [32p + 16h, +16) of a panel-ordered [rows x K] matrix

@@ -70,7 +70,9 @@ struct HostBranch {
     std::atomic<int> finished{0};
     // per-call scratch shared by the workers
     std::vector<float> xf;             // [max_tokens x d] fp32 activations of the tokens with host routes
+    std::vector<uint16_t> xb;          // the same in bf16
     std::vector<float> hbuf;           // SwiGLU outputs [rows x f]: every (expert, token) entry of a call
+    std::vector<uint16_t> hbuf16;      // the same in bf16, for experts with many tokens
                                        // with up to max(max_tokens, 2k, min(max_tokens k, 2^21 / f)) entries
     // host-function contexts of calls captured into graphs: each captured
     // call owns one for the life of the branch (a graph may replay it any
@@ -122,9 +124,13 @@ void barrier(HostBranch* hb, int participants) {
 struct WorkerScratch {
     std::vector<float> g, u, y;         // 16 * tokens dot results (32 for one token: a whole panel)
     std::vector<const float*> vec;      // token vectors
-    std::vector<float> wdec;            // one decoded half panel, 16 x K (many-token dots)
+    std::vector<float> wdec;            // one decoded half panel, 16 x K (fp32)
+    std::vector<uint16_t> wdec16;       // one decoded half panel, 16 x K (bf16, many-token dots)
+    std::vector<const uint16_t*> vec16; // token vectors in bf16
     void fit(int nt, int kmax) {
         if ((int64_t)wdec.size() < 16ll * kmax) wdec.resize(16 * (size_t)kmax);
+        if ((int64_t)wdec16.size() < 16ll * kmax) wdec16.resize(16 * (size_t)kmax);
+        if ((int)vec16.size() < nt) vec16.resize(nt);
         if ((int)vec.size() < nt) {
             const size_t n = std::max<size_t>(32, 16 * (size_t)nt);
             g.resize(n);
@@ -175,6 +181,24 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
                 for (int r = 0; r < 32; ++r) hb->hbuf[hrow0 * f + 32 * p + r] = silu(ws.g[r]) * ws.u[r];
                 continue;
             }
+            if (nt >= hostk::kBlockedMinVectors) {      // many tokens: bf16 rows and vectors, h kept in bf16
+                for (int i = 0; i < nt; ++i) ws.vec16[i] = hb->xb.data() + (int64_t)jb.tok[t0 + i] * d;
+                for (int h = 0; h < 2; ++h) {
+                    hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.wdec16.data());
+                    hostk::dots_16xT_bf16(ws.wdec16.data(), d, ws.vec16.data(), nt, ws.g.data());
+                    hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_up, hb->rl.off_su, p, h, d, ws.wdec16.data());
+                    hostk::dots_16xT_bf16(ws.wdec16.data(), d, ws.vec16.data(), nt, ws.u.data());
+                    const int b = 2 * p + h;  // rows 16 b .. 16 b + 15
+                    for (int i = 0; i < nt; ++i) {
+                        alignas(64) float hv[16];
+                        for (int r = 0; r < 16; ++r) hv[r] = silu(ws.g[i * 16 + r]) * ws.u[i * 16 + r];
+                        const __m256bh hb16 = _mm512_cvtneps_pbh(_mm512_load_ps(hv));
+                        _mm256_storeu_si256(reinterpret_cast<__m256i*>(&hb->hbuf16[(hrow0 + i) * f + 16 * b]),
+                                            (__m256i)hb16);
+                    }
+                }
+                continue;
+            }
             for (int h = 0; h < 2; ++h) {
                 hostk::half_panel_dots(fmt, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.vec.data(), nt,
                                        ws.wdec.data(), ws.g.data());
@@ -200,6 +224,20 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
                 ws.fit(nt, std::max(d, f));
                 const int64_t hrow0 = together ? t0 : 0;
                 for (int i = 0; i < nt; ++i) ws.vec[i] = hb->hbuf.data() + (hrow0 + i) * f;
+                if (nt >= hostk::kBlockedMinVectors) {      // many tokens: bf16 (h as phase 1 left it)
+                    for (int i = 0; i < nt; ++i) ws.vec16[i] = hb->hbuf16.data() + (hrow0 + i) * f;
+                    for (int b = 2 * p; b < 2 * p + 2; ++b) {
+                        hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f,
+                                                      ws.wdec16.data());
+                        hostk::dots_16xT_bf16(ws.wdec16.data(), f, ws.vec16.data(), nt, ws.y.data());
+                        for (int i = 0; i < nt; ++i) {
+                            float* pr = P + (int64_t)jb.tok[t0 + i] * d + 16 * b;
+                            const float wt = jb.wt[t0 + i];
+                            for (int r = 0; r < 16; ++r) pr[r] += wt * ws.y[i * 16 + r];
+                        }
+                    }
+                    continue;
+                }
                 if (nt == 1) {      // one token: the whole output panel in one call
                     hostk::panel_dots_1(fmt, rec, hb->rl.off_down, hb->rl.off_sd, p, f, ws.vec[0], ws.y.data());
                     float* pr = P + (int64_t)jb.tok[t0] * d + 32 * p;
@@ -304,12 +342,18 @@ void run_call(HostBranch* hb, int layer, int T) {
         const auto t_start = std::chrono::steady_clock::now();
         for (int t = 0; t < T; ++t)
             if (has[t]) memset(hb->stg.P + (int64_t)t * d, 0, sizeof(float) * d);
-        // fp32 activations of every token with host routes
+        // the activations of every token with host routes, out of the pinned
+        // staging (read once here; the dot loops read them many times): fp32,
+        // and bf16 as they are
         for (int t = 0; t < T; ++t) {
             if (!has[t]) continue;
             const uint16_t* xr = hb->stg.x + (int64_t)t * d;
             float* o = hb->xf.data() + (int64_t)t * d;
-            for (int c = 0; c < d; ++c) o[c] = __builtin_bit_cast(float, (uint32_t)xr[c] << 16);
+            uint16_t* ob = hb->xb.data() + (int64_t)t * d;
+            for (int c = 0; c < d; ++c) {
+                ob[c] = xr[c];
+                o[c] = __builtin_bit_cast(float, (uint32_t)xr[c] << 16);
+            }
         }
         hb->finished.store(0);
         {
@@ -418,11 +462,13 @@ HostBranch* host_branch_create(const ft_shape& sh, const RecordLayout& rl, const
         return nullptr;
     }
     hb->xf.resize((size_t)max_tokens * d);
+    hb->xb.resize((size_t)max_tokens * d);
     // SwiGLU outputs: one row per token for experts run one at a time, or one
     // row per (expert, token) entry when a call's entries fit (at least 2k rows)
     const int64_t hrows = std::max<int64_t>(std::max<int64_t>(max_tokens, 2 * (int64_t)sh.top_k),
                                             std::min<int64_t>((int64_t)max_tokens * sh.top_k, (1 << 21) / f));
     hb->hbuf.resize((size_t)hrows * f);
+    hb->hbuf16.resize((size_t)hrows * f);
     for (int i = 0; i < kRing; ++i) hb->ring[i].hb = hb;
     // worker count: cores in the affinity mask minus four (the caller's thread,
     // the mailbox poller, the HIP runtime's threads), at least one: spinning

@@ -36,6 +36,22 @@ int main(int argc, char** argv) {
     std::vector<const float*> vec(nt);
     for (int i = 0; i < nt; ++i) vec[i] = v.data() + (size_t)i * K;
     std::vector<float> wdec(16 * (size_t)K), out(blocked == 2 ? 32 : 16 * nt);
+    if (blocked >= 3) {     // bf16: 3 = the decoded rows, 4 = their dots with bf16 vectors (v.bin holds bf16)
+        std::vector<uint16_t> w16(16 * (size_t)K);
+        half_panel_decode_bf16(fmt, rec.data(), off, soff, p, h, K, w16.data());
+        f = fopen(argv[10], "wb");
+        if (blocked == 3) {
+            fwrite(w16.data(), 2, w16.size(), f);
+        } else {
+            const uint16_t* v16 = reinterpret_cast<const uint16_t*>(v.data());
+            std::vector<const uint16_t*> vec16(nt);
+            for (int i = 0; i < nt; ++i) vec16[i] = v16 + (size_t)i * K;
+            dots_16xT_bf16(w16.data(), K, vec16.data(), nt, out.data());
+            fwrite(out.data(), 4, out.size(), f);
+        }
+        fclose(f);
+        return 0;
+    }
     if (blocked == 2) panel_dots_1(fmt, rec.data(), off, soff, p, K, vec[0], out.data());
     else if (blocked) { half_panel_decode(fmt, rec.data(), off, soff, p, h, K, wdec.data());
                    dots_16xT(wdec.data(), K, vec.data(), nt, out.data()); }
@@ -55,7 +71,7 @@ def harness(tmp_path_factory):
     src = d / "h.cpp"
     src.write_text(HARNESS)
     exe = d / "h"
-    subprocess.check_call(["g++", "-O2", "-std=c++17", "-mavx512f", "-mavx512bw", "-mavx512vl", "-mavx512dq",
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-mavx512f", "-mavx512bw", "-mavx512vl", "-mavx512dq", "-mavx512bf16",
                            "-I", CSRC, str(src), "-o", str(exe)])
     return exe, d
 
@@ -126,3 +142,46 @@ def test_panel_dots_1_same_bits_as_halves(harness, fmt):
             ref = v.astype(np.float64) @ rows[32 * p: 32 * p + 32].T
             bound = 1e-5 * (np.abs(v).astype(np.float64) @ np.abs(rows[32 * p: 32 * p + 32]).T)
             assert np.all(np.abs(whole - ref[0]) <= bound[0] + 1e-30), (K, p)
+
+
+def _bf16_rne(a):
+    """float64 -> bf16 bits: to float32, then round to nearest even on the upper 16 bits."""
+    u = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("nt", [4, 7, 13])
+def test_bf16_blocked_dots(harness, fmt, nt):
+    """Many vectors in bf16: the decoded half-panel rows are the oracle's
+    values exactly for bf16 and MXFP4 and e4m3 x block scale rounded to bf16
+    for FP8 (within 2^-8 relative); their dots with bf16 vectors are the fp64
+    dots of those same bf16 operands within fp32 rounding."""
+    exe, tmp = harness
+    d, f = 256, 128
+    cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=d, f=f, E=2, cfg_id=91)
+    rec = synth.bank(cfg, 0, 1)[0]
+    Wg, Wu, Wd = OF.decode_record(rec, fmt, d, f)
+    og, od, osg, osd = offsets(fmt, d, f)
+    rng = np.random.default_rng(nt)
+    (tmp / "rec.bin").write_bytes(rec.tobytes())
+    for K, rows, off, soff in ((d, Wg.T, og, osg), (f, Wd.T, od, osd)):
+        v16 = _bf16_rne(rng.standard_normal((nt, K)))                            # bf16 vectors
+        v64 = OF.bf16_to_f64(v16)
+        (tmp / "v.bin").write_bytes(v16.tobytes() + bytes(2 * nt * K))
+        for p in range(rows.shape[0] // 32):
+            for h in (0, 1):
+                args = [str(exe), str(FMT[fmt]), str(K), str(nt), str(p), str(h), str(off), str(soff),
+                        str(tmp / "rec.bin"), str(tmp / "v.bin"), str(tmp / "o.bin")]
+                subprocess.check_call(args + ["3"])
+                w16 = OF.bf16_to_f64(np.fromfile(tmp / "o.bin", dtype=np.uint16)).reshape(16, K)
+                ref_w = rows[32 * p + 16 * h: 32 * p + 16 * h + 16]
+                if fmt == "fp8":
+                    assert np.all(np.abs(w16 - ref_w) <= 2.0 ** -8 * np.abs(ref_w)), (K, p, h)
+                else:
+                    assert np.array_equal(w16, ref_w), (K, p, h)
+                subprocess.check_call(args + ["4"])
+                got = np.fromfile(tmp / "o.bin", dtype=np.float32).reshape(nt, 16)
+                ref = v64 @ w16.T
+                bound = 1e-5 * (np.abs(v64) @ np.abs(w16).T)
+                assert np.all(np.abs(got - ref) <= bound + 1e-30), (K, p, h, np.abs(got - ref).max())
