@@ -156,7 +156,8 @@ typedef struct {
  * Errors: FT_ERR_ARG (shape, null, N, max_tokens; a host_bank that is not
  *   pinned, or whose allocation is known to end before layers * experts
  *   records), FT_ERR_NOMEM, FT_ERR_HIP.
- * Synchronises the current device.
+ * Synchronises the current device.  The host workers it starts use AVX-512
+ *   (F, BW, VL, DQ and the BF16 extension) on the host CPU.
  *
  * Record layout (S bytes), matrices [rows x K] in this order:
  *   BF16       WgT [f x d] | WuT [f x d] | WdT [d x f]                  (bf16)
