@@ -136,10 +136,11 @@ inline void half_panel_dots_stream(int fmt, const uint8_t* rec, int64_t off, int
 // One vector, a whole panel: out[r] = row 32p + r of the matrix dotted with
 // x, r < 32.  Every lane block is read front to back: bf16 in one pass with
 // two rows per accumulator (16 of them), block-FP8 and MXFP4 in two passes
-// of 16 rows (the halves), one row per accumulator.  For each row the
-// multiply-adds run in the order of half_panel_dots_stream<1>, so the sums
-// are the same numbers; what changes is that a 1 KiB lane block is read in
-// one or two passes instead of four.
+// of 16 rows (the halves), one row per accumulator, so a 1 KiB lane block is
+// read in one or two passes instead of four.  For bf16 and block-FP8 each
+// row's multiply-adds run in the order of half_panel_dots_stream<1> (the
+// same numbers); MXFP4 sums each chunk before applying its scale (fp32
+// rounding of the same products).
 inline void panel_dots_1(int fmt, const uint8_t* rec, int64_t off, int64_t soff, int p, int K, const float* x,
                          float* out) {
     if (fmt == FMT_BF16) {
@@ -175,18 +176,34 @@ inline void panel_dots_1(int fmt, const uint8_t* rec, int64_t off, int64_t soff,
                     a[j] = _mm512_fmadd_ps(_mm512_mul_ps(e4m3x16_div256(u + 16 * j), s), xv, a[j]);
             }
         } else {
+            // A row's 16 code bytes hold its 32 values of the chunk: the low
+            // nibbles are the even elements, the high nibbles the odd ones, so
+            // each half converts with one table permute against the even or the
+            // odd half of x (de-interleaved once per chunk for all 16 rows).  The
+            // row's block scale (a power of two) multiplies the chunk's sum once;
+            // the 16 rows' scale bytes are one 16-byte load.
             const __m512 lut = _mm512_load_ps(e2m1_table());
+            const __m512i even = _mm512_set_epi32(30, 28, 26, 24, 22, 20, 18, 16, 14, 12, 10, 8, 6, 4, 2, 0);
+            const __m512i odd = _mm512_add_epi32(even, _mm512_set1_epi32(1));
             const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h;     // scale panel: 32 x K/32 bytes
             for (int c = 0; c < K / 32; ++c) {
                 const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
                 const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
                 const __m512 x0 = _mm512_loadu_ps(x + 32 * c);
                 const __m512 x1 = _mm512_loadu_ps(x + 32 * c + 16);
+                const __m512 xe = _mm512_permutex2var_ps(x0, even, x1);
+                const __m512 xo = _mm512_permutex2var_ps(x0, odd, x1);
+                // e8m0 -> 2^(e - 127): e << 23, and the subnormal 2^-127 for e = 0
+                const __m512i e = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(su)));
+                const __m512 sv = _mm512_castsi512_ps(_mm512_mask_blend_epi32(
+                    _mm512_cmpeq_epi32_mask(e, _mm512_setzero_si512()), _mm512_slli_epi32(e, 23),
+                    _mm512_set1_epi32(0x00400000)));
                 for (int j = 0; j < 16; ++j) {
-                    const __m512 s = _mm512_set1_ps(e8m0(su[j]));
-                    const __m512 w0 = _mm512_mul_ps(e2m1x16(u + 16 * j, lut), s);
-                    const __m512 w1 = _mm512_mul_ps(e2m1x16(u + 16 * j + 8, lut), s);
-                    a[j] = _mm512_fmadd_ps(w1, x1, _mm512_fmadd_ps(w0, x0, a[j]));
+                    const __m512i b = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(u + 16 * j)));
+                    const __m512 we = _mm512_permutexvar_ps(_mm512_and_si512(b, _mm512_set1_epi32(0xF)), lut);
+                    const __m512 wo = _mm512_permutexvar_ps(_mm512_srli_epi32(b, 4), lut);
+                    const __m512 t = _mm512_fmadd_ps(wo, xo, _mm512_mul_ps(we, xe));
+                    a[j] = _mm512_fmadd_ps(t, _mm512_permutexvar_ps(_mm512_set1_epi32(j), sv), a[j]);
                 }
             }
         }

@@ -116,8 +116,9 @@ def test_half_panel_dots_match_decoded_rows(harness, fmt, blocked, nt):
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
 def test_panel_dots_1_same_bits_as_halves(harness, fmt):
     """One vector over a whole panel (rows 32p .. 32p + 31): the same float32
-    bits as the streaming pass over its two halves, and within the bound of
-    the oracle-decoded rows; gate (K = d) and down (K = f) panels."""
+    bits as the streaming pass over its two halves (bf16, block-FP8), and
+    within the bound of the oracle-decoded rows (every format); gate (K = d)
+    and down (K = f) panels."""
     exe, tmp = harness
     d, f = 384, 256
     cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=d, f=f, E=2, cfg_id=92)
@@ -138,7 +139,8 @@ def test_panel_dots_1_same_bits_as_halves(harness, fmt):
         for p in range(rows.shape[0] // 32):
             whole = run(K, p, 0, off, soff, 2, 32)
             halves = np.concatenate([run(K, p, 0, off, soff, 0, 16), run(K, p, 1, off, soff, 0, 16)])
-            assert np.array_equal(whole.view(np.uint32), halves.view(np.uint32)), (K, p)
+            if fmt != "mxfp4":      # MXFP4 scales each chunk's sum instead: fp32 rounding of the same products
+                assert np.array_equal(whole.view(np.uint32), halves.view(np.uint32)), (K, p)
             ref = v.astype(np.float64) @ rows[32 * p: 32 * p + 32].T
             bound = 1e-5 * (np.abs(v).astype(np.float64) @ np.abs(rows[32 * p: 32 * p + 32]).T)
             assert np.all(np.abs(whole - ref[0]) <= bound[0] + 1e-30), (K, p)
