@@ -31,13 +31,14 @@ inline const float* e2m1_table() {
 // normal (1 + m/8) 2^(e-15), subnormal m 2^-17, i.e. exactly 2^-8 times the
 // e4m3 value in both cases, so the hardware fp16 -> fp32 conversion decodes
 // it and the caller folds the 2^8 into its scale.  (NaN codes are not
-// produced by the encoder and decode as finite values here.)
+// produced by the encoder and decode as finite values here.)  The byte is
+// sign-extended to 16 bits, so one shift by 7 puts the magnitude at bits
+// 7..13 and a copy of the sign at bits 14 and 15; clearing bit 14 leaves
+// the fp16 pattern.
 constexpr float kE4M3Fp16Scale = 256.0f;
 inline __m512 e4m3x16_div256(const uint8_t* p) {
-    const __m256i v = _mm256_cvtepu8_epi16(_mm_loadu_si128(reinterpret_cast<const __m128i*>(p)));
-    const __m256i mag = _mm256_slli_epi16(_mm256_and_si256(v, _mm256_set1_epi16(0x7F)), 7);
-    const __m256i sgn = _mm256_slli_epi16(_mm256_and_si256(v, _mm256_set1_epi16(0x80)), 8);
-    return _mm512_cvtph_ps(_mm256_or_si256(mag, sgn));
+    const __m256i v = _mm256_cvtepi8_epi16(_mm_loadu_si128(reinterpret_cast<const __m128i*>(p)));
+    return _mm512_cvtph_ps(_mm256_and_si256(_mm256_slli_epi16(v, 7), _mm256_set1_epi16((short)0xBF80)));
 }
 
 // e8m0 scale byte -> 2^(e - 127) as fp32 bits (e = 0 gives the subnormal
@@ -98,13 +99,15 @@ inline void half_panel_dots_stream(int fmt, const uint8_t* rec, int64_t off, int
         }
         if (fmt == FMT_FP8_B128) {
             const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
+            // the block scale is one number for the chunk's rows: it multiplies
+            // the NT vector chunks, not the 8 rows' codes
             for (int c = 0; c < K / 16; ++c) {
                 const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512 + 16 * r0;
                 const __m512 s = _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale);
                 __m512 x[NT];
-                for (int i = 0; i < NT; ++i) x[i] = _mm512_loadu_ps(vec[i] + 16 * c);
+                for (int i = 0; i < NT; ++i) x[i] = _mm512_mul_ps(_mm512_loadu_ps(vec[i] + 16 * c), s);
                 for (int j = 0; j < 8; ++j) {
-                    const __m512 w = _mm512_mul_ps(e4m3x16_div256(u + 16 * j), s);
+                    const __m512 w = e4m3x16_div256(u + 16 * j);
                     for (int i = 0; i < NT; ++i) a[j][i] = _mm512_fmadd_ps(w, x[i], a[j][i]);
                 }
             }
@@ -170,10 +173,9 @@ inline void panel_dots_1(int fmt, const uint8_t* rec, int64_t off, int64_t soff,
             const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
             for (int c = 0; c < K / 16; ++c) {
                 const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
-                const __m512 s = _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale);
-                const __m512 xv = _mm512_loadu_ps(x + 16 * c);
-                for (int j = 0; j < 16; ++j)
-                    a[j] = _mm512_fmadd_ps(_mm512_mul_ps(e4m3x16_div256(u + 16 * j), s), xv, a[j]);
+                const __m512 xv = _mm512_mul_ps(_mm512_loadu_ps(x + 16 * c),
+                                                _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale));
+                for (int j = 0; j < 16; ++j) a[j] = _mm512_fmadd_ps(e4m3x16_div256(u + 16 * j), xv, a[j]);
             }
         } else {
             // A row's 16 code bytes hold its 32 values of the chunk: the low

@@ -187,3 +187,50 @@ def test_bf16_blocked_dots(harness, fmt, nt):
                 ref = v64 @ w16.T
                 bound = 1e-5 * (np.abs(v64) @ np.abs(w16).T)
                 assert np.all(np.abs(got - ref) <= bound + 1e-30), (K, p, h, np.abs(got - ref).max())
+
+
+def test_fp8_every_code(harness):
+    """A block-FP8 gate matrix whose codes run through all 254 non-NaN e4m3
+    codes (both signs, zero, subnormals, the largest normal): the fp32
+    decode gives each element as the oracle's decode times the block scale,
+    rounded once to fp32 (read back by dots with one-hot vectors), and the
+    streaming passes and the one-vector panel pass stay within the fp32
+    bound of the oracle's dots."""
+    exe, tmp = harness
+    d, f = 256, 128
+    cfg = synth.CONFIGS["tiny"].with_(fmt="fp8", d=d, f=f, E=2, cfg_id=94)
+    rec = synth.bank(cfg, 0, 1)[0].copy()
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    rec[: d * f] = np.resize(codes, d * f)
+    Wg = OF.decode_record(rec, "fp8", d, f)[0]
+    rows = Wg.T                                   # f rows of length d
+    assert np.isin(codes, rec[: d * f]).all()
+    og, _, osg, _ = offsets("fp8", d, f)
+    (tmp / "rec.bin").write_bytes(rec.tobytes())
+    (tmp / "v.bin").write_bytes(np.eye(d, dtype=np.float32).tobytes())
+    for p in range(f // 32):
+        for h in (0, 1):
+            subprocess.check_call([str(exe), "1", str(d), str(d), str(p), str(h), str(og), str(osg),
+                                   str(tmp / "rec.bin"), str(tmp / "v.bin"), str(tmp / "o.bin"), "1"])
+            got = np.fromfile(tmp / "o.bin", dtype=np.float32).reshape(d, 16)
+            want = rows[32 * p + 16 * h: 32 * p + 16 * h + 16].T.astype(np.float32)
+            assert np.array_equal(got, want), (p, h)
+    rng = np.random.default_rng(94)
+    for nt in (1, 2, 3):
+        v = rng.standard_normal((nt, d)).astype(np.float32)
+        (tmp / "v.bin").write_bytes(v.tobytes())
+        for p in range(f // 32):
+            halves = []
+            for h in (0, 1):
+                subprocess.check_call([str(exe), "1", str(d), str(nt), str(p), str(h), str(og), str(osg),
+                                       str(tmp / "rec.bin"), str(tmp / "v.bin"), str(tmp / "o.bin"), "0"])
+                halves.append(np.fromfile(tmp / "o.bin", dtype=np.float32).reshape(nt, 16))
+            got = np.concatenate(halves, axis=1)
+            blk = rows[32 * p: 32 * p + 32]
+            ref = v.astype(np.float64) @ blk.T
+            bound = 1e-5 * (np.abs(v).astype(np.float64) @ np.abs(blk).T)
+            assert np.all(np.abs(got - ref) <= bound + 1e-30), (nt, p, np.abs(got - ref).max())
+            if nt == 1:
+                subprocess.check_call([str(exe), "1", str(d), "1", str(p), "0", str(og), str(osg),
+                                       str(tmp / "rec.bin"), str(tmp / "v.bin"), str(tmp / "o.bin"), "2"])
+                assert np.array_equal(np.fromfile(tmp / "o.bin", dtype=np.float32), got[0]), p
