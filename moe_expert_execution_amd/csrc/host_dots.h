@@ -65,74 +65,117 @@ inline const uint8_t* half_panel_base(int fmt, const uint8_t* rec, int64_t off, 
     return rec + off + (int64_t)p * 32 * row_bytes + h * 256;
 }
 
-// One pass over the half panel for NT <= 3 vectors: each chunk of codes is
-// decoded once and dotted with the NT vectors; rows go in two groups of 8, so
-// the 8 * NT accumulators stay in registers.  Suits few vectors (decode: one
-// token), where the record's bytes set the pace.
+// Software prefetch distance of the dot loops, in 16-byte row units: each
+// loop touches the panel lines it will read this many units on (8 KiB of the
+// panel ahead).  One core's own demand misses leave it waiting on memory:
+// block-FP8, one vector, 12 cores of a 16-core EPYC host read 103 GB/s of
+// codes without it and 180 GB/s with it, against 366 GB/s from L2.
+constexpr int kPrefetchUnits = 16;
+
+// Prefetch the first `bytes` bytes (a multiple of 16, at most 512) of unit
+// column c of the rows that start at `base`, if c < nunits.
+inline void prefetch_unit(const uint8_t* base, int c, int nunits, int bytes) {
+    if (c >= nunits) return;
+    const char* q = reinterpret_cast<const char*>(base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512);
+    for (int o = 0; o < bytes; o += 64) _mm_prefetch(q + o, _MM_HINT_T0);
+}
+
+// Most vectors the streaming pass below takes for a format; with more, the
+// half panel is decoded once into bf16 and dotted by register-blocked tiles.
+// One core streams the codes once per pass, so below these counts the record's
+// bytes set the pace and the pass beats decoding (block-FP8, 12 cores, codes in
+// L2: 4 vectors 249 against 91 GB/s, 6 vectors 187 against 83).
+inline int stream_max_vectors(int fmt) { return fmt == FMT_MXFP4_B32 ? 3 : 8; }
+
+// One pass over the half panel for NT vectors: each unit of codes is decoded
+// once and dotted with the NT vectors; the 16 rows go in passes of R rows, R
+// set so that the R x NT accumulators and the NT vector chunks stay in
+// registers.  A row's multiply-adds run in the same order for every R.
 template <int NT>
 inline void half_panel_dots_stream(int fmt, const uint8_t* rec, int64_t off, int64_t soff, int p, int h, int K,
                                    const float* const* vec, float* out) {
     const uint8_t* base = half_panel_base(fmt, rec, off, p, h, K);
-    for (int r0 = 0; r0 < 16; r0 += 8) {
-        __m512 a[8][NT];
-        for (int j = 0; j < 8; ++j)
-            for (int i = 0; i < NT; ++i) a[j][i] = _mm512_setzero_ps();
-        if (fmt == FMT_BF16) {
-            // a zmm holds rows (r0 + 2q, r0 + 2q + 1) x 8 values: a[q] for q < 4, the two
-            // halves reduced separately
+    if (fmt == FMT_BF16) {
+        // a zmm holds rows (r0 + 2q, r0 + 2q + 1) x 8 values, the two halves
+        // reduced separately
+        constexpr int R = NT <= 6 ? 8 : 4, Q = R / 2;
+        for (int r0 = 0; r0 < 16; r0 += R) {
+            const uint8_t* b0 = base + 16 * r0;
+            __m512 a[Q][NT];
+            for (int q = 0; q < Q; ++q)
+                for (int i = 0; i < NT; ++i) a[q][i] = _mm512_setzero_ps();
             for (int c = 0; c < K / 8; ++c) {
-                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512 + 16 * r0;
+                prefetch_unit(b0, c + kPrefetchUnits, K / 8, 16 * R);
+                const uint8_t* u = b0 + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
                 __m512 x[NT];
                 for (int i = 0; i < NT; ++i) x[i] = _mm512_broadcast_f32x8(_mm256_loadu_ps(vec[i] + 8 * c));
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < Q; ++q) {
                     const __m256i w16 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(u + 32 * q));
                     const __m512 w = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(w16), 16));
                     for (int i = 0; i < NT; ++i) a[q][i] = _mm512_fmadd_ps(w, x[i], a[q][i]);
                 }
             }
             for (int i = 0; i < NT; ++i)
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < Q; ++q) {
                     out[i * 16 + r0 + 2 * q] = _mm512_mask_reduce_add_ps(0x00FF, a[q][i]);
                     out[i * 16 + r0 + 2 * q + 1] = _mm512_mask_reduce_add_ps(0xFF00, a[q][i]);
                 }
-            continue;
         }
-        if (fmt == FMT_FP8_B128) {
-            const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
-            // the block scale is one number for the chunk's rows: it multiplies
-            // the NT vector chunks, not the 8 rows' codes
+        return;
+    }
+    if (fmt == FMT_FP8_B128) {
+        // the block scale is one number for the unit's rows: it multiplies the
+        // NT vector chunks, not the rows' codes
+        constexpr int R = NT <= 3 ? 8 : NT <= 6 ? 4 : 2;
+        const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
+        for (int r0 = 0; r0 < 16; r0 += R) {
+            const uint8_t* b0 = base + 16 * r0;
+            __m512 a[R][NT];
+            for (int j = 0; j < R; ++j)
+                for (int i = 0; i < NT; ++i) a[j][i] = _mm512_setzero_ps();
             for (int c = 0; c < K / 16; ++c) {
-                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512 + 16 * r0;
+                prefetch_unit(b0, c + kPrefetchUnits, K / 16, 16 * R);
+                const uint8_t* u = b0 + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
                 const __m512 s = _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale);
                 __m512 x[NT];
                 for (int i = 0; i < NT; ++i) x[i] = _mm512_mul_ps(_mm512_loadu_ps(vec[i] + 16 * c), s);
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < R; ++j) {
                     const __m512 w = e4m3x16_div256(u + 16 * j);
                     for (int i = 0; i < NT; ++i) a[j][i] = _mm512_fmadd_ps(w, x[i], a[j][i]);
                 }
             }
-        } else {
-            const __m512 lut = _mm512_load_ps(e2m1_table());
-            const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h + r0;     // scale panel: 32 x K/32 bytes
-            for (int c = 0; c < K / 32; ++c) {
-                const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512 + 16 * r0;
-                const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
-                __m512 x0[NT], x1[NT];
-                for (int i = 0; i < NT; ++i) {
-                    x0[i] = _mm512_loadu_ps(vec[i] + 32 * c);
-                    x1[i] = _mm512_loadu_ps(vec[i] + 32 * c + 16);
-                }
-                for (int j = 0; j < 8; ++j) {
-                    const __m512 s = _mm512_set1_ps(e8m0(su[j]));
-                    const __m512 w0 = _mm512_mul_ps(e2m1x16(u + 16 * j, lut), s);
-                    const __m512 w1 = _mm512_mul_ps(e2m1x16(u + 16 * j + 8, lut), s);
-                    for (int i = 0; i < NT; ++i)
-                        a[j][i] = _mm512_fmadd_ps(w1, x1[i], _mm512_fmadd_ps(w0, x0[i], a[j][i]));
-                }
+            for (int i = 0; i < NT; ++i)
+                for (int j = 0; j < R; ++j) out[i * 16 + r0 + j] = _mm512_reduce_add_ps(a[j][i]);
+        }
+        return;
+    }
+    constexpr int R = NT <= 3 ? 8 : NT <= 6 ? 2 : 1;
+    const __m512 lut = _mm512_load_ps(e2m1_table());
+    for (int r0 = 0; r0 < 16; r0 += R) {
+        const uint8_t* b0 = base + 16 * r0;
+        const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h + r0;     // scale panel: 32 x K/32 bytes
+        __m512 a[R][NT];
+        for (int j = 0; j < R; ++j)
+            for (int i = 0; i < NT; ++i) a[j][i] = _mm512_setzero_ps();
+        for (int c = 0; c < K / 32; ++c) {
+            prefetch_unit(b0, c + kPrefetchUnits, K / 32, 16 * R);
+            const uint8_t* u = b0 + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
+            const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
+            __m512 x0[NT], x1[NT];
+            for (int i = 0; i < NT; ++i) {
+                x0[i] = _mm512_loadu_ps(vec[i] + 32 * c);
+                x1[i] = _mm512_loadu_ps(vec[i] + 32 * c + 16);
+            }
+            for (int j = 0; j < R; ++j) {
+                const __m512 s = _mm512_set1_ps(e8m0(su[j]));
+                const __m512 w0 = _mm512_mul_ps(e2m1x16(u + 16 * j, lut), s);
+                const __m512 w1 = _mm512_mul_ps(e2m1x16(u + 16 * j + 8, lut), s);
+                for (int i = 0; i < NT; ++i)
+                    a[j][i] = _mm512_fmadd_ps(w1, x1[i], _mm512_fmadd_ps(w0, x0[i], a[j][i]));
             }
         }
         for (int i = 0; i < NT; ++i)
-            for (int j = 0; j < 8; ++j) out[i * 16 + r0 + j] = _mm512_reduce_add_ps(a[j][i]);
+            for (int j = 0; j < R; ++j) out[i * 16 + r0 + j] = _mm512_reduce_add_ps(a[j][i]);
     }
 }
 
@@ -151,6 +194,7 @@ inline void panel_dots_1(int fmt, const uint8_t* rec, int64_t off, int64_t soff,
         __m512 a[16];
         for (int q = 0; q < 16; ++q) a[q] = _mm512_setzero_ps();
         for (int c = 0; c < K / 8; ++c) {
+            prefetch_unit(base, c + kPrefetchUnits, K / 8, 512);
             const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
             const __m512 xv = _mm512_broadcast_f32x8(_mm256_loadu_ps(x + 8 * c));
             for (int q = 0; q < 16; ++q) {      // rows 2q, 2q + 1
@@ -172,6 +216,7 @@ inline void panel_dots_1(int fmt, const uint8_t* rec, int64_t off, int64_t soff,
         if (fmt == FMT_FP8_B128) {
             const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
             for (int c = 0; c < K / 16; ++c) {
+                prefetch_unit(base, c + kPrefetchUnits, K / 16, 256);
                 const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
                 const __m512 xv = _mm512_mul_ps(_mm512_loadu_ps(x + 16 * c),
                                                 _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale));
@@ -189,6 +234,7 @@ inline void panel_dots_1(int fmt, const uint8_t* rec, int64_t off, int64_t soff,
             const __m512i odd = _mm512_add_epi32(even, _mm512_set1_epi32(1));
             const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h;     // scale panel: 32 x K/32 bytes
             for (int c = 0; c < K / 32; ++c) {
+                prefetch_unit(base, c + kPrefetchUnits, K / 32, 256);
                 const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
                 const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
                 const __m512 x0 = _mm512_loadu_ps(x + 32 * c);
@@ -314,6 +360,7 @@ inline void half_panel_decode_bf16(int fmt, const uint8_t* rec, int64_t off, int
     switch (fmt) {
         case FMT_BF16:
             for (int c = 0; c < K / 8; ++c) {
+                prefetch_unit(base, c + kPrefetchUnits, K / 8, 256);
                 const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
                 for (int r = 0; r < 16; ++r)
                     _mm_storeu_si128(reinterpret_cast<__m128i*>(w + (int64_t)r * K + 8 * c),
@@ -323,6 +370,7 @@ inline void half_panel_decode_bf16(int fmt, const uint8_t* rec, int64_t off, int
         case FMT_FP8_B128: {
             const float* sc = reinterpret_cast<const float*>(rec + soff) + (int64_t)(p >> 2) * (K >> 7);
             for (int c = 0; c < K / 16; ++c) {
+                prefetch_unit(base, c + kPrefetchUnits, K / 16, 256);
                 const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
                 const __m512 s = _mm512_set1_ps(sc[(16 * c) >> 7] * kE4M3Fp16Scale);
                 for (int r = 0; r < 16; ++r) {
@@ -336,6 +384,7 @@ inline void half_panel_decode_bf16(int fmt, const uint8_t* rec, int64_t off, int
             const __m512 lut = _mm512_load_ps(e2m1_table());
             const uint8_t* sb = rec + soff + (int64_t)p * K + 16 * h;
             for (int c = 0; c < K / 32; ++c) {
+                prefetch_unit(base, c + kPrefetchUnits, K / 32, 256);
                 const uint8_t* u = base + (int64_t)(c >> 1) * 1024 + (c & 1) * 512;
                 const uint8_t* su = sb + (c >> 1) * 64 + (c & 1) * 32;
                 for (int r = 0; r < 16; ++r) {
@@ -387,28 +436,30 @@ inline void dots_16xT_bf16(const uint16_t* w, int K, const uint16_t* const* vec,
     }
 }
 
-// Vectors at which the half panel is decoded once and dotted by
-// register-blocked tiles: there the multiply-adds, not the record's bytes,
-// set the pace.  The host branch takes the bf16 form above from here on
-// (decode, FP8 configuration, one box: T = 64 calls +15%, T = 2,048 calls
-// +80% against the fp32 form); the fp32 form below (`wdec`, 16 * K floats)
-// is what half_panel_dots does for such counts.
-constexpr int kBlockedMinVectors = 4;
-
 // Dots of the 16 rows [32p + 16h, +16) of a panel-ordered [rows x K] matrix
 // (codes at `off`, scales at `soff`) with nt >= 1 fp32 vectors vec[i] (length
-// K): out[i * 16 + r].  wdec: scratch of 16 * K floats.
+// K): out[i * 16 + r].  Up to stream_max_vectors(fmt) vectors one streaming
+// pass; more, the half panel decoded to fp32 once (wdec: scratch of 16 * K
+// floats) and dotted by register-blocked tiles.  (The host branch takes the
+// bf16 form above for such counts: T = 2,048 calls of the FP8 configuration
+// ran 80% faster with it on one box.)
 inline void half_panel_dots(int fmt, const uint8_t* rec, int64_t off, int64_t soff, int p, int h, int K,
                             const float* const* vec, int nt, float* wdec, float* out) {
-    static_assert(kBlockedMinVectors == 4, "the streaming pass is instantiated for 1..3 vectors");
-    switch (nt) {
-        case 1: half_panel_dots_stream<1>(fmt, rec, off, soff, p, h, K, vec, out); return;
-        case 2: half_panel_dots_stream<2>(fmt, rec, off, soff, p, h, K, vec, out); return;
-        case 3: half_panel_dots_stream<3>(fmt, rec, off, soff, p, h, K, vec, out); return;
-        default:
-            half_panel_decode(fmt, rec, off, soff, p, h, K, wdec);
-            dots_16xT(wdec, K, vec, nt, out);
+    if (nt <= stream_max_vectors(fmt)) {
+        switch (nt) {
+            case 1: half_panel_dots_stream<1>(fmt, rec, off, soff, p, h, K, vec, out); return;
+            case 2: half_panel_dots_stream<2>(fmt, rec, off, soff, p, h, K, vec, out); return;
+            case 3: half_panel_dots_stream<3>(fmt, rec, off, soff, p, h, K, vec, out); return;
+            case 4: half_panel_dots_stream<4>(fmt, rec, off, soff, p, h, K, vec, out); return;
+            case 5: half_panel_dots_stream<5>(fmt, rec, off, soff, p, h, K, vec, out); return;
+            case 6: half_panel_dots_stream<6>(fmt, rec, off, soff, p, h, K, vec, out); return;
+            case 7: half_panel_dots_stream<7>(fmt, rec, off, soff, p, h, K, vec, out); return;
+            case 8: half_panel_dots_stream<8>(fmt, rec, off, soff, p, h, K, vec, out); return;
+            default: break;
+        }
     }
+    half_panel_decode(fmt, rec, off, soff, p, h, K, wdec);
+    dots_16xT(wdec, K, vec, nt, out);
 }
 
 }  // namespace hostk

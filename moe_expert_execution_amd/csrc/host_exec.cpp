@@ -181,7 +181,7 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
                 for (int r = 0; r < 32; ++r) hb->hbuf[hrow0 * f + 32 * p + r] = silu(ws.g[r]) * ws.u[r];
                 continue;
             }
-            if (nt >= hostk::kBlockedMinVectors) {      // many tokens: bf16 rows and vectors, h kept in bf16
+            if (nt > hostk::stream_max_vectors(fmt)) {      // many tokens: bf16 rows and vectors, h kept in bf16
                 for (int i = 0; i < nt; ++i) ws.vec16[i] = hb->xb.data() + (int64_t)jb.tok[t0 + i] * d;
                 for (int h = 0; h < 2; ++h) {
                     hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.wdec16.data());
@@ -224,7 +224,7 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
                 ws.fit(nt, std::max(d, f));
                 const int64_t hrow0 = together ? t0 : 0;
                 for (int i = 0; i < nt; ++i) ws.vec[i] = hb->hbuf.data() + (hrow0 + i) * f;
-                if (nt >= hostk::kBlockedMinVectors) {      // many tokens: bf16 (h as phase 1 left it)
+                if (nt > hostk::stream_max_vectors(fmt)) {      // many tokens: bf16 (h as phase 1 left it)
                     for (int i = 0; i < nt; ++i) ws.vec16[i] = hb->hbuf16.data() + (hrow0 + i) * f;
                     for (int b = 2 * p; b < 2 * p + 2; ++b) {
                         hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f,

@@ -2,9 +2,9 @@
 on the CPU: for every record format, both paths (one streaming pass for few
 vectors; decode once + register-blocked tiles for many) give the dots of the
 oracle-decoded matrix rows with the vectors, within fp32 rounding (the
-streaming pass exists for 1..3 vectors; above that the dispatcher is used);
-the one-vector whole-panel pass gives the same bits as the two half-panel
-passes.  A small g++ harness includes the header as the library does.  CPU
+streaming pass is called directly for 1..8 vectors, the dispatcher above
+that); the streaming pass gives each vector the bits of a one-vector pass,
+and the one-vector whole-panel pass the bits of the two half-panel passes.  A small g++ harness includes the header as the library does.  CPU
 only."""
 import os
 import subprocess
@@ -58,6 +58,11 @@ int main(int argc, char** argv) {
     else if (nt == 1) half_panel_dots_stream<1>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
     else if (nt == 2) half_panel_dots_stream<2>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
     else if (nt == 3) half_panel_dots_stream<3>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
+    else if (nt == 4) half_panel_dots_stream<4>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
+    else if (nt == 5) half_panel_dots_stream<5>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
+    else if (nt == 6) half_panel_dots_stream<6>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
+    else if (nt == 7) half_panel_dots_stream<7>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
+    else if (nt == 8) half_panel_dots_stream<8>(fmt, rec.data(), off, soff, p, h, K, vec.data(), out.data());
     else half_panel_dots(fmt, rec.data(), off, soff, p, h, K, vec.data(), nt, wdec.data(), out.data());
     f = fopen(argv[10], "wb"); fwrite(out.data(), 4, out.size(), f); fclose(f);
     return 0;
@@ -90,7 +95,7 @@ def offsets(fmt, d, f):
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
 @pytest.mark.parametrize("blocked", [0, 1])
-@pytest.mark.parametrize("nt", [1, 2, 3, 4, 7, 13])
+@pytest.mark.parametrize("nt", [1, 2, 3, 4, 5, 6, 7, 8, 13])
 def test_half_panel_dots_match_decoded_rows(harness, fmt, blocked, nt):
     exe, tmp = harness
     d, f = 256, 128
@@ -234,3 +239,30 @@ def test_fp8_every_code(harness):
                 subprocess.check_call([str(exe), "1", str(d), "1", str(p), "0", str(og), str(osg),
                                        str(tmp / "rec.bin"), str(tmp / "v.bin"), str(tmp / "o.bin"), "2"])
                 assert np.array_equal(np.fromfile(tmp / "o.bin", dtype=np.float32), got[0]), p
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_stream_rows_per_pass_same_bits(harness, fmt):
+    """The streaming pass for NT vectors takes the 16 rows in passes of fewer
+    rows as NT grows (so its accumulators stay in registers); each row's
+    multiply-adds keep their order, so every vector's dots are the bits the
+    one-vector pass gives it."""
+    exe, tmp = harness
+    d, f = 512, 256
+    cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=d, f=f, E=2, cfg_id=95)
+    rec = synth.bank(cfg, 0, 1)[0]
+    og, od, osg, osd = offsets(fmt, d, f)
+    (tmp / "rec.bin").write_bytes(rec.tobytes())
+    rng = np.random.default_rng(95)
+    v = rng.standard_normal((8, d)).astype(np.float32)
+
+    def run(vs, p, h):
+        (tmp / "v.bin").write_bytes(vs.tobytes())
+        subprocess.check_call([str(exe), str(FMT[fmt]), str(d), str(len(vs)), str(p), str(h), str(og), str(osg),
+                               str(tmp / "rec.bin"), str(tmp / "v.bin"), str(tmp / "o.bin"), "0"])
+        return np.fromfile(tmp / "o.bin", dtype=np.float32).reshape(len(vs), 16)
+
+    for p, h in ((0, 0), (f // 32 - 1, 1)):
+        one = np.concatenate([run(v[i: i + 1], p, h) for i in range(8)])
+        for nt in (2, 3, 4, 6, 7, 8):
+            assert np.array_equal(run(v[:nt], p, h), one[:nt]), (nt, p, h)
