@@ -129,7 +129,7 @@ struct WorkerScratch {
     std::vector<const uint16_t*> vec16; // token vectors in bf16
     void fit(int nt, int kmax) {
         if ((int64_t)wdec.size() < 16ll * kmax) wdec.resize(16 * (size_t)kmax);
-        if ((int64_t)wdec16.size() < 16ll * kmax) wdec16.resize(16 * (size_t)kmax);
+        if ((int64_t)wdec16.size() < 16 * hostk::decoded_ld(kmax)) wdec16.resize(16 * (size_t)hostk::decoded_ld(kmax));
         if ((int)vec16.size() < nt) vec16.resize(nt);
         if ((int)vec.size() < nt) {
             const size_t n = std::max<size_t>(32, 16 * (size_t)nt);
@@ -183,11 +183,12 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
             }
             if (nt > hostk::stream_max_vectors(fmt)) {      // many tokens: bf16 rows and vectors, h kept in bf16
                 for (int i = 0; i < nt; ++i) ws.vec16[i] = hb->xb.data() + (int64_t)jb.tok[t0 + i] * d;
+                const int64_t ld = hostk::decoded_ld(d);
                 for (int h = 0; h < 2; ++h) {
-                    hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.wdec16.data());
-                    hostk::dots_16xT_bf16(ws.wdec16.data(), d, ws.vec16.data(), nt, ws.g.data());
-                    hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_up, hb->rl.off_su, p, h, d, ws.wdec16.data());
-                    hostk::dots_16xT_bf16(ws.wdec16.data(), d, ws.vec16.data(), nt, ws.u.data());
+                    hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_gate, hb->rl.off_sg, p, h, d, ws.wdec16.data(), ld);
+                    hostk::dots_16xT_bf16(ws.wdec16.data(), ld, d, ws.vec16.data(), nt, ws.g.data());
+                    hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_up, hb->rl.off_su, p, h, d, ws.wdec16.data(), ld);
+                    hostk::dots_16xT_bf16(ws.wdec16.data(), ld, d, ws.vec16.data(), nt, ws.u.data());
                     const int b = 2 * p + h;  // rows 16 b .. 16 b + 15
                     for (int i = 0; i < nt; ++i) {
                         alignas(64) float hv[16];
@@ -226,10 +227,11 @@ void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
                 for (int i = 0; i < nt; ++i) ws.vec[i] = hb->hbuf.data() + (hrow0 + i) * f;
                 if (nt > hostk::stream_max_vectors(fmt)) {      // many tokens: bf16 (h as phase 1 left it)
                     for (int i = 0; i < nt; ++i) ws.vec16[i] = hb->hbuf16.data() + (hrow0 + i) * f;
+                    const int64_t ld = hostk::decoded_ld(f);
                     for (int b = 2 * p; b < 2 * p + 2; ++b) {
                         hostk::half_panel_decode_bf16(fmt, rec, hb->rl.off_down, hb->rl.off_sd, b >> 1, b & 1, f,
-                                                      ws.wdec16.data());
-                        hostk::dots_16xT_bf16(ws.wdec16.data(), f, ws.vec16.data(), nt, ws.y.data());
+                                                      ws.wdec16.data(), ld);
+                        hostk::dots_16xT_bf16(ws.wdec16.data(), ld, f, ws.vec16.data(), nt, ws.y.data());
                         for (int i = 0; i < nt; ++i) {
                             float* pr = P + (int64_t)jb.tok[t0 + i] * d + 16 * b;
                             const float wt = jb.wt[t0 + i];

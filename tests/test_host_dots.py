@@ -37,16 +37,17 @@ int main(int argc, char** argv) {
     for (int i = 0; i < nt; ++i) vec[i] = v.data() + (size_t)i * K;
     std::vector<float> wdec(16 * (size_t)K), out(blocked == 2 ? 32 : 16 * nt);
     if (blocked >= 3) {     // bf16: 3 = the decoded rows, 4 = their dots with bf16 vectors (v.bin holds bf16)
-        std::vector<uint16_t> w16(16 * (size_t)K);
-        half_panel_decode_bf16(fmt, rec.data(), off, soff, p, h, K, w16.data());
+        const long long ld = decoded_ld(K);
+        std::vector<uint16_t> w16(16 * (size_t)ld);
+        half_panel_decode_bf16(fmt, rec.data(), off, soff, p, h, K, w16.data(), ld);
         f = fopen(argv[10], "wb");
         if (blocked == 3) {
-            fwrite(w16.data(), 2, w16.size(), f);
+            for (int r = 0; r < 16; ++r) fwrite(w16.data() + r * ld, 2, K, f);
         } else {
             const uint16_t* v16 = reinterpret_cast<const uint16_t*>(v.data());
             std::vector<const uint16_t*> vec16(nt);
             for (int i = 0; i < nt; ++i) vec16[i] = v16 + (size_t)i * K;
-            dots_16xT_bf16(w16.data(), K, vec16.data(), nt, out.data());
+            dots_16xT_bf16(w16.data(), ld, K, vec16.data(), nt, out.data());
             fwrite(out.data(), 4, out.size(), f);
         }
         fclose(f);
@@ -164,15 +165,26 @@ def test_bf16_blocked_dots(harness, fmt, nt):
     values exactly for bf16 and MXFP4 and e4m3 x block scale rounded to bf16
     for FP8 (within 2^-8 relative); their dots with bf16 vectors are the fp64
     dots of those same bf16 operands within fp32 rounding."""
+    _check_bf16_blocked(harness, fmt, nt, 256, 128, down=True)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_bf16_blocked_dots_sliced(harness, fmt):
+    """As above with K = 2,304: the dots run over column slices of 1,024 (two
+    whole slices and a ragged one), accumulators carried across slices."""
+    _check_bf16_blocked(harness, fmt, 13, 2304, 128, down=False)
+
+
+def _check_bf16_blocked(harness, fmt, nt, d, f, down):
     exe, tmp = harness
-    d, f = 256, 128
     cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=d, f=f, E=2, cfg_id=91)
     rec = synth.bank(cfg, 0, 1)[0]
     Wg, Wu, Wd = OF.decode_record(rec, fmt, d, f)
     og, od, osg, osd = offsets(fmt, d, f)
     rng = np.random.default_rng(nt)
     (tmp / "rec.bin").write_bytes(rec.tobytes())
-    for K, rows, off, soff in ((d, Wg.T, og, osg), (f, Wd.T, od, osd)):
+    mats = ((d, Wg.T, og, osg), (f, Wd.T, od, osd)) if down else ((d, Wg.T, og, osg),)
+    for K, rows, off, soff in mats:
         v16 = _bf16_rne(rng.standard_normal((nt, K)))                            # bf16 vectors
         v64 = OF.bf16_to_f64(v16)
         (tmp / "v.bin").write_bytes(v16.tobytes() + bytes(2 * nt * K))
