@@ -359,8 +359,8 @@ ft_status ft_cache_resize(ft_cache* cache, int64_t new_num_slots);
  * B_P: the fill kernel pulls `records` layer-0 records from the pinned host
  * bank into slots 0 .. records-1, max_tokens * k records per launch (best of
  * three passes, HIP events).  B_H: the host workers run `records` records as
- * host experts of up to max_tokens tokens per call (two passes after a
- * warm-up, the workers' own clock).  Each pass reads records of its own
+ * host experts of up to max_tokens tokens per call (best of three passes
+ * after a warm-up, the workers' own clock).  Each pass reads records of its own
  * (pass p: p * records + i, modulo E), so no pass is timed on data a previous
  * one left in a host cache.  Both are record bytes / time in MB/s, written to `out`
  * (max_fetch copied from the cache's profile).  Safe point: the caller

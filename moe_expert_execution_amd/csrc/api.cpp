@@ -809,14 +809,18 @@ ft_status ft_cache_profile(ft_cache* c, int32_t records, ft_profile* out) {
             host_branch_run_sync(c->host, 0, T);
         }
     };
-    uint64_t b0c, b1c, x0, x1;
-    double s0, s1;
+    // best of three passes, as for B_P: one pass is a millisecond or so, and a
+    // worker the OS delays for part of it stretches the whole pass
     host_pass(3);                      // warm-up (worker wake-up), records not timed
-    host_branch_counters(c->host, &b0c, &s0, &x0);
-    host_pass(4);
-    host_pass(5);
-    host_branch_counters(c->host, &b1c, &s1, &x1);
-    const double bh = (double)(b1c - b0c) / std::max(s1 - s0, 1e-9) / 1e6;
+    double bh = 0.0;
+    for (int pass = 4; pass < 7; ++pass) {
+        uint64_t b0c, b1c, x0, x1;
+        double s0, s1;
+        host_branch_counters(c->host, &b0c, &s0, &x0);
+        host_pass(pass);
+        host_branch_counters(c->host, &b1c, &s1, &x1);
+        bh = std::max(bh, (double)(b1c - b0c) / std::max(s1 - s0, 1e-9) / 1e6);
+    }
     // the pool's slots were overwritten: the cache restarts empty
     const int64_t nids = (int64_t)c->sh.layers * c->sh.experts;
     const uint64_t one = 1;
