@@ -297,6 +297,46 @@ def test_one_token_width_boundary(fmt, d):
 
 
 @gpu
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_host_token_counts(fmt):
+    """One CACHED call whose eight experts all run on the host (max_fetch 0,
+    cold cache) with 1, 2, 3, 4, 7, 8, 9 and 16 tokens each: the host
+    branch's one-token, streaming and decode-once forms side by side in its
+    pooled phases (the streaming form takes up to 8 tokens for bf16 and
+    block-FP8, up to 3 for MXFP4), d = 2,304 so the many-token dots end in a
+    ragged column slice.  Routes as classify rewrote them against the
+    simulator, every output row against the oracle; then the same call again."""
+    cuda()
+    cfg = synth.CONFIGS["tiny"].with_(fmt=fmt, d=2304, f=256, E=16, k=2, slots=4, cfg_id=100)
+    counts = (1, 2, 3, 4, 7, 8, 9, 16)
+    col = np.repeat(np.arange(len(counts)) * 2 + 1, counts)          # experts 1, 3, ..., 15
+    T = col.size // 2
+    ids = np.stack([col[:T], col[T:]], axis=1).astype(np.int32)      # 16 < T: a token's two experts differ
+    assert np.all(ids[:, 0] != ids[:, 1])
+    w = np.random.default_rng(100).uniform(0.2, 1.0, size=ids.shape).astype(np.float32)
+    bank = make_bank(cfg)
+    recs = bank.records(cfg.S)
+    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, fmt, bank.ptr, cfg.slots, T, cfg.bp_mbps, cfg.bh_mbps, 0)
+    sim = OC.SlotCacheSim(1, cfg.E, cfg.slots, cfg.bp_mbps, cfg.bh_mbps, 0)
+    try:
+        ex = expert_fn(recs, cfg, 0, maxsize=cfg.E)
+        for call in range(2):
+            x = synth.tokens(cfg, T, 800 + call)
+            r = sim.classify(0, ids)
+            assert set(r.cls) == {OC.CPU}, r.cls
+            before = M.ft_cache_stats(sc.handle).as_dict()
+            y, routes = run_cached(sc, 0, x, ids, w)
+            after = M.ft_cache_stats(sc.handle).as_dict()
+            assert np.array_equal(routes, r.routes)
+            assert after["cpu_experts"] - before["cpu_experts"] == len(counts)
+            assert_close_rel(y, oracle_rows(x, ids, w, ex, np.arange(T)), TOL[fmt], f"{fmt} call {call}")
+        assert M.ft_cache_stats(sc.handle).error_flags == 0
+    finally:
+        sc.close()
+        bank.close()
+
+
+@gpu
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
 def test_top16_layer(fmt):
     """The largest top-k (16): E = 32 over 24 slots, so calls mix hits, fills
