@@ -962,7 +962,8 @@ def mxfp4_config_bench(args, phys_layers=8):
 def tiny_config_bench(args, calls=8):
     """The tiny configuration: one layer (d=256, E=8, top-2, f=128, bf16), a
     4-slot cache from cold, B_P/B_H 25/50 GB/s; `calls` calls of 16 fresh
-    tokens (route, classify, CACHED forward)."""
+    tokens (route, classify, CACHED forward), timed after the same calls ran
+    once untimed on a cache of their own."""
     import numpy as np
     import torch
 
@@ -974,7 +975,6 @@ def tiny_config_bench(args, calls=8):
     T = cfg.tokens[0]
     bank = PinnedBank(cfg.E * cfg.S)
     synth.bank(cfg, out=bank.records(cfg.S))
-    sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, T, cfg.bp_mbps, cfg.bh_mbps)
     stream = torch.cuda.current_stream().cuda_stream
     xs = torch.stack([torch.from_numpy(synth.tokens(cfg, T, 0 if c == 0 else 100 + c).view(np.int16))
                       for c in range(calls)]).cuda()
@@ -982,18 +982,27 @@ def tiny_config_bench(args, calls=8):
     ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
     y = torch.empty((T, cfg.d), dtype=torch.int16, device="cuda")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for c in range(calls):
-        M.ft_moe_route(sc.shape, xs[c].data_ptr(), wr.data_ptr(), T, ids.data_ptr(), w.data_ptr(), stream)
-        M.ft_cache_classify(sc.handle, 0, ids.data_ptr(), T, None, stream)
-        M.ft_moe_forward(sc.handle, 0, M.FT_MODE_CACHED, xs[c].data_ptr(), ids.data_ptr(), w.data_ptr(), T,
-                         y.data_ptr(), stream)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    st = M.ft_cache_stats(sc.handle)
-    assert st.error_flags == 0
-    sc.close()
+
+    def run(n):
+        sc = SlotCache(1, cfg.E, cfg.k, cfg.d, cfg.f, "bf16", bank.ptr, cfg.slots, T, cfg.bp_mbps, cfg.bh_mbps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for c in range(n):
+            M.ft_moe_route(sc.shape, xs[c].data_ptr(), wr.data_ptr(), T, ids.data_ptr(), w.data_ptr(), stream)
+            M.ft_cache_classify(sc.handle, 0, ids.data_ptr(), T, None, stream)
+            M.ft_moe_forward(sc.handle, 0, M.FT_MODE_CACHED, xs[c].data_ptr(), ids.data_ptr(), w.data_ptr(), T,
+                             y.data_ptr(), stream)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        st = M.ft_cache_stats(sc.handle)
+        assert st.error_flags == 0
+        sc.close()
+        return el, st
+
+    # untimed: the same calls on a cache of their own (the first launches of
+    # this shape's kernels in the process cost several hundred microseconds)
+    run(calls)
+    el, st = run(calls)       # timed: a new cache, cold
     bank.close()
     return {"workload": f"tiny layer d={cfg.d}, E={cfg.E}, top-{cfg.k}, f={cfg.f}, bf16, {cfg.slots} slots from "
                         f"cold, {calls} calls of {T} tokens", "tokens_per_s": calls * T / el,
