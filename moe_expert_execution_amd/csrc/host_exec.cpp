@@ -153,7 +153,10 @@ struct WorkerScratch {
 // tokens; (2) 32 output columns per item, every expert's down matrix in
 // expert order, so each output element still receives its experts' terms in
 // the same order.  Otherwise the experts run one after the other, two phases
-// each.
+// each.  An expert's token count picks its dot form (host_dots.h), the same
+// in both phases: one token, the whole-panel pass; up to
+// stream_max_vectors(fmt), the streaming pass with h kept in fp32; more, the
+// half panel decoded once to bf16 and h kept in bf16.
 void run_job(HostBranch* hb, int participants, WorkerScratch& ws) {
     const Job& jb = hb->job;
     const int d = hb->sh.d_model, f = hb->sh.d_ff, E = hb->sh.experts, fmt = hb->sh.fmt;
