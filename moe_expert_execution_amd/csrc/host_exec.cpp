@@ -8,9 +8,14 @@
 // workers pinned to physical cores; "The Expert Cache That Follows the
 // Router": a host-run miss reads the source without changing residency).
 //
-// The GPU side never waits on the host: the work is enqueued as a stream host
-// function after the routes, weights and activations are copied to pinned
-// staging, and the partial sum is copied back on the same stream.
+// Signalling: the planner kernel copies the call's routes, weights and
+// activations into pinned staging and posts the call's sequence number to a
+// pinned mailbox; a poller thread runs the call with the workers and posts
+// it done.  The partial sum P stays in pinned memory, where the combine
+// kernel reads it after waiting (bounded) for the done word; the GPU experts
+// and fills run meanwhile.  Without the poller (FTMOE_HOST_SIGNAL=callback)
+// the call is a host function on a stream of the library's, and the caller's
+// stream waits for its event before the combine.
 #include <hip/hip_runtime.h>
 #include <immintrin.h>
 #include <pthread.h>
